@@ -1,0 +1,144 @@
+"""CPU oracle for the SS2D forward operator (float64).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use it; the GPU library never imports, links or calls anything here, and this
+package imports nothing from the GPU package.
+
+The arithmetic lives in ``ss2d_oracle.c`` (plain C, one sequential loop per channel and route,
+every operation in double; see its header for the definition and the pages it follows).
+This module only compiles it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+HERE = pathlib.Path(__file__).resolve().parent
+SOURCE = HERE / "ss2d_oracle.c"
+LIBRARY = HERE / "liboracle_ss2d.so"
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(source: os.PathLike = SOURCE, output: os.PathLike = LIBRARY) -> pathlib.Path:
+    """Compile the oracle into a shared library with gcc (IEEE double, no fast-math)."""
+    output = pathlib.Path(output)
+    tmp = output.with_suffix(".so.tmp")
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           "-fno-fast-math", str(source), "-o", str(tmp), "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, output)
+    return output
+
+
+class Oracle:
+    """ctypes handle on one compiled oracle library (the tests also load planted mutants)."""
+
+    def __init__(self, path: os.PathLike = LIBRARY):
+        path = pathlib.Path(path)
+        if not path.exists():
+            if path != LIBRARY:
+                raise FileNotFoundError(path)
+            build()
+        self.path = path
+        lib = ctypes.CDLL(str(path))
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [ctypes.c_int] + [_f32p] * 7 + [_f64p] + \
+            [ctypes.c_int64] * 5 + [ctypes.c_int]
+        lib.oracle_forward_channels.restype = ctypes.c_int
+        lib.oracle_forward_channels.argtypes = [ctypes.c_int] + [_f32p] * 7 + \
+            [ctypes.c_int64] * 5 + [_i64p, _i64p, ctypes.c_int64, _f64p, ctypes.c_int]
+        self.lib = lib
+        self.last_threads = None
+
+    # -- argument marshalling -----------------------------------------------------------
+    @staticmethod
+    def _f32(a):
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        return a, a.ctypes.data_as(_f32p)
+
+    def _prep(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias):
+        x = np.asarray(x)
+        if K == 4:
+            if x.ndim != 4:
+                raise ValueError("x must be (B, D, H, W)")
+            B, D, H, W = x.shape
+        else:
+            if x.ndim != 3:
+                raise ValueError("x must be (B, D, L)")
+            B, D, L = x.shape
+            H, W = 1, L
+        L = H * W
+        N = np.asarray(A_log).shape[-1]
+        shapes = dict(dt_raw=(B, K, D, L), A_log=(K, D, N), Bs=(B, K, N, L), Cs=(B, K, N, L),
+                      Ds=(K, D), dt_bias=(K, D))
+        arrs = dict(dt_raw=dt_raw, A_log=A_log, Bs=Bs, Cs=Cs, Ds=Ds, dt_bias=dt_bias)
+        for k, shp in shapes.items():
+            if tuple(np.shape(arrs[k])) != shp:
+                raise ValueError(f"{k} has shape {np.shape(arrs[k])}, expected {shp}")
+        keep, ptrs = [], []
+        for a in (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias):
+            a2, p = self._f32(a)
+            keep.append(a2)
+            ptrs.append(p)
+        return (B, D, H, W, N), keep, ptrs
+
+    # -- public calls -----------------------------------------------------------------
+    def forward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+        (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+        y = np.empty((B, D, H * W), dtype=np.float64)
+        rc = self.lib.oracle_forward(K, *ptrs, y.ctypes.data_as(_f64p), B, D, H, W, N,
+                                     int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_forward rejected its arguments")
+        self.last_threads = rc
+        return y.reshape(np.shape(x))
+
+    def forward_channels(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx,
+                         threads=0):
+        (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+        bi = np.ascontiguousarray(b_idx, dtype=np.int64)
+        di = np.ascontiguousarray(d_idx, dtype=np.int64)
+        if bi.shape != di.shape or bi.ndim != 1:
+            raise ValueError("b_idx and d_idx must be 1-D and of equal length")
+        y = np.empty((bi.size, H * W), dtype=np.float64)
+        rc = self.lib.oracle_forward_channels(K, *ptrs, B, D, H, W, N,
+                                              bi.ctypes.data_as(_i64p),
+                                              di.ctypes.data_as(_i64p), bi.size,
+                                              y.ctypes.data_as(_f64p), int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_forward_channels rejected its arguments")
+        self.last_threads = rc
+        return y.reshape((bi.size,) + tuple(np.shape(x)[2:]))
+
+
+_DEFAULT = None
+
+
+def default() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT
+
+
+def ss2d_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+    """y (B, D, H, W), float64, of the four-route SS2D forward operator."""
+    return default().forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads)
+
+
+def ss1d_bidir_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+    """y (B, D, L), float64, of the bidirectional (forward + reversed) 1D scan."""
+    return default().forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads)
+
+
+def forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx, threads=0):
+    """Output planes of the selected (b, d) channels only."""
+    return default().forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx,
+                                      threads)

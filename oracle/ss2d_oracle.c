@@ -1,0 +1,191 @@
+/*
+ * CPU oracle for the SS2D forward operator and its bidirectional 1D variant.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline load this library.  It shares no code, header or constant with the GPU path:
+ * it is a plain sequential loop in float64, written from the pages' definitions.
+ *
+ * What it computes, per (b, d) channel:
+ *
+ *   for each route k = 0 .. K-1 (in this order), from a zero state h = 0:
+ *     for t = 0 .. L-1:
+ *       l     = pi_k(t)                       image position visited at step t of route k
+ *       u     = x[b, d, l]
+ *       delta = softplus(dt_raw[b, k, d, t] + dt_bias[k, d])
+ *       h_n   = exp(delta * A[k, d, n]) * h_n + delta * Bs[b, k, n, t] * u   (n = 0..N-1)
+ *       y[b, d, l] += sum_n Cs[b, k, n, t] * h_n + Ds[k, d] * u
+ *   with A[k, d, n] = -exp(A_log[k, d, n]).
+ *
+ * Sources (page titles as printed in the reference pages):
+ *   - Recurrence, zero initial state, output taken after the update, skip term D * x:
+ *     "Vision Mamba" explainer (dileepadev), SelectiveSSM._selective_scan listing; the
+ *     discrete system h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t in the Vim summary
+ *     (aipaper.cc), section 4.1.
+ *   - Discretisation Abar = exp(delta * A) and Bbar x = delta * B * x (exponential for A, first
+ *     order for B): the explainer's listing (dA, dB) and the VMamba review (nubint.ai),
+ *     "Proposed method".
+ *   - delta = softplus(dt_proj(.)) with the projection's bias inside the softplus, and
+ *     A = -exp(A_log) real and diagonal: the explainer's SelectiveSSM.__init__ / forward.
+ *   - Four routes and their inverses: the explainer's CrossScanModule listing (row-major,
+ *     its flip, column-major, its flip; inverse flips and (W,H) -> (H,W) transposes) and
+ *     the Chinese VMamba article, section 1 (cross_scan); the outputs are summed (the
+ *     explainer's prose on the Cross-Scan Module).  The sum is taken in route order
+ *     k = 0, 1, 2, 3 for every position.
+ *   - K = 2: the Vim block's forward path and a backward path over a reversed copy of the
+ *     sequence, added together (Vim summary, section 4.3).
+ *
+ * Layouts (all contiguous, row-major):
+ *   x, y      (B, D, H, W)    y written in full
+ *   dt_raw    (B, K, D, L)    scan order of route k (position t is step t of that route)
+ *   Bs, Cs    (B, K, N, L)    scan order of route k
+ *   A_log     (K, D, N)       Ds, dt_bias (K, D)
+ * Inputs arrive as float (the exact values the GPU path receives, bfloat16 widened where
+ * applicable); every operation is done in double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* log(1 + e^z), written to stay finite for large |z| */
+static double softplus(double z) {
+    const double m = z > 0.0 ? z : 0.0;
+    return m + log1p(exp(-fabs(z)));
+}
+
+/* Raster index (h * W + w) of the image position visited at step t of route k.
+ * K = 4: 0 row-major, 1 row-major reversed, 2 column-major, 3 column-major reversed.
+ * K = 2: 0 forward, 1 reversed (H = 1, W = L). */
+static int64_t route_position(int K, int k, int64_t t, int64_t H, int64_t W) {
+    const int64_t L = H * W;
+    int64_t s;
+    if (K == 2)
+        return k == 0 ? t : L - 1 - t;
+    switch (k) {
+    case 0:
+        return t;
+    case 1:
+        return L - 1 - t;
+    case 2:
+        return (t % H) * W + t / H;
+    default:
+        s = L - 1 - t;
+        return (s % H) * W + s / H;
+    }
+}
+
+/* All K routes of one (b, d) channel, summed into out[0 .. L-1] (image order). */
+static void channel_forward(int K, const float *x, const float *dt_raw, const float *A_log,
+                            const float *Bs, const float *Cs, const float *Ds,
+                            const float *dt_bias, int64_t D, int64_t H, int64_t W, int64_t N,
+                            int64_t b, int64_t d, double *out, double *h, double *A) {
+    const int64_t L = H * W;
+    const float *xc = x + (b * D + d) * L;
+    for (int64_t l = 0; l < L; ++l)
+        out[l] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const double bias = dt_bias[k * D + d];
+        const double Dk = Ds[k * D + d];
+        const float *dt = dt_raw + ((b * K + k) * D + d) * L;
+        const float *Bk = Bs + (b * K + k) * N * L;
+        const float *Ck = Cs + (b * K + k) * N * L;
+        for (int64_t n = 0; n < N; ++n) {
+            A[n] = -exp((double)A_log[(k * D + d) * N + n]);
+            h[n] = 0.0;
+        }
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t l = route_position(K, k, t, H, W);
+            const double u = xc[l];
+            const double delta = softplus((double)dt[t] + bias);
+            double yk = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double a = exp(delta * A[n]);
+                h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;
+                yk += (double)Ck[n * L + t] * h[n];
+            }
+            out[l] += yk + Dk * u;
+        }
+    }
+}
+
+static int pick_threads(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Full output y (B, D, H, W) in double.  K is 4 (SS2D) or 2 (bidirectional 1D, H = 1).
+ * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
+int oracle_forward(int K, const float *x, const float *dt_raw, const float *A_log,
+                   const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                   double *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                   int nthreads) {
+    if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
+        return -1;
+    if (K == 2 && H != 1)
+        return -1;
+    const int threads = pick_threads(nthreads);
+    const int64_t L = H * W;
+    const int64_t total = B * D;
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+#endif
+    {
+        double *h = (double *)malloc(sizeof(double) * (size_t)(2 * N));
+        if (!h) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t i = 0; i < total; ++i) {
+                const int64_t b = i / D, d = i % D;
+                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, D, H, W, N, b, d,
+                                y + i * L, h, h + N);
+            }
+            free(h);
+        }
+    }
+    return failed ? -1 : threads;
+}
+
+/* Output planes y[b_idx[i], d_idx[i], :, :] for i < nsel, written to y_sel (nsel, H, W).
+ * Same arithmetic as oracle_forward; used to check large outputs on sampled channels. */
+int oracle_forward_channels(int K, const float *x, const float *dt_raw, const float *A_log,
+                            const float *Bs, const float *Cs, const float *Ds,
+                            const float *dt_bias, int64_t B, int64_t D, int64_t H, int64_t W,
+                            int64_t N, const int64_t *b_idx, const int64_t *d_idx,
+                            int64_t nsel, double *y_sel, int nthreads) {
+    if ((K != 2 && K != 4) || N <= 0 || (K == 2 && H != 1))
+        return -1;
+    for (int64_t i = 0; i < nsel; ++i)
+        if (b_idx[i] < 0 || b_idx[i] >= B || d_idx[i] < 0 || d_idx[i] >= D)
+            return -1;
+    const int threads = pick_threads(nthreads);
+    const int64_t L = H * W;
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+#endif
+    {
+        double *h = (double *)malloc(sizeof(double) * (size_t)(2 * N));
+        if (!h) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t i = 0; i < nsel; ++i)
+                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, D, H, W, N,
+                                b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
+            free(h);
+        }
+    }
+    return failed ? -1 : threads;
+}

@@ -1,0 +1,368 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` handle and raises AssertionError when the handle
+disagrees with the fact it checks.  ``test_oracle_pins.py`` runs them on the real oracle and
+on deliberately broken copies of its source (each planted mistake must trip a pin).
+
+What pins what:
+  brute force       explicit sum over s of (prod of decays) * delta_s B_s u_s on tiny inputs
+                    (the recurrence unrolled; the convolution form of the Vim summary, sec.
+                    4.1, generalised to a time-varying decay)
+  geometric         constant inputs: h_t = delta B u (1 - a^(t+1)) / (1 - a)
+  convolve          time-invariant delta, B, C: y = u * Kbar with Kbar_j = C a^j delta B
+                    (Vim summary, sec. 4.1), evaluated with numpy.convolve
+  lfilter           N = 1: a first-order IIR filter, evaluated with scipy.signal.lfilter
+  halving           A_log = log(log 2) and delta = 1 give a decay of exactly 1/2 per step
+  small delta       delta -> 0: the state stays at zero and y = (sum_k D_k) x (the Chinese
+                    VMamba article, sec. 2: a small step keeps the history)
+  memoryless        a huge |A| forgets at once: y = delta <C_t, B_t> u + D u, with delta taken
+                    from numpy.logaddexp (softplus) -- pins softplus and where dt_bias enters
+  routes            integer-coded steps land on the positions the pages' array recipe gives
+                    (flatten, flip, transpose-then-flatten, flip), on non-square maps
+  flip              the reversed route equals the forward route run on the flipped input
+  transpose, rot180 symmetries of the four routes under exchange of parameter sets
+  linearity         y is linear in x for fixed delta, B, C
+  channels          the sampled-channel entry point agrees with the full one
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.signal
+
+RNG_SEED = 1234
+
+
+def _rng(salt: int) -> np.random.Generator:
+    return np.random.default_rng(RNG_SEED + salt)
+
+
+def _close(got, want, rtol, atol=0.0, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    err = np.abs(got - want)
+    lim = atol + rtol * np.abs(want)
+    bad = ~(err <= lim)
+    if bad.any():
+        worst = float(np.max(np.where(np.isnan(err), np.inf, err)))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements off; worst "
+                             f"|err|={worst:.3e}")
+
+
+def _random_inputs(rng, B, K, D, N, L, xshape=None):
+    x = rng.standard_normal(xshape or (B, D, L)).astype(np.float32)
+    dt = (0.5 * rng.standard_normal((B, K, D, L))).astype(np.float32)
+    Bs = rng.standard_normal((B, K, N, L)).astype(np.float32)
+    Cs = rng.standard_normal((B, K, N, L)).astype(np.float32)
+    A_log = rng.uniform(-0.5, 1.5, size=(K, D, N)).astype(np.float32)
+    Ds = rng.standard_normal((K, D)).astype(np.float32)
+    bias = rng.uniform(-3.0, -1.0, size=(K, D)).astype(np.float32)
+    return x, dt, A_log, Bs, Cs, Ds, bias
+
+
+def _softplus(z):
+    return np.logaddexp(0.0, np.asarray(z, dtype=np.float64))
+
+
+def _brute_force_scan(u, dt, bias, A_log, Bm, Cm, Dv):
+    """One route in its own scan order, by the unrolled sum (pure Python loops)."""
+    L = len(u)
+    N = len(A_log)
+    delta = [float(_softplus(float(dt[t]) + float(bias))) for t in range(L)]
+    A = [-math.exp(float(A_log[n])) for n in range(N)]
+    y = []
+    for t in range(L):
+        acc = 0.0
+        for n in range(N):
+            h = 0.0
+            for s in range(t + 1):
+                decay = 1.0
+                for r in range(s + 1, t + 1):
+                    decay *= math.exp(delta[r] * A[n])
+                h += decay * delta[s] * float(Bm[n][s]) * float(u[s])
+            acc += float(Cm[n][t]) * h
+        y.append(acc + float(Dv) * float(u[t]))
+    return np.array(y)
+
+
+def _routes(H, W, K=4):
+    """Position visited at each step of each route, built the way the pages' listings build
+    the sequences: flatten row-major, flip it, transpose then flatten, flip that."""
+    grid = np.arange(H * W).reshape(H, W)
+    row = grid.reshape(-1)
+    col = grid.T.reshape(-1)
+    if K == 2:
+        return [row, row[::-1]]
+    return [row, row[::-1], col, col[::-1]]
+
+
+# ---------------------------------------------------------------------------------------
+def pin_brute_force(orc):
+    rng = _rng(1)
+    B, K, D, N, L = 2, 2, 3, 3, 9
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L)
+    for keep in (0, 1):
+        Cs2, Ds2 = Cs.copy(), Ds.copy()
+        Cs2[:, 1 - keep] = 0.0
+        Ds2[1 - keep] = 0.0
+        y = orc.forward(2, x, dt, A_log, Bs, Cs2, Ds2, bias)
+        want = np.zeros_like(y)
+        for b in range(B):
+            for d in range(D):
+                order = np.arange(L) if keep == 0 else np.arange(L)[::-1]
+                ys = _brute_force_scan(x[b, d, order], dt[b, keep, d], bias[keep, d],
+                                       A_log[keep, d], Bs[b, keep], Cs2[b, keep], Ds2[keep, d])
+                want[b, d, order] = ys
+        _close(y, want, 1e-12, 1e-14, f"brute force, route {keep}")
+
+
+def pin_geometric(orc):
+    B, K, D, N, L = 1, 2, 2, 2, 40
+    x = np.full((B, D, L), 0.75, np.float32)
+    dt = np.full((B, K, D, L), -0.25, np.float32)
+    bias = np.array([[-1.0, 0.5], [0.0, 0.0]], np.float32)
+    A_log = np.array([[[0.0, 1.0], [-1.0, 0.5]]] * K, np.float32)
+    Bs = np.empty((B, K, N, L), np.float32)
+    Cs = np.empty((B, K, N, L), np.float32)
+    Bs[:, :, 0], Bs[:, :, 1] = 1.5, -0.5
+    Cs[:, :, 0], Cs[:, :, 1] = 0.25, 2.0
+    Cs[:, 1] = 0.0
+    Ds = np.array([[0.5, -1.0], [0.0, 0.0]], np.float32)
+    y = orc.forward(2, x, dt, A_log, Bs, Cs, Ds, bias)
+    t = np.arange(L)
+    for d in range(D):
+        delta = float(_softplus(-0.25 + float(bias[0, d])))
+        want = np.full(L, float(Ds[0, d]) * 0.75)
+        for n in range(N):
+            a = math.exp(-delta * math.exp(float(A_log[0, d, n])))
+            h = delta * float(Bs[0, 0, n, 0]) * 0.75 * (1.0 - a ** (t + 1)) / (1.0 - a)
+            want = want + float(Cs[0, 0, n, 0]) * h
+        _close(y[0, d], want, 1e-12, 0.0, f"geometric series, d={d}")
+
+
+def pin_convolve(orc):
+    rng = _rng(3)
+    B, K, D, N, L = 1, 2, 2, 4, 50
+    x = rng.standard_normal((B, D, L)).astype(np.float32)
+    dt = np.zeros((B, K, D, L), np.float32)
+    bias = np.array([[-2.0, -0.5], [0.0, 0.0]], np.float32)
+    A_log = rng.uniform(-1.0, 1.0, size=(K, D, N)).astype(np.float32)
+    bvec = rng.standard_normal(N).astype(np.float32)
+    cvec = rng.standard_normal(N).astype(np.float32)
+    Bs = np.broadcast_to(bvec[None, None, :, None], (B, K, N, L)).astype(np.float32)
+    Cs = np.broadcast_to(cvec[None, None, :, None], (B, K, N, L)).astype(np.float32)
+    Cs[:, 1] = 0.0
+    Ds = np.array([[0.3, -0.7], [0.0, 0.0]], np.float32)
+    y = orc.forward(2, x, dt, A_log, Bs, Cs, Ds, bias)
+    j = np.arange(L)
+    for d in range(D):
+        delta = float(_softplus(float(bias[0, d])))
+        kbar = np.zeros(L)
+        for n in range(N):
+            a = math.exp(-delta * math.exp(float(A_log[0, d, n])))
+            kbar += float(cvec[n]) * a ** j * delta * float(bvec[n])
+        kbar[0] += float(Ds[0, d])
+        want = np.convolve(x[0, d].astype(np.float64), kbar)[:L]
+        _close(y[0, d], want, 1e-11, 1e-13, f"convolution form, d={d}")
+
+
+def pin_lfilter(orc):
+    rng = _rng(4)
+    B, K, D, N, L = 1, 2, 3, 1, 64
+    x = rng.standard_normal((B, D, L)).astype(np.float32)
+    dt = np.zeros((B, K, D, L), np.float32)
+    bias = np.array([[-3.0, -1.0, 0.5], [0, 0, 0]], np.float32)
+    A_log = np.array([[[-2.0], [0.0], [1.0]], [[0.0], [0.0], [0.0]]], np.float32)
+    Bs = np.full((B, K, N, L), 1.25, np.float32)
+    Cs = np.full((B, K, N, L), -0.5, np.float32)
+    Cs[:, 1] = 0.0
+    Ds = np.array([[0.0, 1.0, 2.0], [0, 0, 0]], np.float32)
+    y = orc.forward(2, x, dt, A_log, Bs, Cs, Ds, bias)
+    for d in range(D):
+        delta = float(_softplus(float(bias[0, d])))
+        a = math.exp(-delta * math.exp(float(A_log[0, d, 0])))
+        h = scipy.signal.lfilter([delta * 1.25], [1.0, -a], x[0, d].astype(np.float64))
+        want = -0.5 * h + float(Ds[0, d]) * x[0, d]
+        _close(y[0, d], want, 1e-12, 1e-14, f"lfilter, d={d}")
+
+
+def pin_halving(orc):
+    B, K, D, N, L = 1, 2, 1, 1, 30
+    x = np.zeros((B, D, L), np.float32)
+    x[0, 0, 0] = 1.0
+    # float32 cannot hold log(e - 1) or log(log 2) exactly; the expected values below use
+    # the float32 numbers actually passed, and reduce to 2^-t up to that rounding.
+    z = np.float32(math.log(math.e - 1.0))
+    alog = np.float32(math.log(math.log(2.0)))
+    dt = np.zeros((B, K, D, L), np.float32)
+    bias = np.array([[z], [0.0]], np.float32)
+    A_log = np.array([[[alog]], [[0.0]]], np.float32)
+    Bs = np.ones((B, K, N, L), np.float32)
+    Cs = np.ones((B, K, N, L), np.float32)
+    Cs[:, 1] = 0.0
+    Ds = np.zeros((K, D), np.float32)
+    y = orc.forward(2, x, dt, A_log, Bs, Cs, Ds, bias)
+    t = np.arange(L)
+    _close(y[0, 0], 0.5 ** t, 5e-6, 0.0, "decay of one half per step")
+    delta = math.log1p(math.exp(float(z)))
+    a = math.exp(-delta * math.exp(float(alog)))
+    _close(y[0, 0], delta * a ** t, 1e-13, 0.0, "impulse response")
+
+
+def pin_small_delta(orc):
+    rng = _rng(6)
+    B, K, D, N, H, W = 2, 4, 3, 4, 3, 5
+    L = H * W
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, (B, D, H, W))
+    dt[:] = -80.0
+    y = orc.forward(4, x, dt, A_log, Bs, Cs, Ds, bias)
+    want = Ds.astype(np.float64).sum(axis=0)[None, :, None, None] * x
+    _close(y, want, 1e-13, 1e-30, "delta -> 0 gives (sum_k D_k) x")
+
+
+def pin_memoryless(orc):
+    rng = _rng(7)
+    B, K, D, N, L = 2, 2, 3, 4, 11
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L)
+    dt = rng.uniform(-3.0, 3.0, size=dt.shape).astype(np.float32)
+    bias = rng.uniform(-1.0, 1.0, size=bias.shape).astype(np.float32)
+    A_log[:] = 12.0  # |A| ~ 1.6e5: exp(delta * A) underflows to 0 for delta > 0.005
+    y = orc.forward(2, x, dt, A_log, Bs, Cs, Ds, bias)
+    want = np.zeros((B, D, L))
+    routes = _routes(1, L, K=2)
+    for k in range(K):
+        delta = _softplus(dt[:, k].astype(np.float64) + bias[k][None, :, None])  # (B,D,L)
+        cb = np.einsum("bnt,bnt->bt", Cs[:, k].astype(np.float64), Bs[:, k].astype(np.float64))
+        pos = routes[k]
+        u = x[:, :, pos].astype(np.float64)
+        want[:, :, pos] += delta * cb[:, None, :] * u + Ds[k][None, :, None] * u
+    _close(y, want, 1e-12, 1e-14, "memoryless limit")
+
+
+def pin_routes(orc):
+    for (H, W) in [(3, 5), (1, 7), (7, 1), (4, 6), (2, 2), (5, 3)]:
+        L = H * W
+        B, K, D, N = 1, 4, 1, 2
+        x = np.ones((B, D, H, W), np.float32)
+        dt = np.zeros((B, K, D, L), np.float32)
+        bias = np.full((K, D), math.log(math.e - 1.0), np.float32)  # delta ~= 1
+        A_log = np.full((K, D, N), 12.0, np.float32)  # forget at once
+        Bs = np.zeros((B, K, N, L), np.float32)
+        Cs = np.zeros((B, K, N, L), np.float32)
+        Bs[:, :, 0, :] = 1.0
+        scale = [1.0, 2.0 ** 6, 2.0 ** 12, 2.0 ** 18]  # exact in float32 times (t + 1)
+        for k in range(K):
+            Cs[0, k, 0, :] = scale[k] * (np.arange(L) + 1)
+        Ds = np.zeros((K, D), np.float32)
+        delta = float(_softplus(float(bias[0, 0])))
+        routes = _routes(H, W)
+        for active in range(K + 1):  # each route alone, then all four summed
+            Cs2 = Cs.copy()
+            if active < K:
+                for k in range(K):
+                    if k != active:
+                        Cs2[:, k] = 0.0
+            y = orc.forward(4, x, dt, A_log, Bs, Cs2, Ds, bias)
+            want = np.zeros(L)
+            for k in range(K):
+                if active < K and k != active:
+                    continue
+                want[routes[k]] += delta * scale[k] * (np.arange(L) + 1)
+            _close(y[0, 0].reshape(-1), want, 1e-12, 0.0, f"routes {H}x{W} active={active}")
+
+
+def pin_flip(orc):
+    rng = _rng(9)
+    B, K, D, N, L = 2, 2, 2, 3, 13
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L)
+    Cs1, Ds1 = Cs.copy(), Ds.copy()
+    Cs1[:, 0] = 0.0
+    Ds1[0] = 0.0
+    y_rev = orc.forward(2, x, dt, A_log, Bs, Cs1, Ds1, bias)
+    # route 1's parameters moved to route 0, run on the flipped sequence
+    dt0, Bs0, Cs0 = dt.copy(), Bs.copy(), Cs1.copy()
+    dt0[:, 0], Bs0[:, 0], Cs0[:, 0] = dt[:, 1], Bs[:, 1], Cs1[:, 1]
+    Cs0[:, 1] = 0.0
+    A0, D0, b0 = A_log.copy(), Ds1.copy(), bias.copy()
+    A0[0], D0[0], b0[0] = A_log[1], Ds1[1], bias[1]
+    D0[1] = 0.0
+    y_fwd = orc.forward(2, np.ascontiguousarray(x[:, :, ::-1]), dt0, A0, Bs0, Cs0, D0, b0)
+    _close(y_rev, y_fwd[:, :, ::-1], 1e-14, 1e-15, "reversed route == forward on flipped")
+
+
+def _swap(a, pairs, axis):
+    out = a.copy()
+    for i, j in pairs:
+        idx_i = [slice(None)] * a.ndim
+        idx_j = [slice(None)] * a.ndim
+        idx_i[axis], idx_j[axis] = i, j
+        out[tuple(idx_i)] = a[tuple(idx_j)]
+        out[tuple(idx_j)] = a[tuple(idx_i)]
+    return out
+
+
+def pin_transpose(orc):
+    rng = _rng(10)
+    B, K, D, N, H, W = 2, 4, 2, 3, 3, 5
+    L = H * W
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, (B, D, H, W))
+    y = orc.forward(4, x, dt, A_log, Bs, Cs, Ds, bias)
+    p = [(0, 2), (1, 3)]
+    yt = orc.forward(4, np.ascontiguousarray(np.swapaxes(x, 2, 3)), _swap(dt, p, 1),
+                     _swap(A_log, p, 0), _swap(Bs, p, 1), _swap(Cs, p, 1), _swap(Ds, p, 0),
+                     _swap(bias, p, 0))
+    _close(yt, np.swapaxes(y, 2, 3), 1e-12, 1e-13, "transpose symmetry")
+
+
+def pin_rot180(orc):
+    rng = _rng(11)
+    B, K, D, N, H, W = 1, 4, 3, 2, 4, 3
+    L = H * W
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, (B, D, H, W))
+    y = orc.forward(4, x, dt, A_log, Bs, Cs, Ds, bias)
+    p = [(0, 1), (2, 3)]
+    yr = orc.forward(4, np.ascontiguousarray(x[:, :, ::-1, ::-1]), _swap(dt, p, 1),
+                     _swap(A_log, p, 0), _swap(Bs, p, 1), _swap(Cs, p, 1), _swap(Ds, p, 0),
+                     _swap(bias, p, 0))
+    _close(yr, y[:, :, ::-1, ::-1], 1e-12, 1e-13, "180-degree rotation symmetry")
+
+
+def pin_linearity(orc):
+    rng = _rng(12)
+    B, K, D, N, H, W = 2, 4, 2, 3, 4, 4
+    L = H * W
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, (B, D, H, W))
+    # dyadic values and power-of-two weights keep alpha*x1 + beta*x2 exact in float32
+    x = (np.round(64 * x) / 64).astype(np.float32)
+    x2 = (np.round(64 * rng.standard_normal(x.shape)) / 64).astype(np.float32)
+    y1 = orc.forward(4, x, dt, A_log, Bs, Cs, Ds, bias)
+    y2 = orc.forward(4, x2, dt, A_log, Bs, Cs, Ds, bias)
+    x12 = (np.float32(0.5) * x + np.float32(-2.0) * x2).astype(np.float32)
+    y12 = orc.forward(4, x12, dt, A_log, Bs, Cs, Ds, bias)
+    _close(y12, 0.5 * y1 - 2.0 * y2, 1e-11, 1e-12, "linearity in x")
+
+
+def pin_channels(orc):
+    rng = _rng(13)
+    B, K, D, N, H, W = 3, 4, 5, 2, 2, 3
+    L = H * W
+    x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, (B, D, H, W))
+    y = orc.forward(4, x, dt, A_log, Bs, Cs, Ds, bias)
+    bi = np.array([0, 2, 1, 2])
+    di = np.array([4, 0, 3, 3])
+    ys = orc.forward_channels(4, x, dt, A_log, Bs, Cs, Ds, bias, bi, di)
+    _close(ys, y[bi, di], 0.0, 0.0, "sampled channels")
+    # a channel depends on its own inputs only
+    x2 = x.copy()
+    x2[1, 2] += 5.0
+    y2 = orc.forward(4, x2, dt, A_log, Bs, Cs, Ds, bias)
+    mask = np.ones((B, D), bool)
+    mask[1, 2] = False
+    _close(y2[mask], y[mask], 0.0, 0.0, "channel isolation")
+
+
+ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
+            pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
+            pin_linearity, pin_channels]

@@ -1,0 +1,104 @@
+"""CPU tests of the oracle: its pins, planted mistakes that the pins must catch, thread
+determinism, and the stored golden output of the smallest workload."""
+import json
+import pathlib
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import oracle_pins
+
+GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build()
+    return oracle.Oracle()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# Planted mistakes: (what, original text in ss2d_oracle.c, replacement).  Every one of them
+# must make at least one pin fail.
+MUTATIONS = [
+    ("drop skip term", "out[l] += yk + Dk * u;", "out[l] += yk;"),
+    ("A sign", "A[n] = -exp(", "A[n] = exp("),
+    ("output before update",
+     "h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;\n"
+     "                yk += (double)Ck[n * L + t] * h[n];",
+     "yk += (double)Ck[n * L + t] * h[n];\n"
+     "                h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;"),
+    ("no decay", "h[n] = a * h[n] +", "h[n] = h[n] +"),
+    ("decay squared", "const double a = exp(delta * A[n]);",
+     "const double a = exp(2.0 * delta * A[n]);"),
+    ("column route transposed", "return (t % H) * W + t / H;", "return (t % W) * H + t / W;"),
+    ("route 1 not reversed", "case 1:\n        return L - 1 - t;", "case 1:\n        return t;"),
+    ("route 3 not reversed", "s = L - 1 - t;", "s = t;"),
+    ("bias outside softplus", "softplus((double)dt[t] + bias)",
+     "(softplus((double)dt[t]) + bias)"),
+    ("no delta on B", "delta * (double)Bk[n * L + t] * u", "(double)Bk[n * L + t] * u"),
+    ("softplus wrong", "return m + log1p(exp(-fabs(z)));", "return m + log1p(exp(fabs(z)));"),
+    ("C replaced by B", "yk += (double)Ck[n * L + t]", "yk += (double)Bk[n * L + t]"),
+    ("B layout (L, N)", "(double)Bk[n * L + t] * u", "(double)Bk[t * N + n] * u"),
+    ("delta read at image position", "(double)dt[t] + bias", "(double)dt[l] + bias"),
+    ("backward 1D route not reversed", "return k == 0 ? t : L - 1 - t;", "return t;"),
+    ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]", "A_log[(k * N + n) * D + d]"),
+    ("Ds indexed (D, K)", "Ds[k * D + d]", "Ds[(d * K + k) % (K * D)]"),
+    ("dt_bias shared by routes", "dt_bias[k * D + d]", "dt_bias[d]"),
+    ("x ignores batch", "x + (b * D + d) * L", "x + d * L"),
+    ("Cs ignores batch", "Cs + (b * K + k) * N * L", "Cs + k * N * L"),
+    ("state not reset per route", "            h[n] = 0.0;\n", "\n"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, what, old, new):
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation anchor for '{what}' not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(mutant_src, tmp_path / "libmutant.so")
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake '{what}'"
+
+
+def test_thread_count_does_not_change_result(orc):
+    wl = workloads.custom(B=2, D=6, H=5, W=7, N=4)
+    inp = workloads.make_inputs(wl, seed=3)
+    args = [inp[k] for k in ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")]
+    y1 = orc.forward(4, *args, threads=1)
+    y4 = orc.forward(4, *args, threads=4)
+    assert np.array_equal(y1, y4)
+
+
+def test_golden_tiny_workload(orc):
+    """The stored output of the smallest workload (written by tests/golden/make_golden.py,
+    which calls only the oracle) still matches: guards the oracle against silent drift."""
+    meta = json.loads((GOLDEN / "tiny_f32.json").read_text())
+    wl = workloads.workload(meta["workload"])
+    inp = workloads.make_inputs(wl, seed=meta["seed"])
+    y = orc.forward(wl.K, *[inp[k] for k in ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds",
+                                              "dt_bias")])
+    want = np.array(meta["y"], dtype=np.float64).reshape(y.shape)
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-15)
+
+
+def test_gcc_present():
+    assert shutil.which("gcc"), "the oracle is built with gcc"
+    out = subprocess.run(["gcc", "--version"], capture_output=True, text=True)
+    assert out.returncode == 0

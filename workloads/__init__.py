@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the SS2D forward operator and its bidirectional 1D variant.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and benchmark.
+It holds none of the operator's arithmetic: only random draws, the rounding of drawn fp32
+values to bfloat16 (round to nearest even), and the recipe that turns a uniform draw into a
+dt_bias value (the inverse of softplus, so that softplus(dt_bias) is the drawn value).
+
+Workloads (shapes from the pages' models, values synthetic):
+  * ``tiny_f32``              B=1,  D=8,   8x8     (L=64),    N=4,  K=4, fp32
+  * ``vmamba_t_stage1_f32``   B=8,  D=192, 56x56   (L=3136),  N=16, K=4, fp32
+  * ``vmamba_t_stage1_bf16``  B=64, D=192, 56x56   (L=3136),  N=16, K=4, bf16 data
+  * ``highres_1024px_bf16``   B=2,  D=192, 256x256 (L=65536), N=16, K=4, bf16 data
+  * ``vim_bidir_bf16``        B=128, D=768, L=197 (14x14 patches + cls), N=16, K=2, bf16
+
+VMamba-T stage 1 is a 224x224 image at patch 4 (56x56 tokens) with 96 channels and an
+expansion ratio of 2 (D=192) (Vision Mamba explainer page, VMamba backbone listing; the
+Chinese VMamba article, section 4).  The high-resolution case is a 1024 px image at patch 4.
+The Vim case is a 224x224 image at patch 16 plus one class token (aipaper.cc Vim summary,
+section 4.2).  ImageNet and the other datasets the pages evaluate on are not used: these
+seeded draws stand in for activations of those shapes.
+
+Value recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order, fp32):
+  1. x       ~ N(0, 1)            shape (B, D, H, W)  [(B, D, L) for K=2]
+  2. dt_raw  ~ N(0, 0.5**2)       shape (B, K, D, L)  (standard deviation 0.5)
+  3. Bs      ~ N(0, 1)            shape (B, K, N, L)
+  4. Cs      ~ N(0, 1)            shape (B, K, N, L)
+  5. v       ~ U[1e-3, 1e-1)      shape (K, D), dt_bias = log(expm1(v)) in fp64, stored fp32
+  6. A_log[k, d, n] = log(n + 1)  (the S4D-real initialisation the explainer's listing uses),
+     or, for ``a_log="random"``, a further draw A_log ~ U[log 1, log 16) of shape (K, D, N)
+  7. Ds = 1                       shape (K, D)
+For bf16 workloads x, dt_raw, Bs and Cs are rounded to bfloat16 after drawing; the returned
+fp32 arrays hold exactly the bfloat16 values, so every consumer sees the same numbers.
+dt_raw, Bs and Cs are laid out in the scan order of each route (time innermost).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    D: int
+    H: int
+    W: int
+    N: int
+    K: int
+    dtype: str  # "f32" or "bf16"
+
+    @property
+    def L(self) -> int:
+        return self.H * self.W
+
+    @property
+    def updates(self) -> int:
+        """State updates per forward call: one per (b, k, d, t, n)."""
+        return self.B * self.K * self.D * self.L * self.N
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the operator must move: x read once, dt_raw, Bs, Cs read once, y written
+        once, plus the fp32 parameters A_log, Ds, dt_bias."""
+        e = self.elem_bytes
+        B, K, D, L, N = self.B, self.K, self.D, self.L, self.N
+        return e * (B * D * L + B * K * D * L + 2 * B * K * N * L + B * D * L) + 4 * (
+            K * D * N + 2 * K * D)
+
+    def as_dict(self) -> dict:
+        return dict(name=self.name, B=self.B, D=self.D, H=self.H, W=self.W, L=self.L,
+                    N=self.N, K=self.K, dtype=self.dtype)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 8, 8, 8, 4, 4, "f32"),
+    "vmamba_t_stage1_f32": Workload("vmamba_t_stage1_f32", 8, 192, 56, 56, 16, 4, "f32"),
+    "vmamba_t_stage1_bf16": Workload("vmamba_t_stage1_bf16", 64, 192, 56, 56, 16, 4, "bf16"),
+    "highres_1024px_bf16": Workload("highres_1024px_bf16", 2, 192, 256, 256, 16, 4, "bf16"),
+    "vim_bidir_bf16": Workload("vim_bidir_bf16", 128, 768, 1, 197, 16, 2, "bf16"),
+}
+ORDER = ["tiny_f32", "vmamba_t_stage1_f32", "vmamba_t_stage1_bf16", "highres_1024px_bf16",
+         "vim_bidir_bf16"]
+
+
+def workload(name_or_index) -> Workload:
+    if isinstance(name_or_index, int):
+        return WORKLOADS[ORDER[name_or_index]]
+    return WORKLOADS[name_or_index]
+
+
+def custom(B, D, H, W, N, K=4, dtype="f32", name="custom") -> Workload:
+    return Workload(name, B, D, H, W, N, K, dtype)
+
+
+# ---------------------------------------------------------------------------------------
+# bfloat16 rounding of drawn values (round to nearest, ties to even; NaN stays NaN)
+# ---------------------------------------------------------------------------------------
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 array holding the bfloat16 (RNE) value of each element of ``a``."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(a))
+
+
+# ---------------------------------------------------------------------------------------
+# Draws
+# ---------------------------------------------------------------------------------------
+def inverse_softplus(v: np.ndarray) -> np.ndarray:
+    """z with log(1 + e^z) = v, for v > 0 (input recipe for dt_bias)."""
+    return np.log(np.expm1(np.asarray(v, dtype=np.float64)))
+
+
+def make_inputs(wl: Workload, seed: int = 0, a_log: str = "init") -> dict:
+    """Seeded inputs for one workload, as fp32 numpy arrays (bf16-exact for bf16 workloads).
+
+    Returns a dict with x, dt_raw, A_log, Bs, Cs, Ds, dt_bias and, for bf16 workloads, the
+    raw bfloat16 bit patterns of x, dt_raw, Bs and Cs under ``<name>_bf16``.
+    """
+    rng = np.random.default_rng(seed)
+    B, D, K, N, L = wl.B, wl.D, wl.K, wl.N, wl.L
+    xshape = (B, D, L) if wl.K == 2 else (B, D, wl.H, wl.W)
+    x = rng.standard_normal(xshape, dtype=np.float32)
+    dt_raw = rng.standard_normal((B, K, D, L), dtype=np.float32)
+    dt_raw *= np.float32(0.5)
+    Bs = rng.standard_normal((B, K, N, L), dtype=np.float32)
+    Cs = rng.standard_normal((B, K, N, L), dtype=np.float32)
+    v = rng.uniform(1e-3, 1e-1, size=(K, D))
+    dt_bias = inverse_softplus(v).astype(np.float32)
+    if a_log == "init":
+        A_log = np.broadcast_to(np.log(np.arange(1, N + 1, dtype=np.float64)),
+                                (K, D, N)).astype(np.float32)
+    elif a_log == "random":
+        A_log = rng.uniform(0.0, np.log(16.0), size=(K, D, N)).astype(np.float32)
+    else:
+        raise ValueError(f"a_log must be 'init' or 'random', not {a_log!r}")
+    Ds = np.ones((K, D), dtype=np.float32)
+    out = dict(x=x, dt_raw=dt_raw, A_log=np.ascontiguousarray(A_log), Bs=Bs, Cs=Cs, Ds=Ds,
+               dt_bias=dt_bias)
+    if wl.dtype == "bf16":
+        for key in ("x", "dt_raw", "Bs", "Cs"):
+            bits = f32_to_bf16_bits(out[key])
+            out[key + "_bf16"] = bits
+            out[key] = bf16_bits_to_f32(bits)
+    elif wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype!r}")
+    return out
