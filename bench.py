@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the SS2D forward operator on one MI355X.
+
+A step is one full forward call (transpose, scan, merge: every kernel of the operator) on
+one batch of seeded synthetic input already resident in HBM.  W untimed warm-up steps, then
+K timed steps between device synchronisations, timed with HIP events on the stream the
+library launches on.  Prints ONE JSON line on stdout (details go to stderr):
+
+  value        state updates per second (B*K*D*L*N per step / seconds per step)
+  roofline     the dominant kernel (the scan) against the fp32 VALU peak
+  cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = ("SS2D fwd state-updates/s (B·K·D·L·N) + achieved HBM GB/s, "
+          "VMamba-T stage1")
+# fp32 VALU peak without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# Arithmetic of one state update: delta*A (mul), (delta*u)*B (mul), h update (FMA),
+# C*h accumulation (FMA) = 6 flops; the exp of each update is a transcendental, not a flop.
+FLOPS_PER_UPDATE = 6
+HBM_PEAK_GBPS = 8000.0
+ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted((ROOT / "selective_scan_ss2d_amd" / "csrc").glob("*")) + [
+        ROOT / "include" / "ss2d.h"]
+    for f in files:
+        if f.suffix in (".hip", ".inc", ".h"):
+            h.update(f.name.encode())
+            h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scan launch from the committed counter summary, if it was taken on the
+    current kernel sources; else None."""
+    f = ROOT / "profiles" / f"traffic_{workload}.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+    except ValueError:
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, target_s: float) -> dict:
+    """The float64 oracle, as it is, on all host cores, over a bounded sample of channels."""
+    import numpy as np
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.Oracle()
+    args = [inp[k] for k in ARGS]
+    total = wl.B * wl.D
+    rng = np.random.default_rng(0)
+    n = min(total, max(cores, 64))
+    order = rng.permutation(total)
+    t0 = time.perf_counter()
+    sel = order[:n]
+    orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores)
+    dt = time.perf_counter() - t0
+    if n < total and dt < target_s:
+        n = int(min(total, max(n, n * target_s / max(dt, 1e-3))))
+        sel = order[:n]
+        t0 = time.perf_counter()
+        orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores)
+        dt = time.perf_counter() - t0
+    upd = n * wl.K * wl.L * wl.N
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
+            "kind": "oracle",
+            "sample": f"{n} of {total} (b,d) channels of {wl.name} (all {wl.K} routes, full "
+                      f"L={wl.L}, N={wl.N}), {upd:.3e} state updates in {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vmamba_t_stage1_bf16")
+    ap.add_argument("--a-log", default="init", choices=["init", "random"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the operator on one GPU only: it has no multi-GPU path "
+              "(sharding across GPUs is described in DESIGN.md, not implemented). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import selective_scan_ss2d_amd as ss
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    ss.load_library()  # raises when the HIP library is not built: there is no fallback
+    wl = workloads.workload(args.workload)
+    log(f"workload {wl.name}: {wl.as_dict()}; generating seeded inputs")
+    inp = workloads.make_inputs(wl, seed=0, a_log=args.a_log)
+    dev = {}
+    for k in ("x", "dt_raw", "Bs", "Cs"):
+        if wl.dtype == "bf16":
+            dev[k] = torch.from_numpy(inp[k + "_bf16"].view(np.int16)).view(torch.bfloat16)
+        else:
+            dev[k] = torch.from_numpy(inp[k])
+        dev[k] = dev[k].to("cuda:0")
+    for k in ("A_log", "Ds", "dt_bias"):
+        dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
+    fn = ss.ss2d_forward if wl.K == 4 else ss.ss1d_bidir_forward
+    y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
+    call = lambda: fn(*[dev[k] for k in ARGS], y=y)  # noqa: E731
+
+    log(f"warm-up {args.warmup} steps")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ss.timing_enable(True)
+    ss.timing_read()  # clear
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ss.timing_enable(False)
+    kernels = ss.timing_read()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    upd_per_s = wl.updates / (ms_step / 1e3)
+    alg_bytes = wl.algorithmic_bytes()
+    gbps = alg_bytes / (ms_step / 1e3) / 1e9
+    for name, (ms, n) in kernels.items():
+        if n:
+            log(f"  kernel {name:10s}: {n} launches, {ms / n * 1e3:9.1f} us avg")
+    log(f"step {ms_step * 1e3:.1f} us, {upd_per_s:.4e} updates/s, algorithmic {gbps:.1f} GB/s")
+
+    # Dominant kernel: the scan (with the chunked plan, both scan passes are counted).
+    scan_ms, scan_n = kernels["scan"]
+    agg_ms, _ = kernels["chunk_agg"]
+    scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
+    achieved = wl.updates * FLOPS_PER_UPDATE / scan_avg_s / 1e12
+    traffic = measured_traffic(wl.name)
+    roofline = {"bound": "alu", "achieved": round(achieved, 3),
+                "peak": round(VALU_FP32_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "k_scan", "kernel_avg_us": round(scan_avg_s * 1e6, 1),
+                "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        log(f"  {cpu['sample']} on {cpu['cores']} threads: {cpu['value']:.3e} updates/s")
+
+    out = {
+        "metric": METRIC,
+        "value": upd_per_s,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "H": wl.H, "W": wl.W,
+                   "L": wl.L, "N": wl.N, "K": wl.K, "io_dtype": wl.dtype,
+                   "state_dtype": "f32", "A_log": args.a_log},
+        "hbm_gbps_algorithmic": round(gbps, 1),
+        "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),
+        "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kernels.items() if n},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,131 @@
+/*
+ * ss2d.h -- C ABI of libss2d.so, the MI355X (gfx950) SS2D forward operator.
+ *
+ * The operator (VMamba's 2D selective scan, "SS2D"):
+ *   1. Cross-scan: a (B, D, H, W) feature map is read along four routes, each a sequence of
+ *      length L = H * W over every channel d:
+ *        route 0  row-major              pi_0(t) = t
+ *        route 1  row-major, reversed    pi_1(t) = L - 1 - t
+ *        route 2  column-major           pi_2(t) = (t mod H) * W + floor(t / H)
+ *        route 3  column-major, reversed pi_3(t) = pi_2(L - 1 - t)
+ *      (pi_k(t) is the raster index h * W + w visited at step t.)  Sources: the "Vision
+ *      Mamba" explainer (dileepadev), CrossScanModule listing and its prose; the Chinese
+ *      VMamba article (mhpn.cn), section 1, cross_scan; the VMamba review (nubint.ai),
+ *      "Proposed method" (Cross-Scan Module with four routes).
+ *   2. Selective scan on every route k and channel d, from a zero state h (N values):
+ *        delta_t = softplus(dt_raw[b,k,d,t] + dt_bias[k,d])
+ *        A_n     = -exp(A_log[k,d,n])
+ *        h_n     = exp(delta_t * A_n) * h_n + delta_t * Bs[b,k,n,t] * x[b,d,pi_k(t)]
+ *        y_k,t   = sum_n Cs[b,k,n,t] * h_n + Ds[k,d] * x[b,d,pi_k(t)]
+ *      Sources: the explainer's SelectiveSSM listing (softplus of the dt projection with
+ *      its bias, A = -exp(A_log), the exp discretisation of A and delta * B for B, zero
+ *      initial state, output after the update, D skip term); the Vim summary (aipaper.cc),
+ *      section 4.1 (discrete recurrence); one independent parameter set per route (the
+ *      explainer's four SSMs).
+ *   3. Cross-merge: y[b,d,pi_k(t)] = sum over k of y_k,t, each route's permutation undone
+ *      and the routes summed (the explainer's CrossScanModule: inverse flips and
+ *      transposes, outputs summed).
+ *   ss1d_bidir_forward is the K = 2 case over a 1D sequence: route 0 forward, route 1 over
+ *   the reversed sequence, summed after undoing the reversal (Vim summary, section 4.3).
+ *
+ * Precision: x, dt_raw, Bs, Cs and y share one data type (fp32 or bfloat16); A_log, Ds and
+ * dt_bias are always fp32.  delta, the state h and every sum are fp32; y is rounded once
+ * (round to nearest even for bfloat16).  The state never leaves the chip.
+ *
+ * Layouts (contiguous, row-major, device pointers, caller-owned):
+ *   x, y      (B, D, H, W)          [ss1d_bidir_forward: (B, D, L)]
+ *   dt_raw    (B, K, D, L)          in the scan order of route k (index t = step t)
+ *   Bs, Cs    (B, K, N, L)          in the scan order of route k
+ *   A_log     (K, D, N)  fp32
+ *   Ds        (K, D)     fp32
+ *   dt_bias   (K, D)     fp32
+ * with K = 4 for ss2d_forward and K = 2 for ss1d_bidir_forward.
+ *
+ * Conventions shared by every entry point:
+ *   - Inputs are read only.  y is written in full (no pre-zeroing needed) and must not
+ *     overlap any input.
+ *   - All arguments are validated before anything is enqueued; on an error nothing is
+ *     launched and y is untouched.  Nothing is printed and no exception crosses the ABI.
+ *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default stream).
+ *     Faults inside the kernels surface at the caller's next synchronisation.
+ *   - The library keeps no state between calls.  Internal scratch (a transposed copy of x,
+ *     per-route fp32 partial outputs, chunk carries) is taken from HIP's stream-ordered
+ *     allocator on `stream` and released on `stream` in the same call.
+ *   - Results are deterministic: identical inputs, shapes and device give bitwise identical
+ *     y (no atomics; the routes are summed in the fixed order 0, 1, 2, 3).
+ *   - B == 0 or D == 0 is a valid empty call: it returns SS2D_OK, launches nothing and reads
+ *     no pointer.
+ *   - Thread safety: calls from several host threads are safe; calls on different streams
+ *     run independently.
+ */
+#ifndef SS2D_H
+#define SS2D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS2D_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+#define SS2D_OK 0
+#define SS2D_ERR_NULL 1        /* a required pointer is NULL                                */
+#define SS2D_ERR_SHAPE 2       /* a negative dimension, H/W/L/N < 1, or a size beyond the
+                                  kernels' index range (L >= 2^30, or any tensor with
+                                  2^62 elements or more)                                   */
+#define SS2D_ERR_UNSUPPORTED 3 /* N not in {1, 2, 4, 8, 16, 32}, or an unknown dtype        */
+#define SS2D_ERR_ALIGN 4       /* a pointer not aligned to its element size                 */
+#define SS2D_ERR_HIP 5         /* a HIP runtime call failed (see ss2d_last_hip_error)       */
+#define SS2D_ERR_ALIAS 6       /* y overlaps an input                                        */
+
+/* Data types of x, dt_raw, Bs, Cs and y. */
+#define SS2D_F32 0
+#define SS2D_BF16 1
+
+/* Four-route SS2D forward.  x, y: (B, D, H, W); dt_raw: (B, 4, D, L); Bs, Cs: (B, 4, N, L);
+ * A_log: (4, D, N); Ds, dt_bias: (4, D); L = H * W.  dtype is SS2D_F32 or SS2D_BF16.
+ * Returns SS2D_OK or one of the SS2D_ERR_* codes above. */
+int ss2d_forward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                 const void *Cs, const float *Ds, const float *dt_bias, void *y, int64_t B,
+                 int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void *stream);
+
+/* Bidirectional 1D selective scan forward (Vim block: forward route plus reversed route,
+ * summed).  x, y: (B, D, L); dt_raw: (B, 2, D, L); Bs, Cs: (B, 2, N, L); A_log: (2, D, N);
+ * Ds, dt_bias: (2, D).  Same dtypes, errors and conventions as ss2d_forward. */
+int ss1d_bidir_forward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                       const void *Cs, const float *Ds, const float *dt_bias, void *y,
+                       int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *ss2d_status_string(int status);
+
+/* SS2D_ABI_VERSION of the loaded library. */
+int ss2d_abi_version(void);
+
+/* hipError_t value of the last failed HIP call made by this library on the calling thread
+ * (0 if none). */
+int ss2d_last_hip_error(void);
+
+/* ---- kernel timing (measurement support, not part of the operator) -----------------------
+ * While enabled on a host thread, every call from that thread brackets each kernel launch
+ * with a pair of HIP events on the call's stream.  ss2d_timing_read waits for the recorded
+ * events, adds each kernel's duration to its kind, writes per-kind totals (milliseconds)
+ * and launch counts to ms[SS2D_KERNEL_KINDS] and launches[SS2D_KERNEL_KINDS] (either may be
+ * NULL), and clears the record.  ss2d_timing_enable returns the previous setting. */
+#define SS2D_KERNEL_TRANSPOSE 0 /* per-plane transpose of x for the column routes      */
+#define SS2D_KERNEL_SCAN 1      /* selective scan producing per-route outputs          */
+#define SS2D_KERNEL_CHUNK_AGG 2 /* chunked scan, first pass (chunk end states)         */
+#define SS2D_KERNEL_CARRY 3     /* chunk carries                                       */
+#define SS2D_KERNEL_MERGE 4     /* cross-merge into y                                  */
+#define SS2D_KERNEL_KINDS 5
+int ss2d_timing_enable(int enable);
+int ss2d_timing_read(double *ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS2D_H */

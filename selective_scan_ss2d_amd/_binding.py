@@ -1,0 +1,201 @@
+"""ctypes binding of libss2d.so.
+
+Argument marshalling only: shapes, dtypes and devices are checked, device pointers and the
+current HIP stream are passed through, and every step of the operator runs in the library's
+HIP kernels.  PyTorch supplies device memory and streams.  There is no fallback: when the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import threading
+
+PKG = pathlib.Path(__file__).resolve().parent
+LIBRARY_PATH = PKG / "libss2d.so"
+
+SS2D_OK = 0
+SS2D_ERR_NULL = 1
+SS2D_ERR_SHAPE = 2
+SS2D_ERR_UNSUPPORTED = 3
+SS2D_ERR_ALIGN = 4
+SS2D_ERR_HIP = 5
+SS2D_ERR_ALIAS = 6
+SS2D_F32 = 0
+SS2D_BF16 = 1
+
+# Every symbol include/ss2d.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "ss2d_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 5 + [ctypes.c_int, _P]),
+    "ss1d_bidir_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 4 + [ctypes.c_int, _P]),
+    "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ss2d_abi_version": (ctypes.c_int, []),
+    "ss2d_last_hip_error": (ctypes.c_int, []),
+    "ss2d_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "ss2d_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]),
+}
+KERNEL_KINDS = ("transpose", "scan", "chunk_agg", "carry", "merge")
+
+
+class SS2DError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
+    """Load libss2d.so (once) and attach signatures.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = pathlib.Path(path) if path is not None else LIBRARY_PATH
+        if not p.exists():
+            raise RuntimeError(
+                f"{p} is not built; run `python -m selective_scan_ss2d_amd.build` "
+                "(the SS2D operator has no fallback path)")
+        lib = ctypes.CDLL(str(p))
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return load_library().ss2d_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load_library().ss2d_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != SS2D_OK:
+        lib = load_library()
+        msg = lib.ss2d_status_string(status).decode()
+        if status == SS2D_ERR_HIP:
+            msg += f" (hipError_t {lib.ss2d_last_hip_error()})"
+        raise SS2DError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SS2D_F32
+    if t.dtype == torch.bfloat16:
+        return SS2D_BF16
+    raise TypeError(f"x must be float32 or bfloat16, not {t.dtype}")
+
+
+def _expect(name, t, shape, dtype, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _common(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, xshape, L):
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    B, D = x.shape[0], x.shape[1]
+    N = A_log.shape[-1] if A_log.dim() == 3 else -1
+    dt = x.dtype
+    _dtype_code(x)
+    dev = x.device
+    _expect("x", x, xshape, dt, dev)
+    _expect("dt_raw", dt_raw, (B, K, D, L), dt, dev)
+    _expect("A_log", A_log, (K, D, N), torch.float32, dev)
+    _expect("Bs", Bs, (B, K, N, L), dt, dev)
+    _expect("Cs", Cs, (B, K, N, L), dt, dev)
+    _expect("Ds", Ds, (K, D), torch.float32, dev)
+    _expect("dt_bias", dt_bias, (K, D), torch.float32, dev)
+    if y is None:
+        y = torch.empty(xshape, dtype=dt, device=dev)
+    else:
+        _expect("y", y, xshape, dt, dev)
+    return B, D, N, y
+
+
+def ss2d_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y=None, stream=None):
+    """Four-route SS2D forward on the GPU.
+
+    x (B, D, H, W); dt_raw (B, 4, D, L); Bs, Cs (B, 4, N, L) in each route's scan order;
+    A_log (4, D, N), Ds (4, D), dt_bias (4, D) fp32.  x, dt_raw, Bs, Cs (and y) share one
+    dtype, float32 or bfloat16.  Returns y (B, D, H, W), enqueued on the current stream.
+    """
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    B, D, N, y = _common(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, (B, D, H, W), H * W)
+    status = lib.ss2d_forward(x.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(),
+                              Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(), dt_bias.data_ptr(),
+                              y.data_ptr(), B, D, H, W, N, _dtype_code(x),
+                              _stream_handle(x.device, stream))
+    _check(status)
+    return y
+
+
+def ss1d_bidir_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y=None, stream=None):
+    """Bidirectional (forward + reversed) 1D selective scan on the GPU.
+
+    x (B, D, L); dt_raw (B, 2, D, L); Bs, Cs (B, 2, N, L); A_log (2, D, N), Ds (2, D),
+    dt_bias (2, D) fp32.  Returns y (B, D, L).
+    """
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    B, D, N, y = _common(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, (B, D, L), L)
+    status = lib.ss1d_bidir_forward(x.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(),
+                                    Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
+                                    dt_bias.data_ptr(), y.data_ptr(), B, D, L, N,
+                                    _dtype_code(x), _stream_handle(x.device, stream))
+    _check(status)
+    return y
+
+
+def timing_enable(enable: bool = True) -> bool:
+    """Bracket every kernel launched from this host thread with HIP events (measurement)."""
+    return bool(load_library().ss2d_timing_enable(1 if enable else 0))
+
+
+def timing_read() -> dict:
+    """Per-kernel-kind total milliseconds and launch counts since the last read."""
+    lib = load_library()
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib.ss2d_timing_read(ms, cnt))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}

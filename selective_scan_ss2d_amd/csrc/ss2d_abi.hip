@@ -1,0 +1,376 @@
+// C ABI of the SS2D forward library: argument validation, the launch plan, stream-ordered
+// scratch, and the kernel sequence (transpose -> scan [-> carry -> scan] -> merge).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+#include "ss2d.h"
+#include "ss2d_device.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Per-thread kernel timing record (see ss2d_timing_enable / ss2d_timing_read).
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  bool enabled = false;
+  std::vector<TimedLaunch> launches;
+  ~Timing() {
+    for (auto& t : launches) {
+      (void)hipEventDestroy(t.start);
+      (void)hipEventDestroy(t.stop);
+    }
+  }
+};
+thread_local Timing g_timing;
+
+// Runs `launch` (which enqueues one kernel on `st` and returns a hipError_t value), between
+// two recorded events when timing is enabled on this thread.
+template <typename F>
+int timed(int kind, hipStream_t st, F&& launch) {
+  if (!g_timing.enabled) return launch();
+  TimedLaunch t{kind, nullptr, nullptr};
+  if (hipEventCreate(&t.start) != hipSuccess) return launch();
+  if (hipEventCreate(&t.stop) != hipSuccess) {
+    (void)hipEventDestroy(t.start);
+    return launch();
+  }
+  (void)hipEventRecord(t.start, st);
+  const int rc = launch();
+  (void)hipEventRecord(t.stop, st);
+  g_timing.launches.push_back(t);
+  return rc;
+}
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return SS2D_ERR_HIP;
+}
+
+// Scratch comes from the device's default stream-ordered pool.  Keeping freed blocks in
+// the pool (instead of returning them to the driver at every synchronisation) makes the
+// per-call allocation a cheap pool hit after the first call.
+int prepare_pool(int device) {
+  static std::mutex mu;
+  static bool done[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0 || device >= 64 || done[device]) return SS2D_OK;
+  hipMemPool_t pool;
+  hipError_t e = hipDeviceGetDefaultMemPool(&pool, device);
+  if (e != hipSuccess) return hip_fail(e);
+  uint64_t threshold = UINT64_MAX;
+  e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+  if (e != hipSuccess) return hip_fail(e);
+  done[device] = true;
+  return SS2D_OK;
+}
+
+int64_t env_int(const char* name, int64_t fallback) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long long r = std::strtoll(v, &end, 10);
+  return (end && *end == '\0') ? static_cast<int64_t>(r) : fallback;
+}
+
+constexpr int64_t kMaxL = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+constexpr int kMaxGridZ = 65535;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a == 0 || b == 0) { *out = 0; return true; }
+  if (a > kMaxElems / b) return false;
+  *out = a * b;
+  return true;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + static_cast<uintptr_t>(bbytes) && pb < pa + static_cast<uintptr_t>(abytes);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Plan {
+  int split = 1;        // lanes per channel
+  int num_chunks = 1;
+  int chunk_len = 0;
+  bool vec = false;
+  bool need_xt = false;
+  size_t off_xt = 0, off_yr = 0, off_hend = 0, off_dsum = 0, off_hin = 0, bytes = 0;
+};
+
+// Launch plan.  The scan needs about three waves per SIMD (256 CUs x 4 SIMDs) to keep the
+// VALU issuing; one lane per channel gives B*K*ceil(D/64) waves.  When that is too few,
+// first split each channel's states over 4 lanes (cheap); failing that, cut time into
+// chunks (each chunk scanned twice: once for its carry, once for its outputs).
+Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+               const void* x, const void* dt_raw) {
+  Plan p;
+  const int64_t L = H * W;
+  const int64_t e = dtype == SS2D_F32 ? 4 : 2;
+  const int64_t waves1 = B * K * ((D + 63) / 64);
+  const int64_t waves4 = B * K * ((4 * D + 63) / 64);
+  const int64_t kTargetWaves = 2048;
+  int split = 1;
+  int64_t chunk = 0;
+  if (waves1 < kTargetWaves) {
+    if (N % 4 == 0 && waves4 >= 1536) {
+      split = 4;
+    } else {
+      const int64_t want = (3072 + waves1 - 1) / waves1;  // chunks wanted
+      int64_t len = (L + want - 1) / want;
+      len = ((len + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
+      if (len < 64) len = 64;
+      if (len < L) chunk = len;
+    }
+  }
+  const int64_t forced_split = env_int("SS2D_SPLIT", 0);
+  const int64_t forced_chunk = env_int("SS2D_CHUNK_LEN", -1);
+  if (forced_split == 1 || forced_split == 2 || forced_split == 4) split = int(forced_split);
+  if (split > N || N % split != 0) split = 1;
+  if (forced_chunk >= 0) {
+    int64_t len = ((forced_chunk + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
+    chunk = (len > 0 && len < L) ? len : 0;
+  }
+  if (chunk > 0) split = 1;  // the chunked passes run one lane per channel
+  p.split = split;
+  if (chunk > 0) {
+    p.chunk_len = static_cast<int>(chunk);
+    p.num_chunks = static_cast<int>((L + chunk - 1) / chunk);
+  } else {
+    p.num_chunks = 1;
+    p.chunk_len = static_cast<int>(((L + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) *
+                                   ss2d::kChunkAlign);
+  }
+  const int vec_elems = dtype == SS2D_F32 ? 4 : 8;
+  p.vec = (L % vec_elems == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+          (reinterpret_cast<uintptr_t>(dt_raw) % 16 == 0);
+  p.need_xt = (K == 4) && H > 1 && W > 1;
+  size_t off = 0;
+  if (p.need_xt) {
+    p.off_xt = off;
+    off = align256(off + size_t(B * D * L * e));
+  }
+  p.off_yr = off;
+  off = align256(off + size_t(B * K * D * L) * 4);
+  if (p.num_chunks > 1) {
+    const size_t rows = size_t(B * K * D) * size_t(p.num_chunks);
+    p.off_hend = off;
+    off = align256(off + rows * size_t(N) * 4);
+    p.off_dsum = off;
+    off = align256(off + rows * 4);
+    p.off_hin = off;
+    off = align256(off + rows * size_t(N) * 4);
+  }
+  p.bytes = off;
+  return p;
+}
+
+int run_scan(const ss2d::ScanArgs& a, int dtype, int split, bool vec, int mode,
+             hipStream_t st) {
+  return dtype == SS2D_F32 ? ss2d::launch_scan_f32(a, split, vec, mode, st)
+                           : ss2d::launch_scan_bf16(a, split, vec, mode, st);
+}
+
+// Launch one scan pass over all images, in batches that keep gridDim.z within range.
+int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, hipStream_t st) {
+  const int64_t B = a.B;
+  const int64_t per = a.chunks_in_launch > 0 ? a.chunks_in_launch : 1;
+  const int64_t max_b = kMaxGridZ / per > 0 ? kMaxGridZ / per : 1;
+  const int64_t L = a.L, D = a.D, K = a.K, N = a.N, C = a.num_chunks;
+  for (int64_t b0 = 0; b0 < B; b0 += max_b) {
+    const int64_t nb = (B - b0 < max_b) ? (B - b0) : max_b;
+    ss2d::ScanArgs s = a;
+    s.B = static_cast<int>(nb);
+    s.x_row = static_cast<const char*>(a.x_row) + b0 * D * L * e;
+    s.x_col = static_cast<const char*>(a.x_col) + b0 * D * L * e;
+    s.dt_raw = static_cast<const char*>(a.dt_raw) + b0 * K * D * L * e;
+    s.Bs = static_cast<const char*>(a.Bs) + b0 * K * N * L * e;
+    s.Cs = static_cast<const char*>(a.Cs) + b0 * K * N * L * e;
+    s.y_route = a.y_route + b0 * K * D * L;
+    if (a.h_end) s.h_end = a.h_end + b0 * K * D * C * N;
+    if (a.delta_sum) s.delta_sum = a.delta_sum + b0 * K * D * C;
+    if (a.h_in) s.h_in = a.h_in + b0 * K * D * C * N;
+    const int kind = mode == ss2d::kModeAgg ? SS2D_KERNEL_CHUNK_AGG : SS2D_KERNEL_SCAN;
+    const int rc = timed(kind, st, [&] { return run_scan(s, dtype, p.split, p.vec, mode, st); });
+    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc));
+  }
+  return SS2D_OK;
+}
+
+int forward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+            const void* Cs, const float* Ds, const float* dt_bias, void* y, int64_t B,
+            int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+  // ---- validation (nothing is enqueued before all of it passes) -------------------------
+  if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
+  if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
+  if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS2D_ERR_UNSUPPORTED;
+  if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
+  const int64_t L = H * W;
+  if (D >= (int64_t(1) << 31) / 4 || B >= (int64_t(1) << 31)) return SS2D_ERR_SHAPE;
+  int64_t n_x, n_dt, n_bc, tmp;
+  if (!mul_ok(B, D, &tmp) || !mul_ok(tmp, L, &n_x)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
+  if (B == 0 || D == 0) return SS2D_OK;
+  if (!x || !dt_raw || !A_log || !Bs || !Cs || !Ds || !dt_bias || !y) return SS2D_ERR_NULL;
+  const int64_t e = dtype == SS2D_F32 ? 4 : 2;
+  const uintptr_t emask = static_cast<uintptr_t>(e - 1);
+  for (const void* ptr : {x, dt_raw, Bs, Cs, static_cast<const void*>(y)})
+    if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
+  for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
+                          static_cast<const void*>(dt_bias)})
+    if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
+  const int64_t y_bytes = n_x * e;
+  if (overlaps(y, y_bytes, x, n_x * e) || overlaps(y, y_bytes, dt_raw, n_dt * e) ||
+      overlaps(y, y_bytes, Bs, n_bc * e) || overlaps(y, y_bytes, Cs, n_bc * e) ||
+      overlaps(y, y_bytes, A_log, int64_t(K) * D * N * 4) ||
+      overlaps(y, y_bytes, Ds, int64_t(K) * D * 4) ||
+      overlaps(y, y_bytes, dt_bias, int64_t(K) * D * 4))
+    return SS2D_ERR_ALIAS;
+
+  // ---- plan and scratch --------------------------------------------------------------
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0;
+  hipError_t he = hipGetDevice(&device);
+  if (he != hipSuccess) return hip_fail(he);
+  int rc = prepare_pool(device);
+  if (rc != SS2D_OK) return rc;
+  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, dt_raw);
+  char* ws = nullptr;
+  he = hipMallocAsync(reinterpret_cast<void**>(&ws), p.bytes, st);
+  if (he != hipSuccess) return hip_fail(he);
+
+  ss2d::ScanArgs a{};
+  a.x_row = x;
+  a.x_col = p.need_xt ? static_cast<const void*>(ws + p.off_xt) : x;
+  a.dt_raw = dt_raw;
+  a.Bs = Bs;
+  a.Cs = Cs;
+  a.A_log = A_log;
+  a.Ds = Ds;
+  a.dt_bias = dt_bias;
+  a.y_route = reinterpret_cast<float*>(ws + p.off_yr);
+  a.B = static_cast<int>(B);
+  a.K = K;
+  a.D = static_cast<int>(D);
+  a.L = static_cast<int>(L);
+  a.N = static_cast<int>(N);
+  a.num_chunks = p.num_chunks;
+  a.chunk_len = p.chunk_len;
+
+  int err = 0;
+  if (p.need_xt)
+    err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
+      return ss2d::launch_transpose(x, ws + p.off_xt, a.B, a.D, static_cast<int>(H),
+                                    static_cast<int>(W), dtype, st);
+    });
+  if (!err && p.num_chunks > 1) {
+    a.h_end = reinterpret_cast<float*>(ws + p.off_hend);
+    a.delta_sum = reinterpret_cast<float*>(ws + p.off_dsum);
+    a.h_in = reinterpret_cast<float*>(ws + p.off_hin);
+    ss2d::ScanArgs agg = a;  // aggregates of chunks 0 .. C-2
+    agg.chunk_base = 0;
+    agg.chunks_in_launch = p.num_chunks - 1;
+    rc = scan_pass(agg, dtype, p, ss2d::kModeAgg, e, st);
+    if (rc == SS2D_OK) {
+      err = timed(SS2D_KERNEL_CARRY, st, [&] { return ss2d::launch_carry(a, st); });
+      if (!err) {
+        ss2d::ScanArgs out = a;
+        out.chunk_base = 0;
+        out.chunks_in_launch = p.num_chunks;
+        rc = scan_pass(out, dtype, p, ss2d::kModeOut, e, st);
+      }
+    }
+  } else if (!err) {
+    a.chunk_base = 0;
+    a.chunks_in_launch = 1;
+    rc = scan_pass(a, dtype, p, ss2d::kModeOut, e, st);
+  }
+  if (!err && rc == SS2D_OK) {
+    err = timed(SS2D_KERNEL_MERGE, st, [&] {
+      return (K == 4) ? ss2d::launch_merge4(a.y_route, y, a.B, a.D, static_cast<int>(H),
+                                            static_cast<int>(W), dtype, st)
+                      : ss2d::launch_merge2(a.y_route, y, a.B, a.D, a.L, dtype, st);
+    });
+  }
+  const hipError_t fe = hipFreeAsync(ws, st);
+  if (err) return hip_fail(static_cast<hipError_t>(err));
+  if (rc != SS2D_OK) return rc;
+  if (fe != hipSuccess) return hip_fail(fe);
+  return SS2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss2d_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                 const void* Cs, const float* Ds, const float* dt_bias, void* y, int64_t B,
+                 int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, B, D, H, W, N, dtype, stream);
+}
+
+int ss1d_bidir_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                       const void* Cs, const float* Ds, const float* dt_bias, void* y,
+                       int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
+  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, B, D, 1, L, N, dtype, stream);
+}
+
+const char* ss2d_status_string(int status) {
+  switch (status) {
+    case SS2D_OK: return "success";
+    case SS2D_ERR_NULL: return "a required pointer is NULL";
+    case SS2D_ERR_SHAPE: return "invalid or out-of-range dimensions";
+    case SS2D_ERR_UNSUPPORTED: return "unsupported state size N or data type";
+    case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SS2D_ERR_HIP: return "a HIP runtime call failed";
+    case SS2D_ERR_ALIAS: return "the output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int ss2d_abi_version(void) { return SS2D_ABI_VERSION; }
+
+int ss2d_last_hip_error(void) { return g_last_hip_error; }
+
+int ss2d_timing_enable(int enable) {
+  const int prev = g_timing.enabled ? 1 : 0;
+  g_timing.enabled = enable != 0;
+  return prev;
+}
+
+int ss2d_timing_read(double* ms, int64_t* launches) {
+  double tot[SS2D_KERNEL_KINDS] = {};
+  int64_t cnt[SS2D_KERNEL_KINDS] = {};
+  int status = SS2D_OK;
+  for (auto& t : g_timing.launches) {
+    float e = 0.0f;
+    hipError_t he = hipEventSynchronize(t.stop);
+    if (he == hipSuccess) he = hipEventElapsedTime(&e, t.start, t.stop);
+    if (he != hipSuccess) {
+      status = hip_fail(he);
+    } else if (t.kind >= 0 && t.kind < SS2D_KERNEL_KINDS) {
+      tot[t.kind] += e;
+      cnt[t.kind] += 1;
+    }
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_timing.launches.clear();
+  for (int i = 0; i < SS2D_KERNEL_KINDS; ++i) {
+    if (ms) ms[i] = tot[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers and launch interfaces shared by the SS2D kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss2d {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kChunkAlign = 32;  // chunk lengths are multiples of this (any tile length divides it)
+constexpr int kMaxBlock = 256;   // threads per block of the scan kernel (4 waves)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element types ---------------------------------------------------------------------
+// x, dt_raw, Bs, Cs and y are either fp32 or bfloat16 (raw 16-bit patterns in uint16_t).
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float to_f32(uint16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  static __device__ __forceinline__ float load(const uint16_t* p) { return to_f32(*p); }
+  // fp32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+  static __device__ __forceinline__ uint16_t from_f32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+};
+
+// ---- arithmetic ------------------------------------------------------------------------
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|).  log1p(e) for e in (0, 1] uses
+// the compensated form log(u) * e / (u - 1) with u = 1 + e rounded (D. Goldberg, "What
+// every computer scientist should know about floating-point arithmetic", 1991, thm. 4),
+// which keeps the relative accuracy of log for small e.
+__device__ __forceinline__ float softplus_f32(float z) {
+  const float e = exp2_hw(-fabsf(z) * kLog2e);
+  const float u = 1.0f + e;
+  const float du = u - 1.0f;
+  const float lg = __builtin_amdgcn_logf(u) * kLn2;
+  const float l1p = (du == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(du));
+  return fmaxf(z, 0.0f) + l1p;
+}
+
+// DPP quad_perm helpers (lanes exchange values inside groups of four).
+template <int P0, int P1, int P2, int P3>
+__device__ __forceinline__ float quad_perm(float v) {
+  constexpr int ctrl = P0 | (P1 << 2) | (P2 << 4) | (P3 << 6);
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// ---- launch arguments ------------------------------------------------------------------
+struct ScanArgs {
+  const void* x_row;      // route source for routes 0 and 1: x, (B, D, L)
+  const void* x_col;      // route source for routes 2 and 3: x transposed per plane, (B, D, L)
+  const void* dt_raw;     // (B, K, D, L)
+  const void* Bs;         // (B, K, N, L)
+  const void* Cs;         // (B, K, N, L)
+  const float* A_log;     // (K, D, N)
+  const float* Ds;        // (K, D)
+  const float* dt_bias;   // (K, D)
+  float* y_route;         // (B, K, D, L) fp32 per-route outputs in scan order
+  float* h_end;           // (B, K, D, C, N) chunk end states from a zero start
+  float* delta_sum;       // (B, K, D, C) sum of delta over each chunk
+  float* h_in;            // (B, K, D, C, N) chunk start states (chunk 0 starts at zero)
+  int B, K, D, L, N;
+  int num_chunks;         // C
+  int chunk_len;          // steps per chunk, a multiple of kChunkAlign (>= L when C == 1)
+  int chunk_base;         // first chunk index covered by this launch
+  int chunks_in_launch;   // chunks covered by this launch per (b, k)
+};
+
+enum ScanMode { kModeOut = 0, kModeAgg = 1 };
+
+// Host-side launchers (defined in the .hip files).
+int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
+                     hipStream_t st);
+int launch_carry(const ScanArgs& a, hipStream_t st);
+int launch_merge4(const float* y_route, void* y, int B, int D, int H, int W, int dtype,
+                  hipStream_t st);
+int launch_merge2(const float* y_route, void* y, int B, int D, int L, int dtype,
+                  hipStream_t st);
+
+}  // namespace ss2d
