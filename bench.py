@@ -40,14 +40,16 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+SCAN_SOURCES = ("ss2d_scan.inc", "ss2d_scan_bf16.hip", "ss2d_scan_f32.hip", "ss2d_device.h")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources of the scan kernel (the kernel the roofline line describes)."""
     h = hashlib.sha256()
-    files = sorted((ROOT / "selective_scan_ss2d_amd" / "csrc").glob("*")) + [
-        ROOT / "include" / "ss2d.h"]
-    for f in files:
-        if f.suffix in (".hip", ".inc", ".h"):
-            h.update(f.name.encode())
-            h.update(f.read_bytes())
+    for name in SCAN_SOURCES:
+        f = ROOT / "selective_scan_ss2d_amd" / "csrc" / name
+        h.update(name.encode())
+        h.update(f.read_bytes())
     return h.hexdigest()[:16]
 
 
@@ -105,6 +107,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 device-to-device copies of MIB "
+                         "MiB (a plain copy kernel of known size, for scaling the HBM byte "
+                         "counters of a profiler run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -123,6 +129,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written":
+                          n * 4, "copies": 5}), flush=True)
+        return 0
     ss.load_library()  # raises when the HIP library is not built: there is no fallback
     wl = workloads.workload(args.workload)
     log(f"workload {wl.name}: {wl.as_dict()}; generating seeded inputs")

@@ -107,40 +107,37 @@ struct Plan {
   size_t off_xt = 0, off_yr = 0, off_hend = 0, off_dsum = 0, off_hin = 0, bytes = 0;
 };
 
-// Launch plan.  The scan needs about three waves per SIMD (256 CUs x 4 SIMDs) to keep the
-// VALU issuing; one lane per channel gives B*K*ceil(D/64) waves.  When that is too few,
-// first split each channel's states over 4 lanes (cheap); failing that, cut time into
-// chunks (each chunk scanned twice: once for its carry, once for its outputs).
+// Launch plan.  The scan wants about three resident waves per SIMD (256 CUs x 4 SIMDs)
+// to keep the VALU issuing.  Splitting each channel's N states over 4 lanes (partial
+// outputs combined with DPP) costs a few extra instructions per step and quadruples the
+// waves; it is used whenever N allows.  When even that leaves too few waves, time is cut
+// into chunks: a first pass computes each chunk's end state from a zero start, a carry pass
+// chains them, and a second pass rescans each chunk from its true start state, so chunking
+// roughly doubles the work and is used only for short, long-sequence batches.
 Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                const void* x, const void* dt_raw) {
   Plan p;
   const int64_t L = H * W;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
-  const int64_t waves1 = B * K * ((D + 63) / 64);
-  const int64_t waves4 = B * K * ((4 * D + 63) / 64);
-  const int64_t kTargetWaves = 2048;
-  int split = 1;
-  int64_t chunk = 0;
-  if (waves1 < kTargetWaves) {
-    if (N % 4 == 0 && waves4 >= 1536) {
-      split = 4;
-    } else {
-      const int64_t want = (3072 + waves1 - 1) / waves1;  // chunks wanted
-      int64_t len = (L + want - 1) / want;
-      len = ((len + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
-      if (len < 64) len = 64;
-      if (len < L) chunk = len;
-    }
-  }
+  int split = (N % 4 == 0) ? 4 : ((N % 2 == 0) ? 2 : 1);
   const int64_t forced_split = env_int("SS2D_SPLIT", 0);
-  const int64_t forced_chunk = env_int("SS2D_CHUNK_LEN", -1);
   if (forced_split == 1 || forced_split == 2 || forced_split == 4) split = int(forced_split);
   if (split > N || N % split != 0) split = 1;
+  const int64_t waves = B * K * ((D * split + 63) / 64);
+  int64_t chunk = 0;
+  if (waves < 1536) {
+    const int64_t want = (3072 + waves - 1) / waves;  // chunks wanted
+    int64_t len = (L + want - 1) / want;
+    len = ((len + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
+    if (len < 64) len = 64;
+    if (len < L) chunk = len;
+  }
+  const int64_t forced_chunk = env_int("SS2D_CHUNK_LEN", -1);
   if (forced_chunk >= 0) {
     int64_t len = ((forced_chunk + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
     chunk = (len > 0 && len < L) ? len : 0;
   }
-  if (chunk > 0) split = 1;  // the chunked passes run one lane per channel
+  if (chunk > 0 && split == 2) split = 1;  // the chunked passes run 1 or 4 lanes per channel
   p.split = split;
   if (chunk > 0) {
     p.chunk_len = static_cast<int>(chunk);

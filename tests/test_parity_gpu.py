@@ -71,7 +71,7 @@ def test_small_shapes(orc, case):
 
 # ---- every launch variant: lanes per channel and chunked scans ----------------------
 VARIANTS = [dict(SS2D_SPLIT=s, SS2D_CHUNK_LEN=0) for s in (1, 2, 4)] + [
-    dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=c) for c in (32, 64, 96, 160)]
+    dict(SS2D_SPLIT=sp, SS2D_CHUNK_LEN=c) for sp in (1, 4) for c in (32, 64, 96, 160)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -93,7 +93,9 @@ def test_bidir_small(orc, case):
 
 
 @pytest.mark.parametrize("var", [dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=0),
-                                 dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64)], ids=["S4", "chunk64"])
+                                 dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
+                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96)],
+                         ids=["S4", "S1_chunk64", "S4_chunk96"])
 def test_bidir_variants(orc, var):
     check_case(orc, workloads.custom(2, 96, 1, 300, 16, 2, "bf16"), a_log="random", seed=5,
                **var)
