@@ -75,7 +75,8 @@ VARIANTS = [dict(SS2D_SPLIT=s, SS2D_CHUNK_LEN=0) for s in (1, 2, 4)] + [
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: f"S{v['SS2D_SPLIT']}_C{v['SS2D_CHUNK_LEN']}")
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "S{}_C{}".format(
+    v["SS2D_SPLIT"], v["SS2D_CHUNK_LEN"]))
 def test_launch_variants(orc, dt, var):
     wl = workloads.custom(2, 130, 24, 24, 16, 4, dt)  # L = 576: vector loads, 3 waves/(b,k)
     check_case(orc, wl, a_log="random", seed=11, **var)
@@ -93,9 +94,10 @@ def test_bidir_small(orc, case):
 
 
 @pytest.mark.parametrize("var", [dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=0),
+                                 dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=0),
                                  dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
                                  dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96)],
-                         ids=["S4", "S1_chunk64", "S4_chunk96"])
+                         ids=["S4", "S1", "S1_chunk64", "S4_chunk96"])
 def test_bidir_variants(orc, var):
     check_case(orc, workloads.custom(2, 96, 1, 300, 16, 2, "bf16"), a_log="random", seed=5,
                **var)
