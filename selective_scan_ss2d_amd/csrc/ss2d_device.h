@@ -36,16 +36,15 @@ template <> struct Elem<uint16_t> {
 // ---- arithmetic ------------------------------------------------------------------------
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|).  log1p(e) for e in (0, 1] uses
-// the compensated form log(u) * e / (u - 1) with u = 1 + e rounded (D. Goldberg, "What
-// every computer scientist should know about floating-point arithmetic", 1991, thm. 4),
-// which keeps the relative accuracy of log for small e.
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e) with e = e^-|z| in (0, 1].  With
+// u = 1 + e rounded, c = e - (u - 1) is exactly the rounding error of u, and
+// log1p(e) = log(u) + log(1 + c/u) = log(u) + c up to c * (1 - 1/u) <= 2^-24 * log1p(e):
+// one log2 and three adds recover the accuracy a plain log(1 + e) loses for small e.
 __device__ __forceinline__ float softplus_f32(float z) {
   const float e = exp2_hw(-fabsf(z) * kLog2e);
   const float u = 1.0f + e;
-  const float du = u - 1.0f;
-  const float lg = __builtin_amdgcn_logf(u) * kLn2;
-  const float l1p = (du == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(du));
+  const float c = e - (u - 1.0f);
+  const float l1p = fmaf(__builtin_amdgcn_logf(u), kLn2, c);
   return fmaxf(z, 0.0f) + l1p;
 }
 

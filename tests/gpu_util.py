@@ -62,6 +62,11 @@ def parity_error(y: np.ndarray, ref: np.ndarray) -> dict:
 
 def assert_parity(y, ref, dtype: str, what: str) -> dict:
     e = parity_error(y, ref)
+    record = os.environ.get("SS2D_PARITY_LOG")
+    if record:  # one JSON line per checked case, for the parity summary
+        import json
+        with open(record, "a") as f:
+            f.write(json.dumps(dict(case=what, dtype=dtype, limit=TOL[dtype], **e)) + "\n")
     log(f"  parity {what}: gate={e['gate']:.3e} (limit {TOL[dtype]:.0e}) "
         f"normwise={e['normwise']:.3e} unfloored={e['unfloored']:.3e}")
     assert e["finite"], f"{what}: non-finite output"
