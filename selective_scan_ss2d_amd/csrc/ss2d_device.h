@@ -48,6 +48,17 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return fmaxf(z, 0.0f) + l1p;
 }
 
+// Workgroups are handed to the 8 XCDs of the chip round-robin in linear launch order, and
+// each XCD has its own L2.  This maps the linear workgroup index to a logical one so that
+// logically consecutive workgroups (which share inputs) run on the same XCD: XCD j gets
+// the j-th contiguous range of logical indices.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ unsigned xcd_local_order(unsigned lin, unsigned total) {
+  const unsigned q = total / kNumXcd, r = total % kNumXcd;
+  const unsigned j = lin % kNumXcd, i = lin / kNumXcd;
+  return j * q + min(j, r) + i;
+}
+
 // DPP quad_perm helpers (lanes exchange values inside groups of four).
 template <int P0, int P1, int P2, int P3>
 __device__ __forceinline__ float quad_perm(float v) {
