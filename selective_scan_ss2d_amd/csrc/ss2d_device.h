@@ -59,6 +59,19 @@ __device__ __forceinline__ unsigned xcd_local_order(unsigned lin, unsigned total
   return j * q + min(j, r) + i;
 }
 
+// Issue priority of a wave from its progress through `total` work units: 3 for the first
+// half, 2 to three quarters, 1 to nine tenths, 0 for the rest.  Among waves of equal
+// priority a SIMD issues from the oldest first, so co-resident blocks that start together
+// would otherwise finish far apart, the last one running alone at low utilisation; with
+// falling priority a wave that runs ahead yields to those behind it.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const long long d = done, t = total;
+  if (2 * d < t) __builtin_amdgcn_s_setprio(3);
+  else if (4 * d < 3 * t) __builtin_amdgcn_s_setprio(2);
+  else if (10 * d < 9 * t) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // DPP quad_perm helpers (lanes exchange values inside groups of four).
 template <int P0, int P1, int P2, int P3>
 __device__ __forceinline__ float quad_perm(float v) {
