@@ -21,6 +21,8 @@ HERE = pathlib.Path(__file__).resolve().parent
 SOURCE = HERE / "ss2d_oracle.c"
 LIBRARY = HERE / "liboracle_ss2d.so"
 
+ORACLE_ZOH = 1  # flag bit of oracle_forward_ex: zero-order hold for B
+
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -54,6 +56,13 @@ class Oracle:
         lib.oracle_forward_channels.restype = ctypes.c_int
         lib.oracle_forward_channels.argtypes = [ctypes.c_int] + [_f32p] * 7 + \
             [ctypes.c_int64] * 5 + [_i64p, _i64p, ctypes.c_int64, _f64p, ctypes.c_int]
+        lib.oracle_forward_ex.restype = ctypes.c_int
+        lib.oracle_forward_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + [ctypes.c_int, _f64p] + \
+            [ctypes.c_int64] * 5 + [ctypes.c_int]
+        lib.oracle_forward_channels_ex.restype = ctypes.c_int
+        lib.oracle_forward_channels_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + \
+            [ctypes.c_int] + [ctypes.c_int64] * 5 + [_i64p, _i64p, ctypes.c_int64, _f64p,
+                                                   ctypes.c_int]
         self.lib = lib
         self.last_threads = None
 
@@ -89,29 +98,44 @@ class Oracle:
             ptrs.append(p)
         return (B, D, H, W, N), keep, ptrs
 
+    def _gate(self, z, x):
+        """The optional gate z (same shape as x) as a float32 pointer, or NULL."""
+        if z is None:
+            return None, None
+        z = np.ascontiguousarray(z, dtype=np.float32)
+        if z.shape != np.shape(x):
+            raise ValueError(f"z has shape {z.shape}, expected {np.shape(x)}")
+        return z, z.ctypes.data_as(_f32p)
+
     # -- public calls -----------------------------------------------------------------
-    def forward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+    # z: optional gate (shape of x), each route's output times SiLU(z); zoh: zero-order
+    # hold for B ((exp(delta A) - 1) / A * B instead of delta * B).
+    def forward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0, z=None,
+                zoh=False):
         (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+        zkeep, zp = self._gate(z, x)
         y = np.empty((B, D, H * W), dtype=np.float64)
-        rc = self.lib.oracle_forward(K, *ptrs, y.ctypes.data_as(_f64p), B, D, H, W, N,
-                                     int(threads))
+        rc = self.lib.oracle_forward_ex(K, *ptrs, zp, ORACLE_ZOH if zoh else 0,
+                                        y.ctypes.data_as(_f64p), B, D, H, W, N, int(threads))
         if rc < 0:
             raise RuntimeError("oracle_forward rejected its arguments")
         self.last_threads = rc
         return y.reshape(np.shape(x))
 
     def forward_channels(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx,
-                         threads=0):
+                         threads=0, z=None, zoh=False):
         (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+        zkeep, zp = self._gate(z, x)
         bi = np.ascontiguousarray(b_idx, dtype=np.int64)
         di = np.ascontiguousarray(d_idx, dtype=np.int64)
         if bi.shape != di.shape or bi.ndim != 1:
             raise ValueError("b_idx and d_idx must be 1-D and of equal length")
         y = np.empty((bi.size, H * W), dtype=np.float64)
-        rc = self.lib.oracle_forward_channels(K, *ptrs, B, D, H, W, N,
-                                              bi.ctypes.data_as(_i64p),
-                                              di.ctypes.data_as(_i64p), bi.size,
-                                              y.ctypes.data_as(_f64p), int(threads))
+        rc = self.lib.oracle_forward_channels_ex(K, *ptrs, zp, ORACLE_ZOH if zoh else 0,
+                                                 B, D, H, W, N,
+                                                 bi.ctypes.data_as(_i64p),
+                                                 di.ctypes.data_as(_i64p), bi.size,
+                                                 y.ctypes.data_as(_f64p), int(threads))
         if rc < 0:
             raise RuntimeError("oracle_forward_channels rejected its arguments")
         self.last_threads = rc
@@ -128,17 +152,18 @@ def default() -> Oracle:
     return _DEFAULT
 
 
-def ss2d_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+def ss2d_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0, z=None, zoh=False):
     """y (B, D, H, W), float64, of the four-route SS2D forward operator."""
-    return default().forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads)
+    return default().forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads, z=z, zoh=zoh)
 
 
-def ss1d_bidir_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0):
+def ss1d_bidir_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads=0, z=None, zoh=False):
     """y (B, D, L), float64, of the bidirectional (forward + reversed) 1D scan."""
-    return default().forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads)
+    return default().forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, threads, z=z, zoh=zoh)
 
 
-def forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx, threads=0):
+def forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx, threads=0,
+                     z=None, zoh=False):
     """Output planes of the selected (b, d) channels only."""
     return default().forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx,
-                                      threads)
+                                      threads, z=z, zoh=zoh)

@@ -34,6 +34,16 @@
  *   - K = 2: the Vim block's forward path and a backward path over a reversed copy of the
  *     sequence, added together (Vim summary, section 4.3).
  *
+ * Two options (the _ex entry points):
+ *   - Gate z (B, D, H, W), optional: every route's output is multiplied by SiLU(z) at its
+ *     image position before the routes are added, SiLU(z) = z / (1 + exp(-z)) (Vim
+ *     summary, section 4.3, "Gating and Merging"; the explainer's MambaBlock.forward, which
+ *     multiplies the scan output by silu(z)).
+ *   - ORACLE_ZOH: zero-order hold for B as well, Bbar = (exp(delta A) - 1) / A * B in
+ *     place of delta * B (the Vim summary, section 4.1, defines Abar = exp(delta A) and
+ *     Bbar = (delta A)^-1 (exp(delta A) - I) delta B).  Written with expm1 so that small
+ *     |delta A| keeps its digits; A = 0 takes the limit delta * B.
+ *
  * Layouts (all contiguous, row-major):
  *   x, y      (B, D, H, W)    y written in full
  *   dt_raw    (B, K, D, L)    scan order of route k (position t is step t of that route)
@@ -48,6 +58,8 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+#define ORACLE_ZOH 1
 
 /* log(1 + e^z), written to stay finite for large |z| */
 static double softplus(double z) {
@@ -76,13 +88,21 @@ static int64_t route_position(int K, int k, int64_t t, int64_t H, int64_t W) {
     }
 }
 
+/* z * sigmoid(z), the gate nonlinearity */
+static double silu(double z) {
+    return z / (1.0 + exp(-z));
+}
+
 /* All K routes of one (b, d) channel, summed into out[0 .. L-1] (image order). */
 static void channel_forward(int K, const float *x, const float *dt_raw, const float *A_log,
                             const float *Bs, const float *Cs, const float *Ds,
-                            const float *dt_bias, int64_t D, int64_t H, int64_t W, int64_t N,
-                            int64_t b, int64_t d, double *out, double *h, double *A) {
+                            const float *dt_bias, const float *z, int flags, int64_t D,
+                            int64_t H, int64_t W, int64_t N, int64_t b, int64_t d, double *out,
+                            double *h, double *A) {
     const int64_t L = H * W;
     const float *xc = x + (b * D + d) * L;
+    const float *zc = z ? z + (b * D + d) * L : NULL;
+    const int zoh = (flags & ORACLE_ZOH) != 0;
     for (int64_t l = 0; l < L; ++l)
         out[l] = 0.0;
     for (int k = 0; k < K; ++k) {
@@ -102,10 +122,14 @@ static void channel_forward(int K, const float *x, const float *dt_raw, const fl
             double yk = 0.0;
             for (int64_t n = 0; n < N; ++n) {
                 const double a = exp(delta * A[n]);
-                h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;
+                double bbar = delta;
+                if (zoh && A[n] != 0.0)
+                    bbar = expm1(delta * A[n]) / A[n];
+                h[n] = a * h[n] + bbar * (double)Bk[n * L + t] * u;
                 yk += (double)Ck[n * L + t] * h[n];
             }
-            out[l] += yk + Dk * u;
+            const double gate = zc ? silu((double)zc[l]) : 1.0;
+            out[l] += (yk + Dk * u) * gate;
         }
     }
 }
@@ -120,12 +144,15 @@ static int pick_threads(int nthreads) {
 }
 
 /* Full output y (B, D, H, W) in double.  K is 4 (SS2D) or 2 (bidirectional 1D, H = 1).
+ * z (B, D, H, W) is the optional gate (NULL: none); flags is 0 or ORACLE_ZOH.
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
-int oracle_forward(int K, const float *x, const float *dt_raw, const float *A_log,
-                   const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
-                   double *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
-                   int nthreads) {
+int oracle_forward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
+                      const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                      const float *z, int flags, double *y, int64_t B, int64_t D, int64_t H,
+                      int64_t W, int64_t N, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
+        return -1;
+    if (flags & ~ORACLE_ZOH)
         return -1;
     if (K == 2 && H != 1)
         return -1;
@@ -146,8 +173,8 @@ int oracle_forward(int K, const float *x, const float *dt_raw, const float *A_lo
 #endif
             for (int64_t i = 0; i < total; ++i) {
                 const int64_t b = i / D, d = i % D;
-                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, D, H, W, N, b, d,
-                                y + i * L, h, h + N);
+                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D, H, W,
+                                N, b, d, y + i * L, h, h + N);
             }
             free(h);
         }
@@ -156,13 +183,16 @@ int oracle_forward(int K, const float *x, const float *dt_raw, const float *A_lo
 }
 
 /* Output planes y[b_idx[i], d_idx[i], :, :] for i < nsel, written to y_sel (nsel, H, W).
- * Same arithmetic as oracle_forward; used to check large outputs on sampled channels. */
-int oracle_forward_channels(int K, const float *x, const float *dt_raw, const float *A_log,
-                            const float *Bs, const float *Cs, const float *Ds,
-                            const float *dt_bias, int64_t B, int64_t D, int64_t H, int64_t W,
-                            int64_t N, const int64_t *b_idx, const int64_t *d_idx,
-                            int64_t nsel, double *y_sel, int nthreads) {
+ * Same arithmetic as oracle_forward_ex; used to check large outputs on sampled channels. */
+int oracle_forward_channels_ex(int K, const float *x, const float *dt_raw, const float *A_log,
+                               const float *Bs, const float *Cs, const float *Ds,
+                               const float *dt_bias, const float *z, int flags, int64_t B,
+                               int64_t D, int64_t H, int64_t W, int64_t N,
+                               const int64_t *b_idx, const int64_t *d_idx, int64_t nsel,
+                               double *y_sel, int nthreads) {
     if ((K != 2 && K != 4) || N <= 0 || (K == 2 && H != 1))
+        return -1;
+    if (flags & ~ORACLE_ZOH)
         return -1;
     for (int64_t i = 0; i < nsel; ++i)
         if (b_idx[i] < 0 || b_idx[i] >= B || d_idx[i] < 0 || d_idx[i] >= D)
@@ -182,10 +212,28 @@ int oracle_forward_channels(int K, const float *x, const float *dt_raw, const fl
 #pragma omp for schedule(dynamic, 1)
 #endif
             for (int64_t i = 0; i < nsel; ++i)
-                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, D, H, W, N,
-                                b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
+                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D, H, W,
+                                N, b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
             free(h);
         }
     }
     return failed ? -1 : threads;
+}
+
+/* The plain operator: no gate, delta * B for B. */
+int oracle_forward(int K, const float *x, const float *dt_raw, const float *A_log,
+                   const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                   double *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                   int nthreads) {
+    return oracle_forward_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, 0, y, B, D, H, W,
+                             N, nthreads);
+}
+
+int oracle_forward_channels(int K, const float *x, const float *dt_raw, const float *A_log,
+                            const float *Bs, const float *Cs, const float *Ds,
+                            const float *dt_bias, int64_t B, int64_t D, int64_t H, int64_t W,
+                            int64_t N, const int64_t *b_idx, const int64_t *d_idx,
+                            int64_t nsel, double *y_sel, int nthreads) {
+    return oracle_forward_channels_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, 0, B, D,
+                                      H, W, N, b_idx, d_idx, nsel, y_sel, nthreads);
 }

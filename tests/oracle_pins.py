@@ -23,6 +23,9 @@ What pins what:
   transpose, rot180 symmetries of the four routes under exchange of parameter sets
   linearity         y is linear in x for fixed delta, B, C
   channels          the sampled-channel entry point agrees with the full one
+  gate              the optional gate against sigmoid written through tanh, z = 0, z = 40
+  zoh exact         zero-order hold reproduces the exact solution of h' = A h + B u for inputs
+                    held constant (Vim summary, sec. 4.1, defines the ZOH discretisation)
 """
 from __future__ import annotations
 
@@ -363,6 +366,68 @@ def pin_channels(orc):
     _close(y2[mask], y[mask], 0.0, 0.0, "channel isolation")
 
 
+def pin_gate(orc):
+    """The gate multiplies every route's output, skip term included, by SiLU(z) at the image
+    position: checked against the logistic function written through tanh,
+    sigmoid(z) = (1 + tanh(z / 2)) / 2, and at z = 0 (output exactly zero) and z = 40
+    (SiLU(z) = z to 1e-17)."""
+    rng = _rng(14)
+    for K, xshape in ((4, (2, 3, 4, 5)), (2, (2, 3, 7))):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 4
+        x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, xshape)
+        args = (K, x, dt, A_log, Bs, Cs, Ds, bias)
+        y = orc.forward(*args)
+        z = (2.0 * rng.standard_normal(xshape)).astype(np.float32)
+        zd = z.astype(np.float64)
+        _close(orc.forward(*args, z=z), y * zd * (1.0 + np.tanh(zd / 2.0)) / 2.0, 1e-12,
+               1e-14, f"gate, K={K}")
+        y0 = orc.forward(*args, z=np.zeros(xshape, np.float32))
+        assert np.all(y0 == 0.0), "gate at z = 0"
+        _close(orc.forward(*args, z=np.full(xshape, 40.0, np.float32)), 40.0 * y, 1e-14,
+               1e-15, f"gate at z = 40, K={K}")
+        # the gate is the same for every route: the same result whether z is read per route
+        # or once; and it does not touch the plain path
+        _close(orc.forward(*args, z=np.ones(xshape, np.float32)), y / (1.0 + math.exp(-1.0)),
+               1e-13, 1e-15, f"gate at z = 1, K={K}")
+
+
+def pin_zoh_exact(orc):
+    """Zero-order hold is exact for inputs held constant over each step: with B_t, u and C
+    constant in time and D = 0, route k's state after t steps is the solution of
+    h' = A h + B u at time S_t = sum of its deltas, h_n = B_n u (exp(A_n S_t) - 1) / A_n,
+    whatever the individual deltas are.  Checked for both routes of the 1D variant and for
+    the four routes of a 2D map (constant x, so every route sees the same u)."""
+    rng = _rng(15)
+    for K, xshape in ((2, (1, 2, 60)), (4, (1, 2, 5, 6))):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 4
+        _, dt, A_log, _, _, _, bias = _random_inputs(rng, B, K, D, N, L, xshape)
+        u0 = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+        x = np.broadcast_to(u0[None, :, None], (B, D, L)).reshape(xshape).astype(np.float32)
+        bconst = rng.standard_normal((B, K, N)).astype(np.float32)
+        Bs = np.repeat(bconst[..., None], L, axis=-1).astype(np.float32)
+        Cs = np.ones((B, K, N, L), np.float32)
+        Ds = np.zeros((K, D), np.float32)
+        got = orc.forward(K, x, dt, A_log, Bs, Cs, Ds, bias, zoh=True).reshape(B, D, L)
+        want = np.zeros((B, D, L))
+        routes = _routes(*(xshape[2:] if K == 4 else (1, L)), K=K)
+        for d in range(D):
+            for k in range(K):
+                delta = _softplus(dt[0, k, d].astype(np.float64) + float(bias[k, d]))
+                S = np.cumsum(delta)
+                A = -np.exp(A_log[k, d].astype(np.float64))
+                h = (bconst[0, k][:, None].astype(np.float64) * float(u0[d]) *
+                     np.expm1(A[:, None] * S[None, :]) / A[:, None])
+                want[0, d, routes[k]] += h.sum(axis=0)
+        _close(got, want, 1e-11, 1e-13, f"zero-order hold, K={K}")
+        # the plain path (delta * B) is not exact here
+        plain = orc.forward(K, x, dt, A_log, Bs, Cs, Ds, bias).reshape(B, D, L)
+        assert np.max(np.abs(plain - want)) > 1e-6 * np.max(np.abs(want)), "ZOH had no effect"
+
+
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
-            pin_linearity, pin_channels]
+            pin_linearity, pin_channels, pin_gate, pin_zoh_exact]

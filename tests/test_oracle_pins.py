@@ -29,13 +29,13 @@ def test_pin(orc, pin):
 # Planted mistakes: (what, original text in ss2d_oracle.c, replacement).  Every one of them
 # must make at least one pin fail.
 MUTATIONS = [
-    ("drop skip term", "out[l] += yk + Dk * u;", "out[l] += yk;"),
+    ("drop skip term", "out[l] += (yk + Dk * u) * gate;", "out[l] += yk * gate;"),
     ("A sign", "A[n] = -exp(", "A[n] = exp("),
     ("output before update",
-     "h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;\n"
+     "h[n] = a * h[n] + bbar * (double)Bk[n * L + t] * u;\n"
      "                yk += (double)Ck[n * L + t] * h[n];",
      "yk += (double)Ck[n * L + t] * h[n];\n"
-     "                h[n] = a * h[n] + delta * (double)Bk[n * L + t] * u;"),
+     "                h[n] = a * h[n] + bbar * (double)Bk[n * L + t] * u;"),
     ("no decay", "h[n] = a * h[n] +", "h[n] = h[n] +"),
     ("decay squared", "const double a = exp(delta * A[n]);",
      "const double a = exp(2.0 * delta * A[n]);"),
@@ -44,10 +44,10 @@ MUTATIONS = [
     ("route 3 not reversed", "s = L - 1 - t;", "s = t;"),
     ("bias outside softplus", "softplus((double)dt[t] + bias)",
      "(softplus((double)dt[t]) + bias)"),
-    ("no delta on B", "delta * (double)Bk[n * L + t] * u", "(double)Bk[n * L + t] * u"),
+    ("no delta on B", "double bbar = delta;", "double bbar = 1.0;"),
     ("softplus wrong", "return m + log1p(exp(-fabs(z)));", "return m + log1p(exp(fabs(z)));"),
     ("C replaced by B", "yk += (double)Ck[n * L + t]", "yk += (double)Bk[n * L + t]"),
-    ("B layout (L, N)", "(double)Bk[n * L + t] * u", "(double)Bk[t * N + n] * u"),
+    ("B layout (L, N)", "bbar * (double)Bk[n * L + t] * u", "bbar * (double)Bk[t * N + n] * u"),
     ("delta read at image position", "(double)dt[t] + bias", "(double)dt[l] + bias"),
     ("backward 1D route not reversed", "return k == 0 ? t : L - 1 - t;", "return t;"),
     ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]", "A_log[(k * N + n) * D + d]"),
@@ -56,6 +56,15 @@ MUTATIONS = [
     ("x ignores batch", "x + (b * D + d) * L", "x + d * L"),
     ("Cs ignores batch", "Cs + (b * K + k) * N * L", "Cs + k * N * L"),
     ("state not reset per route", "            h[n] = 0.0;\n", "\n"),
+    ("gate is the sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("gate misses the skip term", "out[l] += (yk + Dk * u) * gate;",
+     "out[l] += yk * gate + Dk * u;"),
+    ("gate read at the scan step", "silu((double)zc[l])", "silu((double)zc[t])"),
+    ("ZOH without the minus one", "bbar = expm1(delta * A[n]) / A[n];",
+     "bbar = exp(delta * A[n]) / A[n];"),
+    ("ZOH divided by delta", "bbar = expm1(delta * A[n]) / A[n];",
+     "bbar = expm1(delta * A[n]) / delta;"),
+    ("ZOH ignored", "if (zoh && A[n] != 0.0)", "if (0)"),
 ]
 
 
