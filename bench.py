@@ -38,6 +38,12 @@ FMA_PEAK_TFLOPS = VALU_LANE_OPS * 2 / 1e12
 FLOPS_PER_UPDATE = 6
 ISSUE_SLOTS_PER_UPDATE = 4 + 2
 UPDATE_PEAK_TFLOPS = VALU_LANE_OPS / ISSUE_SLOTS_PER_UPDATE * FLOPS_PER_UPDATE / 1e12
+# With zero-order hold the update is delta*A (1 flop), (a - 1) / A as one FMA (2), times B
+# and u (2), the h update (2) and C*h (2): 9 flops in at least 6 VALU slots plus the exp.
+ZOH_FLOPS_PER_UPDATE = 9
+ZOH_ISSUE_SLOTS_PER_UPDATE = 6 + 2
+ZOH_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / ZOH_ISSUE_SLOTS_PER_UPDATE * ZOH_FLOPS_PER_UPDATE
+                          / 1e12)
 HBM_PEAK_GBPS = 8000.0
 ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
 
@@ -74,7 +80,7 @@ def measured_traffic(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, target_s: float) -> dict:
+def cpu_baseline(wl, inp, target_s: float, z=None, zoh=False) -> dict:
     """The float64 oracle, as it is, on all host cores, over a bounded sample of channels."""
     import numpy as np
 
@@ -82,19 +88,20 @@ def cpu_baseline(wl, inp, target_s: float) -> dict:
     cores = len(os.sched_getaffinity(0))
     orc = oracle.Oracle()
     args = [inp[k] for k in ARGS]
+    opts = dict(z=z, zoh=zoh)
     total = wl.B * wl.D
     rng = np.random.default_rng(0)
     n = min(total, max(cores, 64))
     order = rng.permutation(total)
     t0 = time.perf_counter()
     sel = order[:n]
-    orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores)
+    orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores, **opts)
     dt = time.perf_counter() - t0
     if n < total and dt < target_s:
         n = int(min(total, max(n, n * target_s / max(dt, 1e-3))))
         sel = order[:n]
         t0 = time.perf_counter()
-        orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores)
+        orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores, **opts)
         dt = time.perf_counter() - t0
     upd = n * wl.K * wl.L * wl.N
     return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
@@ -113,6 +120,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate", action="store_true",
+                    help="gated entry point: y * SiLU(z), z of the shape of x")
+    ap.add_argument("--zoh", action="store_true",
+                    help="zero-order-hold discretisation of B")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 device-to-device copies of MIB "
                          "MiB (a plain copy kernel of known size, for scaling the HBM byte "
@@ -158,9 +169,18 @@ def main() -> int:
         dev[k] = dev[k].to("cuda:0")
     for k in ("A_log", "Ds", "dt_bias"):
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
-    fn = ss.ss2d_forward if wl.K == 4 else ss.ss1d_bidir_forward
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
-    call = lambda: fn(*[dev[k] for k in ARGS], y=y)  # noqa: E731
+    gate = workloads.make_gate(wl, 0) if args.gate else None
+    if args.gate or args.zoh:
+        fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
+        z = None
+        if gate is not None:
+            z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
+                 if wl.dtype == "bf16" else torch.from_numpy(gate["z"])).to("cuda:0")
+        call = lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)  # noqa: E731
+    else:
+        fn = ss.ss2d_forward if wl.K == 4 else ss.ss1d_bidir_forward
+        call = lambda: fn(*[dev[k] for k in ARGS], y=y)  # noqa: E731
 
     log(f"warm-up {args.warmup} steps")
     for _ in range(args.warmup):
@@ -183,7 +203,7 @@ def main() -> int:
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     upd_per_s = wl.updates / (ms_step / 1e3)
-    alg_bytes = wl.algorithmic_bytes()
+    alg_bytes = wl.algorithmic_bytes() + (wl.elem_bytes * wl.B * wl.D * wl.L if args.gate else 0)
     gbps = alg_bytes / (ms_step / 1e3) / 1e9
     for name, (ms, n) in kernels.items():
         if n:
@@ -194,11 +214,14 @@ def main() -> int:
     scan_ms, scan_n = kernels["scan"]
     agg_ms, _ = kernels["chunk_agg"]
     scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
-    achieved = wl.updates * FLOPS_PER_UPDATE / scan_avg_s / 1e12
+    flops, peak = ((ZOH_FLOPS_PER_UPDATE, ZOH_UPDATE_PEAK_TFLOPS) if args.zoh
+                   else (FLOPS_PER_UPDATE, UPDATE_PEAK_TFLOPS))
+    achieved = wl.updates * flops / scan_avg_s / 1e12
     traffic = measured_traffic(wl.name)
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
-                "peak": round(UPDATE_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / UPDATE_PEAK_TFLOPS, 4), "traffic": traffic,
+                "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
+                "traffic": traffic if not (args.gate or args.zoh) else None,
                 "kernel": "k_scan", "kernel_avg_us": round(scan_avg_s * 1e6, 1),
                 "frac_of_fma_peak": round(achieved / FMA_PEAK_TFLOPS, 4),
                 "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
@@ -206,7 +229,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
+                           zoh=args.zoh)
         log(f"  {cpu['sample']} on {cpu['cores']} threads: {cpu['value']:.3e} updates/s")
 
     out = {
@@ -224,7 +248,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "H": wl.H, "W": wl.W,
                    "L": wl.L, "N": wl.N, "K": wl.K, "io_dtype": wl.dtype,
-                   "state_dtype": "f32", "A_log": args.a_log},
+                   "state_dtype": "f32", "A_log": args.a_log, "gate": bool(args.gate),
+                   "zoh": bool(args.zoh)},
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kernels.items() if n},

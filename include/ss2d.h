@@ -43,7 +43,7 @@
  *
  * Conventions shared by every entry point:
  *   - Inputs are read only.  y is written in full (no pre-zeroing needed) and must not
- *     overlap any input.
+ *     overlap any input (z included, for the entry points that take it).
  *   - All arguments are validated before anything is enqueued; on an error nothing is
  *     launched and y is untouched.  Nothing is printed and no exception crosses the ABI.
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default stream).
@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 1
+#define SS2D_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -98,6 +98,35 @@ int ss2d_forward(const void *x, const void *dt_raw, const float *A_log, const vo
 int ss1d_bidir_forward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
                        const void *Cs, const float *Ds, const float *dt_bias, void *y,
                        int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void *stream);
+
+/* ---- options: gate and zero-order hold --------------------------------------------------
+ * ss2d_forward_ex and ss1d_bidir_forward_ex take two more arguments than the plain entry
+ * points (which equal them with z = NULL, flags = 0):
+ *
+ *   z      optional gate, NULL for none.  Same shape, layout and data type as x and y.
+ *          Each route's output is multiplied by SiLU(z) = z / (1 + exp(-z)) at its image
+ *          position before the routes are added (the Vim summary, section 4.3, "Gating and
+ *          Merging": forward and backward outputs each gated by SiLU(z), then added; the
+ *          explainer's MambaBlock multiplies the scan output by silu(z)).  As z is shared by
+ *          the routes, the library applies SiLU(z) once to the fp32 sum, before the single
+ *          rounding.  z must be aligned to its element size and must not overlap y.
+ *   flags  0 or SS2D_FLAG_ZOH.  SS2D_FLAG_ZOH discretises B by zero-order hold as well:
+ *          Bbar = (exp(delta A) - 1) / A * B in place of delta * B (the Vim summary,
+ *          section 4.1: Bbar = (delta A)^-1 (exp(delta A) - I) delta B); A = 0 takes the
+ *          limit delta * B.  Unknown bits give SS2D_ERR_UNSUPPORTED.
+ *
+ * Every other argument, error and convention is that of the plain entry point. */
+#define SS2D_FLAG_ZOH 1
+
+int ss2d_forward_ex(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                    const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                    void *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                    int flags, void *stream);
+
+int ss1d_bidir_forward_ex(const void *x, const void *dt_raw, const float *A_log,
+                          const void *Bs, const void *Cs, const float *Ds,
+                          const float *dt_bias, const void *z, void *y, int64_t B, int64_t D,
+                          int64_t L, int64_t N, int dtype, int flags, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ss2d_status_string(int status);

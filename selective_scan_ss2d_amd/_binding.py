@@ -23,6 +23,7 @@ SS2D_ERR_HIP = 5
 SS2D_ERR_ALIAS = 6
 SS2D_F32 = 0
 SS2D_BF16 = 1
+SS2D_FLAG_ZOH = 1
 
 # Every symbol include/ss2d.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -30,6 +31,8 @@ _I64 = ctypes.c_int64
 SIGNATURES = {
     "ss2d_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 5 + [ctypes.c_int, _P]),
     "ss1d_bidir_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 4 + [ctypes.c_int, _P]),
+    "ss2d_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -182,6 +185,55 @@ def ss1d_bidir_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y=None, stream=Non
                                     Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
                                     dt_bias.data_ptr(), y.data_ptr(), B, D, L, N,
                                     _dtype_code(x), _stream_handle(x.device, stream))
+    _check(status)
+    return y
+
+
+def _gate_ptr(z, xshape, x):
+    """Device pointer of the optional gate (None -> NULL), checked like the other inputs."""
+    if z is None:
+        return None
+    _expect("z", z, xshape, x.dtype, x.device)
+    return z.data_ptr()
+
+
+def ss2d_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False, y=None,
+                    stream=None):
+    """ss2d_forward with the two options of the C entry point of the same name.
+
+    z: optional gate, shape and dtype of x; the output is multiplied by SiLU(z) before its
+    single rounding.  zoh: zero-order hold for B ((exp(delta A) - 1) / A * B instead of
+    delta * B).
+    """
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    B, D, N, y = _common(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, (B, D, H, W), H * W)
+    zp = _gate_ptr(z, (B, D, H, W), x)
+    status = lib.ss2d_forward_ex(x.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(),
+                                 Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
+                                 dt_bias.data_ptr(), zp, y.data_ptr(), B, D, H, W, N,
+                                 _dtype_code(x), SS2D_FLAG_ZOH if zoh else 0,
+                                 _stream_handle(x.device, stream))
+    _check(status)
+    return y
+
+
+def ss1d_bidir_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False, y=None,
+                          stream=None):
+    """ss1d_bidir_forward with the gate z and the zero-order-hold option."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    B, D, N, y = _common(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, (B, D, L), L)
+    zp = _gate_ptr(z, (B, D, L), x)
+    status = lib.ss1d_bidir_forward_ex(x.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(),
+                                       Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
+                                       dt_bias.data_ptr(), zp, y.data_ptr(), B, D, L, N,
+                                       _dtype_code(x), SS2D_FLAG_ZOH if zoh else 0,
+                                       _stream_handle(x.device, stream))
     _check(status)
     return y
 

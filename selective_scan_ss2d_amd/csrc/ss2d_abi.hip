@@ -173,6 +173,9 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
 
 int run_scan(const ss2d::ScanArgs& a, int dtype, int split, bool vec, int mode,
              hipStream_t st) {
+  if (a.zoh)
+    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh(a, split, vec, mode, st)
+                             : ss2d::launch_scan_bf16_zoh(a, split, vec, mode, st);
   return dtype == SS2D_F32 ? ss2d::launch_scan_f32(a, split, vec, mode, st)
                            : ss2d::launch_scan_bf16(a, split, vec, mode, st);
 }
@@ -204,10 +207,12 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
 }
 
 int forward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
-            const void* Cs, const float* Ds, const float* dt_bias, void* y, int64_t B,
-            int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+            const void* Cs, const float* Ds, const float* dt_bias, const void* z, void* y,
+            int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
+            void* stream) {
   // ---- validation (nothing is enqueued before all of it passes) -------------------------
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
+  if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
   if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS2D_ERR_UNSUPPORTED;
   if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
@@ -221,7 +226,7 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   if (!x || !dt_raw || !A_log || !Bs || !Cs || !Ds || !dt_bias || !y) return SS2D_ERR_NULL;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
-  for (const void* ptr : {x, dt_raw, Bs, Cs, static_cast<const void*>(y)})
+  for (const void* ptr : {x, dt_raw, Bs, Cs, z, static_cast<const void*>(y)})
     if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
   for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
                           static_cast<const void*>(dt_bias)})
@@ -231,7 +236,8 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
       overlaps(y, y_bytes, Bs, n_bc * e) || overlaps(y, y_bytes, Cs, n_bc * e) ||
       overlaps(y, y_bytes, A_log, int64_t(K) * D * N * 4) ||
       overlaps(y, y_bytes, Ds, int64_t(K) * D * 4) ||
-      overlaps(y, y_bytes, dt_bias, int64_t(K) * D * 4))
+      overlaps(y, y_bytes, dt_bias, int64_t(K) * D * 4) ||
+      (z && overlaps(y, y_bytes, z, n_x * e)))
     return SS2D_ERR_ALIAS;
 
   // ---- plan and scratch --------------------------------------------------------------
@@ -263,6 +269,7 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   a.N = static_cast<int>(N);
   a.num_chunks = p.num_chunks;
   a.chunk_len = p.chunk_len;
+  a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
 
   int err = 0;
   if (p.need_xt)
@@ -294,9 +301,9 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   }
   if (!err && rc == SS2D_OK) {
     err = timed(SS2D_KERNEL_MERGE, st, [&] {
-      return (K == 4) ? ss2d::launch_merge4(a.y_route, y, a.B, a.D, static_cast<int>(H),
+      return (K == 4) ? ss2d::launch_merge4(a.y_route, z, y, a.B, a.D, static_cast<int>(H),
                                             static_cast<int>(W), dtype, st)
-                      : ss2d::launch_merge2(a.y_route, y, a.B, a.D, a.L, dtype, st);
+                      : ss2d::launch_merge2(a.y_route, z, y, a.B, a.D, a.L, dtype, st);
     });
   }
   const hipError_t fe = hipFreeAsync(ws, st);
@@ -313,13 +320,31 @@ extern "C" {
 int ss2d_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
                  const void* Cs, const float* Ds, const float* dt_bias, void* y, int64_t B,
                  int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
-  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, B, D, H, W, N, dtype, stream);
+  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, H, W, N, dtype, 0,
+                 stream);
 }
 
 int ss1d_bidir_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
                        const void* Cs, const float* Ds, const float* dt_bias, void* y,
                        int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
-  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, B, D, 1, L, N, dtype, stream);
+  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, 1, L, N, dtype, 0,
+                 stream);
+}
+
+int ss2d_forward_ex(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                    const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                    void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                    int flags, void* stream) {
+  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype, flags,
+                 stream);
+}
+
+int ss1d_bidir_forward_ex(const void* x, const void* dt_raw, const float* A_log,
+                          const void* Bs, const void* Cs, const float* Ds,
+                          const float* dt_bias, const void* z, void* y, int64_t B, int64_t D,
+                          int64_t L, int64_t N, int dtype, int flags, void* stream) {
+  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype, flags,
+                 stream);
 }
 
 const char* ss2d_status_string(int status) {

@@ -187,12 +187,14 @@ __global__ void __launch_bounds__(256) k_carry(const ScanArgs a) {
 
 // Four-route merge.  For image position (h, w), l = h * W + w and s = w * H + h (its step
 // on the column-major route):
-//   y[l] = ((y0[l] + y1[L-1-l]) + y2[s]) + y3[L-1-s]
+//   y[l] = ((y0[l] + y1[L-1-l]) + y2[s]) + y3[L-1-s]          (times SiLU(z[l]) with GATE)
 // with y_k the per-route outputs in scan order.  Column-route values go through an LDS tile
-// so that every global access is a contiguous run.
-template <typename T>
+// so that every global access is a contiguous run.  The gate is shared by the routes, so
+// gating the sum once equals summing the gated route outputs.
+template <typename T, bool GATE>
 __global__ void __launch_bounds__(kTr * kTrRows)
-k_merge4(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int W, int64_t planes) {
+k_merge4(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D, int H,
+         int W, int64_t planes) {
   __shared__ float t2[kTr][kTr + 1];
   __shared__ float t3[kTr][kTr + 1];
   const int tx = threadIdx.x, ty = threadIdx.y;
@@ -222,6 +224,7 @@ k_merge4(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int W, i
         float v = y0[l] + y1[L - 1 - l];
         v += t2[tx][r];
         v += t3[tx][r];
+        if (GATE) v *= silu_f32(Elem<T>::load(z + p * L + l));
         y[p * L + l] = Elem<T>::from_f32(v);
       }
     }
@@ -234,6 +237,22 @@ k_merge4(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int W, i
 // the column-route values (contiguous along h) are staged in LDS with float4 loads, the
 // row-route values are read as float4 runs along w (reversed for route 1), and each thread
 // writes 4 consecutive outputs of a row.  Same fixed summation order as k_merge4.
+// Four consecutive elements (8- or 16-byte loads), kept raw until used.
+template <typename T> struct In4;
+template <> struct In4<float> {
+  float4 r;
+  __device__ __forceinline__ void load(const float* p) { r = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float4 get() const { return r; }
+};
+template <> struct In4<uint16_t> {
+  uint2 r;
+  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ float4 get() const {
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+};
+
 template <typename T> struct Out4;
 template <> struct Out4<float> {
   static __device__ __forceinline__ void store(float* p, float a, float b, float c, float d) {
@@ -257,10 +276,10 @@ __device__ __forceinline__ float4 load4_stream(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-template <typename T>
+template <typename T, bool GATE>
 __global__ void __launch_bounds__(256)
-k_merge4_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int W,
-             int64_t planes) {
+k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D,
+             int H, int W, int64_t planes) {
   // A block covers a 64 x 64 tile (h x w) of one plane; every thread keeps four float4
   // loads of each route in flight (the row-route loads are issued before the barrier).
   constexpr int TS = 64;
@@ -314,6 +333,12 @@ k_merge4_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int 
         float v2 = r0[j].z + r1[j].y, v3 = r0[j].w + r1[j].x;
         v0 += t2[ow + 0][ht]; v1 += t2[ow + 1][ht]; v2 += t2[ow + 2][ht]; v3 += t2[ow + 3][ht];
         v0 += t3[ow + 0][ht]; v1 += t3[ow + 1][ht]; v2 += t3[ow + 2][ht]; v3 += t3[ow + 3][ht];
+        if constexpr (GATE) {
+          In4<T> g;
+          g.load(z + p * L + l);
+          const float4 gz = g.get();
+          v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
+        }
         Out4<T>::store(y + p * L + l, v0, v1, v2, v3);
       }
     }
@@ -321,33 +346,54 @@ k_merge4_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int H, int 
   }
 }
 
-// Two-route merge (forward + reversed 1D sequence): y[l] = y0[l] + y1[L-1-l].
-template <typename T>
+// Two-route merge (forward + reversed 1D sequence): y[l] = y0[l] + y1[L-1-l], times
+// SiLU(z[l]) with GATE.
+template <typename T, bool GATE>
 __global__ void __launch_bounds__(256)
-k_merge2(const float* __restrict__ yr, T* __restrict__ y, int D, int L, int64_t planes) {
+k_merge2(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D, int L,
+         int64_t planes) {
   const int l = blockIdx.x * blockDim.x + threadIdx.x;
   if (l >= L) return;
   for (int64_t p = blockIdx.y; p < planes; p += gridDim.y) {
     const int64_t b = p / D, d = p % D;
     const float* y0 = yr + ((b * 2 + 0) * D + d) * L;
     const float* y1 = yr + ((b * 2 + 1) * D + d) * L;
-    y[p * L + l] = Elem<T>::from_f32(y0[l] + y1[L - 1 - l]);
+    float v = y0[l] + y1[L - 1 - l];
+    if (GATE) v *= silu_f32(Elem<T>::load(z + p * L + l));
+    y[p * L + l] = Elem<T>::from_f32(v);
   }
 }
 
-// Vectorized two-route merge for L a multiple of 4: 4 consecutive outputs per thread.
-template <typename T>
+// Vectorized two-route merge over whole images: with D * L a multiple of 4, the outputs of
+// image b form one contiguous run of D * L elements, as do the route-0 outputs (the routes
+// are the outer dimension of the per-route buffer).  Each thread takes 4 consecutive
+// elements e .. e+3 of the run: route 0 with one 16-byte load, route 1 (reversed within each
+// plane of length L) with four 4-byte loads that may straddle a plane boundary.
+template <typename T, bool GATE>
 __global__ void __launch_bounds__(256)
-k_merge2_vec(const float* __restrict__ yr, T* __restrict__ y, int D, int L, int64_t planes) {
-  const int l = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
-  if (l >= L) return;
-  for (int64_t p = blockIdx.y; p < planes; p += gridDim.y) {
-    const int64_t b = p / D, d = p % D;
-    const float* y0 = yr + ((b * 2 + 0) * D + d) * L;
-    const float* y1 = yr + ((b * 2 + 1) * D + d) * L;
-    const float4 a = load4_stream(y0 + l);
-    const float4 r = load4_stream(y1 + (L - 4 - l));
-    Out4<T>::store(y + p * L + l, a.x + r.w, a.y + r.z, a.z + r.y, a.w + r.x);
+k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D,
+             int L, int64_t images) {
+  const int64_t run = static_cast<int64_t>(D) * L;
+  const int64_t e = 4 * (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+  if (e >= run) return;
+  for (int64_t b = blockIdx.y; b < images; b += gridDim.y) {
+    const float* y0 = yr + b * 2 * run;
+    const float* y1 = y0 + run;
+    const float4 a = load4_stream(y0 + e);
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t d = (e + i) / L, l = (e + i) - d * L;
+      r[i] = __builtin_nontemporal_load(y1 + d * L + (L - 1 - l));
+    }
+    float v0 = a.x + r[0], v1 = a.y + r[1], v2 = a.z + r[2], v3 = a.w + r[3];
+    if constexpr (GATE) {
+      In4<T> g;
+      g.load(z + b * run + e);
+      const float4 gz = g.get();
+      v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
+    }
+    Out4<T>::store(y + b * run + e, v0, v1, v2, v3);
   }
 }
 
@@ -399,57 +445,89 @@ int launch_carry(const ScanArgs& a, hipStream_t st) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_merge4(const float* y_route, void* y, int B, int D, int H, int W, int dtype,
-                  hipStream_t st) {
-  const int64_t planes = static_cast<int64_t>(B) * D;
-  dim3 grid((W + kTr - 1) / kTr, (H + kTr - 1) / kTr,
-            static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ));
-  dim3 block(kTr, kTrRows);
-  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(y) % (dtype == 0 ? 16 : 8) == 0);
-  if (aligned && H % 4 == 0 && W % 4 == 0) {
-    dim3 g((W + 63) / 64, (H + 63) / 64,
-           static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ));
-    if (dtype == 0)
-      hipLaunchKernelGGL(k_merge4_vec<float>, g, dim3(256), 0, st, y_route,
-                         static_cast<float*>(y), D, H, W, planes);
-    else
-      hipLaunchKernelGGL(k_merge4_vec<uint16_t>, g, dim3(256), 0, st, y_route,
-                         static_cast<uint16_t*>(y), D, H, W, planes);
-    return static_cast<int>(hipGetLastError());
-  }
+namespace {
+
+// Launches one merge kernel instantiation for the element type and gate of the call.
+template <template <typename, bool> class Launch, typename... Args>
+int merge_dispatch(int dtype, const void* z, Args... args) {
   if (dtype == 0)
-    hipLaunchKernelGGL(k_merge4<float>, grid, block, 0, st, y_route, static_cast<float*>(y), D,
-                       H, W, planes);
-  else
-    hipLaunchKernelGGL(k_merge4<uint16_t>, grid, block, 0, st, y_route,
-                       static_cast<uint16_t*>(y), D, H, W, planes);
-  return static_cast<int>(hipGetLastError());
+    return z ? Launch<float, true>::run(static_cast<const float*>(z), args...)
+             : Launch<float, false>::run(nullptr, args...);
+  return z ? Launch<uint16_t, true>::run(static_cast<const uint16_t*>(z), args...)
+           : Launch<uint16_t, false>::run(nullptr, args...);
 }
 
-int launch_merge2(const float* y_route, void* y, int B, int D, int L, int dtype,
-                  hipStream_t st) {
-  const int64_t planes = static_cast<int64_t>(B) * D;
-  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(y) % (dtype == 0 ? 16 : 8) == 0);
-  if (aligned && L % 4 == 0) {
-    dim3 g((L / 4 + 255) / 256, static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ));
-    if (dtype == 0)
-      hipLaunchKernelGGL(k_merge2_vec<float>, g, dim3(256), 0, st, y_route,
-                         static_cast<float*>(y), D, L, planes);
-    else
-      hipLaunchKernelGGL(k_merge2_vec<uint16_t>, g, dim3(256), 0, st, y_route,
-                         static_cast<uint16_t*>(y), D, L, planes);
+template <typename T, bool GATE>
+struct Merge4Vec {
+  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int H,
+                 int W, int64_t planes) {
+    hipLaunchKernelGGL((k_merge4_vec<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y),
+                       D, H, W, planes);
     return static_cast<int>(hipGetLastError());
   }
-  dim3 grid((L + 255) / 256, static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ));
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_merge2<float>, grid, dim3(256), 0, st, y_route, static_cast<float*>(y),
-                       D, L, planes);
-  else
-    hipLaunchKernelGGL(k_merge2<uint16_t>, grid, dim3(256), 0, st, y_route,
-                       static_cast<uint16_t*>(y), D, L, planes);
-  return static_cast<int>(hipGetLastError());
+};
+template <typename T, bool GATE>
+struct Merge4 {
+  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int H,
+                 int W, int64_t planes) {
+    hipLaunchKernelGGL((k_merge4<T, GATE>), g, dim3(kTr, kTrRows), 0, st, yr, z,
+                       static_cast<T*>(y), D, H, W, planes);
+    return static_cast<int>(hipGetLastError());
+  }
+};
+template <typename T, bool GATE>
+struct Merge2Vec {
+  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int L,
+                 int64_t images) {
+    hipLaunchKernelGGL((k_merge2_vec<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y),
+                       D, L, images);
+    return static_cast<int>(hipGetLastError());
+  }
+};
+template <typename T, bool GATE>
+struct Merge2 {
+  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int L,
+                 int64_t planes) {
+    hipLaunchKernelGGL((k_merge2<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y), D,
+                       L, planes);
+    return static_cast<int>(hipGetLastError());
+  }
+};
+
+}  // namespace
+
+int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, int H, int W,
+                  int dtype, hipStream_t st) {
+  const int64_t planes = static_cast<int64_t>(B) * D;
+  const unsigned gz = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
+  const uintptr_t out_align = dtype == 0 ? 16 : 8;
+  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(y) % out_align == 0) &&
+                       (reinterpret_cast<uintptr_t>(z) % out_align == 0);
+  if (aligned && H % 4 == 0 && W % 4 == 0)
+    return merge_dispatch<Merge4Vec>(dtype, z, dim3((W + 63) / 64, (H + 63) / 64, gz), st,
+                                     y_route, y, D, H, W, planes);
+  return merge_dispatch<Merge4>(dtype, z, dim3((W + kTr - 1) / kTr, (H + kTr - 1) / kTr, gz), st,
+                                y_route, y, D, H, W, planes);
+}
+
+int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L, int dtype,
+                  hipStream_t st) {
+  const int64_t planes = static_cast<int64_t>(B) * D;
+  const unsigned gy = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
+  const uintptr_t out_align = dtype == 0 ? 16 : 8;
+  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(y) % out_align == 0) &&
+                       (reinterpret_cast<uintptr_t>(z) % out_align == 0);
+  const int64_t run = static_cast<int64_t>(D) * L;
+  if (aligned && run % 4 == 0) {
+    const unsigned gb = static_cast<unsigned>(B < kMaxGridZ ? B : kMaxGridZ);
+    return merge_dispatch<Merge2Vec>(dtype, z,
+                                     dim3(static_cast<unsigned>((run / 4 + 255) / 256), gb), st,
+                                     y_route, y, D, L, static_cast<int64_t>(B));
+  }
+  return merge_dispatch<Merge2>(dtype, z, dim3((L + 255) / 256, gy), st, y_route, y, D, L,
+                                planes);
 }
 
 }  // namespace ss2d

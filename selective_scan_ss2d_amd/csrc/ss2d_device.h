@@ -36,6 +36,12 @@ template <> struct Elem<uint16_t> {
 // ---- arithmetic ------------------------------------------------------------------------
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// SiLU(v) = v / (1 + e^-v), the gate nonlinearity, with the hardware reciprocal (about
+// 1 ulp).  v -> -inf gives -0 (the reciprocal of +inf), v = +inf gives +inf.
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e));
+}
+
 // softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e) with e = e^-|z| in (0, 1].  With
 // u = 1 + e rounded, c = e - (u - 1) is exactly the rounding error of u, and
 // log1p(e) = log(u) + log(1 + c/u) = log(u) + c up to c * (1 - 1/u) <= 2^-24 * log1p(e):
@@ -98,19 +104,24 @@ struct ScanArgs {
   int chunk_len;          // steps per chunk, a multiple of kChunkAlign (>= L when C == 1)
   int chunk_base;         // first chunk index covered by this launch
   int chunks_in_launch;   // chunks covered by this launch per (b, k)
+  int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
 };
 
 enum ScanMode { kModeOut = 0, kModeAgg = 1 };
 
-// Host-side launchers (defined in the .hip files).
+// Host-side launchers (defined in the .hip files).  The _zoh scan launchers run the
+// zero-order-hold discretisation of B (a.zoh set), the others delta * B.
 int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
 int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_f32_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_bf16_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st);
 int launch_carry(const ScanArgs& a, hipStream_t st);
-int launch_merge4(const float* y_route, void* y, int B, int D, int H, int W, int dtype,
-                  hipStream_t st);
-int launch_merge2(const float* y_route, void* y, int B, int D, int L, int dtype,
-                  hipStream_t st);
+// z: optional gate (NULL for none), same element type and layout as y.
+int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, int H, int W,
+                  int dtype, hipStream_t st);
+int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L,
+                  int dtype, hipStream_t st);
 
 }  // namespace ss2d

@@ -1,8 +1,8 @@
-// bfloat16 instantiations of the selective-scan kernel.
+// bfloat16 instantiations of the selective-scan kernel, delta * B discretisation.
 #include "ss2d_scan.inc"
 
 namespace ss2d {
 int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
-  return launch_scan_t<uint16_t>(a, split, vec, mode, st);
+  return launch_scan_t<uint16_t, false>(a, split, vec, mode, st);
 }
 }  // namespace ss2d

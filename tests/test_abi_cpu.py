@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 1
+    assert lib.ss2d_abi_version() == 2
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -124,6 +124,45 @@ def test_output_aliasing_an_input_rejected(lib):
         p = fake_ptrs()
         p[7] = p[i] + 64  # y starts inside input i
         assert call2d(lib, p) == bnd.SS2D_ERR_ALIAS, i
+
+
+# ---- the entry points with a gate and the zero-order-hold flag -----------------------------
+def call2d_ex(lib, ptrs, z, flags=0, B=1, D=8, H=8, W=8, N=4, dtype=0):
+    return lib.ss2d_forward_ex(*ptrs[:7], z, ptrs[7], B, D, H, W, N, dtype, flags, None)
+
+
+def call1d_ex(lib, ptrs, z, flags=0, B=1, D=8, L=16, N=4, dtype=0):
+    return lib.ss1d_bidir_forward_ex(*ptrs[:7], z, ptrs[7], B, D, L, N, dtype, flags, None)
+
+
+def test_ex_unknown_flags_rejected(lib):
+    z = (1 << 40) + 9 * (1 << 32)
+    for flags in (2, 4, -1, 1 << 20):
+        assert call2d_ex(lib, fake_ptrs(), z, flags) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call1d_ex(lib, fake_ptrs(), z, flags) == bnd.SS2D_ERR_UNSUPPORTED
+
+
+def test_ex_null_inputs_rejected_but_null_gate_allowed(lib):
+    z = (1 << 40) + 9 * (1 << 32)
+    for i in range(8):
+        p = fake_ptrs()
+        p[i] = None
+        assert call2d_ex(lib, p, z) == bnd.SS2D_ERR_NULL
+        assert call1d_ex(lib, p, z, bnd.SS2D_FLAG_ZOH) == bnd.SS2D_ERR_NULL
+    import torch
+    if not torch.cuda.is_available():  # a NULL gate is valid: the call reaches the runtime
+        assert call2d_ex(lib, fake_ptrs(), None, bnd.SS2D_FLAG_ZOH) == bnd.SS2D_ERR_HIP
+        assert call1d_ex(lib, fake_ptrs(), None) == bnd.SS2D_ERR_HIP
+
+
+def test_ex_gate_alignment_and_aliasing(lib):
+    z = (1 << 40) + 9 * (1 << 32)
+    assert call2d_ex(lib, fake_ptrs(), z + 1) == bnd.SS2D_ERR_ALIGN
+    assert call2d_ex(lib, fake_ptrs(), z + 2, dtype=0) == bnd.SS2D_ERR_ALIGN
+    p = fake_ptrs()
+    assert call2d_ex(lib, p, p[7] + 128) == bnd.SS2D_ERR_ALIAS        # gate inside y
+    assert call1d_ex(lib, p, p[7] - 64, dtype=1) == bnd.SS2D_ERR_ALIAS  # y starts inside z
+    assert call2d_ex(lib, [None] * 8, None, B=0) == bnd.SS2D_OK
 
 
 def test_valid_call_without_gpu_reports_hip_error(lib):

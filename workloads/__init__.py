@@ -163,3 +163,19 @@ def make_inputs(wl: Workload, seed: int = 0, a_log: str = "init") -> dict:
     elif wl.dtype != "f32":
         raise ValueError(f"unknown dtype {wl.dtype!r}")
     return out
+
+
+def make_gate(wl: Workload, seed: int = 0) -> dict:
+    """Seeded gate z for the gated entry points: standard normal, the shape of x (the output
+    of a linear projection, like x).  Drawn from a generator of its own so that the other
+    inputs of the same seed are unchanged.  Returns z (fp32, bf16-exact for bf16 workloads)
+    and, for bf16 workloads, its bit patterns under z_bf16."""
+    rng = np.random.default_rng([seed, 0x9a7e])
+    xshape = (wl.B, wl.D, wl.L) if wl.K == 2 else (wl.B, wl.D, wl.H, wl.W)
+    z = rng.standard_normal(xshape, dtype=np.float32)
+    out = dict(z=z)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(z)
+        out["z_bf16"] = bits
+        out["z"] = bf16_bits_to_f32(bits)
+    return out
