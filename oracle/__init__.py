@@ -31,7 +31,7 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 def build(source: os.PathLike = SOURCE, output: os.PathLike = LIBRARY) -> pathlib.Path:
     """Compile the oracle into a shared library with gcc (IEEE double, no fast-math)."""
     output = pathlib.Path(output)
-    tmp = output.with_suffix(".so.tmp")
+    tmp = output.with_suffix(f".so.tmp{os.getpid()}")  # concurrent builds never share a file
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
            "-fno-fast-math", str(source), "-o", str(tmp), "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
@@ -63,6 +63,9 @@ class Oracle:
         lib.oracle_forward_channels_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + \
             [ctypes.c_int] + [ctypes.c_int64] * 5 + [_i64p, _i64p, ctypes.c_int64, _f64p,
                                                    ctypes.c_int]
+        lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [ctypes.c_int] + [_f32p] * 8 + [_f64p] * 7 + \
+            [ctypes.c_int64] * 5 + [ctypes.c_int]
         self.lib = lib
         self.last_threads = None
 
@@ -140,6 +143,28 @@ class Oracle:
             raise RuntimeError("oracle_forward_channels rejected its arguments")
         self.last_threads = rc
         return y.reshape((bi.size,) + tuple(np.shape(x)[2:]))
+
+
+    def backward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, threads=0):
+        """Gradients of sum(dy * y) for the plain operator, float64, as a dict with keys
+        x, dt_raw, A_log, Bs, Cs, Ds, dt_bias (each the shape of that input)."""
+        (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+        dyk, dyp = self._gate(dy, x)
+        if dyp is None:
+            raise ValueError("dy is required")
+        L = H * W
+        out = dict(x=np.empty((B, D, L)), dt_raw=np.empty((B, K, D, L)),
+                   A_log=np.empty((K, D, N)), Bs=np.empty((B, K, N, L)),
+                   Cs=np.empty((B, K, N, L)), Ds=np.empty((K, D)), dt_bias=np.empty((K, D)))
+        order = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+        rc = self.lib.oracle_backward(K, *ptrs, dyp,
+                                      *[out[k].ctypes.data_as(_f64p) for k in order],
+                                      B, D, H, W, N, int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_backward rejected its arguments")
+        self.last_threads = rc
+        out["x"] = out["x"].reshape(np.shape(x))
+        return out
 
 
 _DEFAULT = None

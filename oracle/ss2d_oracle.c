@@ -237,3 +237,159 @@ int oracle_forward_channels(int K, const float *x, const float *dt_raw, const fl
     return oracle_forward_channels_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, 0, B, D,
                                       H, W, N, b_idx, d_idx, nsel, y_sel, nthreads);
 }
+
+/* ---- backward ----------------------------------------------------------------------------
+ * Gradients of L = sum over (b, d, l) of dy[b, d, l] * y[b, d, l] for the plain operator (no
+ * gate, delta * B), by reverse-mode differentiation of the recurrence above.  Per route, with
+ * g_t = dy at the position visited at step t:
+ *   lambda_t,n = g_t C_t,n + a_t+1,n lambda_t+1,n          (adjoint of h_t,n; lambda_L = 0)
+ *   dC_t,n     = g_t h_t,n              dB_t,n = lambda_t,n delta_t u_t
+ *   da_t,n     = lambda_t,n h_t-1,n     (h_-1 = 0)
+ *   ddelta_t   = sum_n (da_t,n a_t,n A_n + lambda_t,n B_t,n u_t)
+ *   du_t       = g_t D + sum_n lambda_t,n delta_t B_t,n
+ *   dA_n      += da_t,n a_t,n delta_t,   dA_log_n = A_n dA_n   (A = -exp(A_log))
+ *   dD        += g_t u_t
+ *   ddt_raw_t  = ddelta_t sigmoid(dt_raw_t + dt_bias)          (softplus' = sigmoid)
+ *   ddt_bias  += ddt_raw_t
+ * dx accumulates du_t at the visited position over the routes; dBs, dCs sum over the
+ * channels d (Bs and Cs are shared by all channels of a (b, k)).  Everything in double.
+ * Work is split over images b (each thread owns whole images, so no sum is shared between
+ * threads); the per-image contributions to dA_log, dDs and ddt_bias are added in b order. */
+
+static double sigmoid(double z) {
+    return 1.0 / (1.0 + exp(-z));
+}
+
+/* One image b, all routes and channels.  Accumulates into dx_b (D, L), ddt_b (K, D, L),
+ * dB_b, dC_b (K, N, L) and the parameter partials pA (K, D, N), pD (K, D), pbias (K, D);
+ * ws holds 2 L N + 2 L + N doubles. */
+static void image_backward(int K, const float *x, const float *dt_raw, const float *A_log,
+                           const float *Bs, const float *Cs, const float *Ds,
+                           const float *dt_bias, const float *dy, int64_t D, int64_t H,
+                           int64_t W, int64_t N, int64_t b, double *dx_b, double *ddt_b,
+                           double *dB_b, double *dC_b, double *pA, double *pD, double *pbias,
+                           double *ws) {
+    const int64_t L = H * W;
+    double *hs = ws;               /* h_t,n, t-major */
+    double *as = hs + L * N;       /* a_t,n */
+    double *delta = as + L * N;    /* delta_t */
+    double *lam = delta + L;       /* lambda_n */
+    double *A = lam + N;           /* A_n */
+    for (int64_t d = 0; d < D; ++d) {
+        const float *xc = x + (b * D + d) * L;
+        const float *gc = dy + (b * D + d) * L;
+        for (int k = 0; k < K; ++k) {
+            const double bias = dt_bias[k * D + d];
+            const double Dk = Ds[k * D + d];
+            const float *dt = dt_raw + ((b * K + k) * D + d) * L;
+            const float *Bk = Bs + (b * K + k) * N * L;
+            const float *Ck = Cs + (b * K + k) * N * L;
+            for (int64_t n = 0; n < N; ++n)
+                A[n] = -exp((double)A_log[(k * D + d) * N + n]);
+            /* forward, keeping every state */
+            for (int64_t t = 0; t < L; ++t) {
+                const double u = xc[route_position(K, k, t, H, W)];
+                delta[t] = softplus((double)dt[t] + bias);
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = exp(delta[t] * A[n]);
+                    const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;
+                    as[t * N + n] = a;
+                    hs[t * N + n] = a * hprev + delta[t] * (double)Bk[n * L + t] * u;
+                }
+            }
+            /* reverse */
+            for (int64_t n = 0; n < N; ++n)
+                lam[n] = 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t l = route_position(K, k, t, H, W);
+                const double u = xc[l];
+                const double g = gc[l];
+                double ddelta = 0.0, du = g * Dk;
+                pD[k * D + d] += g * u;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double anext = t + 1 < L ? as[(t + 1) * N + n] : 0.0;
+                    lam[n] = g * (double)Ck[n * L + t] + anext * lam[n];
+                    const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;
+                    const double a = as[t * N + n];
+                    const double da = lam[n] * hprev;
+                    dC_b[(k * N + n) * L + t] += g * hs[t * N + n];
+                    dB_b[(k * N + n) * L + t] += lam[n] * delta[t] * u;
+                    ddelta += da * a * A[n] + lam[n] * (double)Bk[n * L + t] * u;
+                    pA[(k * D + d) * N + n] += da * a * delta[t] * A[n];
+                    du += lam[n] * delta[t] * (double)Bk[n * L + t];
+                }
+                const double dz = ddelta * sigmoid((double)dt[t] + bias);
+                ddt_b[(k * D + d) * L + t] = dz;
+                pbias[k * D + d] += dz;
+                dx_b[d * L + l] += du;
+            }
+        }
+    }
+}
+
+/* Gradients of sum(dy * y) with respect to every input (outputs in double, caller-owned):
+ *   dx (B, D, H, W), ddt_raw (B, K, D, L), dA_log (K, D, N), dBs, dCs (B, K, N, L),
+ *   dDs, ddt_bias (K, D).
+ * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
+int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_log,
+                    const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                    const float *dy, double *dx, double *ddt_raw, double *dA_log, double *dBs,
+                    double *dCs, double *dDs, double *ddt_bias, int64_t B, int64_t D,
+                    int64_t H, int64_t W, int64_t N, int nthreads) {
+    if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
+        return -1;
+    if (K == 2 && H != 1)
+        return -1;
+    const int threads = pick_threads(nthreads);
+    const int64_t L = H * W;
+    const int64_t np = K * D * N + 2 * K * D; /* per-image parameter partials */
+    double *part = (double *)calloc((size_t)(B > 0 ? B : 1) * (size_t)np, sizeof(double));
+    if (!part)
+        return -1;
+    for (int64_t i = 0; i < B * D * L; ++i)
+        dx[i] = 0.0;
+    for (int64_t i = 0; i < B * K * N * L; ++i) {
+        dBs[i] = 0.0;
+        dCs[i] = 0.0;
+    }
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+#endif
+    {
+        double *ws = (double *)malloc(sizeof(double) * (size_t)(2 * L * N + 2 * L + 2 * N));
+        if (!ws) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t b = 0; b < B; ++b) {
+                double *p = part + b * np;
+                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, D, H, W, N, b,
+                               dx + b * D * L, ddt_raw + b * K * D * L, dBs + b * K * N * L,
+                               dCs + b * K * N * L, p, p + K * D * N, p + K * D * N + K * D,
+                               ws);
+            }
+            free(ws);
+        }
+    }
+    for (int64_t i = 0; i < K * D * N; ++i)
+        dA_log[i] = 0.0;
+    for (int64_t i = 0; i < K * D; ++i) {
+        dDs[i] = 0.0;
+        ddt_bias[i] = 0.0;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        const double *p = part + b * np;
+        for (int64_t i = 0; i < K * D * N; ++i)
+            dA_log[i] += p[i];
+        for (int64_t i = 0; i < K * D; ++i) {
+            dDs[i] += p[K * D * N + i];
+            ddt_bias[i] += p[K * D * N + K * D + i];
+        }
+    }
+    free(part);
+    return failed ? -1 : threads;
+}
+

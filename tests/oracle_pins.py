@@ -26,6 +26,8 @@ What pins what:
   gate              the optional gate against sigmoid written through tanh, z = 0, z = 40
   zoh exact         zero-order hold reproduces the exact solution of h' = A h + B u for inputs
                     held constant (Vim summary, sec. 4.1, defines the ZOH discretisation)
+  backward fd       every gradient against central finite differences of the forward
+  backward adjoint  <dy, y(v) - y(0)> = <grad, v> for the inputs y is affine in; dDs closed form
 """
 from __future__ import annotations
 
@@ -428,6 +430,73 @@ def pin_zoh_exact(orc):
         assert np.max(np.abs(plain - want)) > 1e-6 * np.max(np.abs(want)), "ZOH had no effect"
 
 
+BWD_NAMES = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+
+
+def pin_backward_fd(orc):
+    """Every gradient of L = sum(dy * y), element by element, against central finite
+    differences of the forward oracle (steps of 1e-3 relative, taken as the difference of the
+    two float32 inputs actually used), on tiny inputs for both route sets."""
+    rng = _rng(16)
+    for K, xshape in ((4, (2, 2, 3, 4)), (2, (2, 2, 9))):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 2
+        args = list(_random_inputs(rng, B, K, D, N, L, xshape))
+        dy = rng.standard_normal(xshape).astype(np.float32)
+        got = orc.backward(K, *args, dy)
+
+        def loss(a):
+            return float(np.sum(orc.forward(K, *a) * dy.astype(np.float64)))
+
+        for i, name in enumerate(BWD_NAMES):
+            flat = args[i].reshape(-1)
+            fd = np.empty(flat.size)
+            for j in range(flat.size):
+                base = float(flat[j])
+                step = 1e-3 * max(1.0, abs(base))
+                hi, lo = np.float32(base + step), np.float32(base - step)
+                pert = [a.copy() for a in args]
+                pert[i].reshape(-1)[j] = hi
+                lp = loss(pert)
+                pert[i].reshape(-1)[j] = lo
+                lm = loss(pert)
+                fd[j] = (lp - lm) / (float(hi) - float(lo))
+            g = got[name].reshape(-1)
+            scale = max(float(np.max(np.abs(fd))), 1e-12)
+            err = float(np.max(np.abs(g - fd))) / scale
+            assert err < 2e-5, f"d/d{name} (K={K}) differs from finite differences: {err:.2e}"
+
+
+def pin_backward_adjoint(orc):
+    """Exact identities of reverse mode: y is linear in x and affine in Bs, Cs and Ds, so
+    <dy, y(v) - y(0)> = <dL/dinput, v> for any v (up to float64 rounding); and
+    dDs[k, d] = sum over (b, l) of dy * x for every route k."""
+    rng = _rng(17)
+    for K, xshape in ((4, (2, 3, 5, 4)), (2, (2, 3, 23))):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 4
+        args = list(_random_inputs(rng, B, K, D, N, L, xshape))
+        dy = rng.standard_normal(xshape).astype(np.float32)
+        got = orc.backward(K, *args, dy)
+        dyd = dy.astype(np.float64)
+        for i, name in ((0, "x"), (3, "Bs"), (4, "Cs"), (5, "Ds")):
+            v = rng.standard_normal(args[i].shape).astype(np.float32)
+            with_v = list(args)
+            with_v[i] = v
+            zero = list(args)
+            zero[i] = np.zeros_like(args[i])
+            lhs = float(np.sum(dyd * (orc.forward(K, *with_v) - orc.forward(K, *zero))))
+            rhs = float(np.sum(got[name] * v.astype(np.float64)))
+            assert abs(lhs - rhs) <= 1e-10 * max(abs(lhs), 1.0), \
+                f"adjoint identity for {name} (K={K}): {lhs} vs {rhs}"
+        want = np.einsum("bdl,bdl->d", dyd.reshape(B, D, L),
+                         args[0].astype(np.float64).reshape(B, D, L))
+        _close(got["Ds"], np.broadcast_to(want, (K, D)), 1e-12, 1e-13, f"dDs closed form, K={K}")
+
+
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
-            pin_linearity, pin_channels, pin_gate, pin_zoh_exact]
+            pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
+            pin_backward_adjoint]

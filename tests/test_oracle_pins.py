@@ -30,7 +30,11 @@ def test_pin(orc, pin):
 # must make at least one pin fail.
 MUTATIONS = [
     ("drop skip term", "out[l] += (yk + Dk * u) * gate;", "out[l] += yk * gate;"),
-    ("A sign", "A[n] = -exp(", "A[n] = exp("),
+    ("A sign", "A[n] = -exp((double)A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;",
+     "A[n] = exp((double)A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;"),
+    ("bwd: A sign in the recomputed forward",
+     "A[n] = -exp((double)A_log[(k * D + d) * N + n]);\n            /* forward",
+     "A[n] = exp((double)A_log[(k * D + d) * N + n]);\n            /* forward"),
     ("output before update",
      "h[n] = a * h[n] + bbar * (double)Bk[n * L + t] * u;\n"
      "                yk += (double)Ck[n * L + t] * h[n];",
@@ -42,19 +46,25 @@ MUTATIONS = [
     ("column route transposed", "return (t % H) * W + t / H;", "return (t % W) * H + t / W;"),
     ("route 1 not reversed", "case 1:\n        return L - 1 - t;", "case 1:\n        return t;"),
     ("route 3 not reversed", "s = L - 1 - t;", "s = t;"),
-    ("bias outside softplus", "softplus((double)dt[t] + bias)",
-     "(softplus((double)dt[t]) + bias)"),
+    ("bias outside softplus", "const double delta = softplus((double)dt[t] + bias);",
+     "const double delta = (softplus((double)dt[t]) + bias);"),
     ("no delta on B", "double bbar = delta;", "double bbar = 1.0;"),
     ("softplus wrong", "return m + log1p(exp(-fabs(z)));", "return m + log1p(exp(fabs(z)));"),
     ("C replaced by B", "yk += (double)Ck[n * L + t]", "yk += (double)Bk[n * L + t]"),
     ("B layout (L, N)", "bbar * (double)Bk[n * L + t] * u", "bbar * (double)Bk[t * N + n] * u"),
-    ("delta read at image position", "(double)dt[t] + bias", "(double)dt[l] + bias"),
+    ("delta read at image position", "const double delta = softplus((double)dt[t] + bias);",
+     "const double delta = softplus((double)dt[l] + bias);"),
     ("backward 1D route not reversed", "return k == 0 ? t : L - 1 - t;", "return t;"),
-    ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]", "A_log[(k * N + n) * D + d]"),
-    ("Ds indexed (D, K)", "Ds[k * D + d]", "Ds[(d * K + k) % (K * D)]"),
-    ("dt_bias shared by routes", "dt_bias[k * D + d]", "dt_bias[d]"),
-    ("x ignores batch", "x + (b * D + d) * L", "x + d * L"),
-    ("Cs ignores batch", "Cs + (b * K + k) * N * L", "Cs + k * N * L"),
+    ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;",
+     "A_log[(k * N + n) * D + d]);\n            h[n] = 0.0;"),
+    ("Ds indexed (D, K)", "\n        const double Dk = Ds[k * D + d];",
+     "\n        const double Dk = Ds[(d * K + k) % (K * D)];"),
+    ("dt_bias shared by routes", "\n        const double bias = dt_bias[k * D + d];",
+     "\n        const double bias = dt_bias[d];"),
+    ("x ignores batch", "const float *xc = x + (b * D + d) * L;\n    const float *zc",
+     "const float *xc = x + d * L;\n    const float *zc"),
+    ("Cs ignores batch", "\n        const float *Ck = Cs + (b * K + k) * N * L;",
+     "\n        const float *Ck = Cs + k * N * L;"),
     ("state not reset per route", "            h[n] = 0.0;\n", "\n"),
     ("gate is the sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     ("gate misses the skip term", "out[l] += (yk + Dk * u) * gate;",
@@ -65,6 +75,46 @@ MUTATIONS = [
     ("ZOH divided by delta", "bbar = expm1(delta * A[n]) / A[n];",
      "bbar = expm1(delta * A[n]) / delta;"),
     ("ZOH ignored", "if (zoh && A[n] != 0.0)", "if (0)"),
+    ("bwd: adjoint without decay", "lam[n] = g * (double)Ck[n * L + t] + anext * lam[n];",
+     "lam[n] = g * (double)Ck[n * L + t] + lam[n];"),
+    ("bwd: adjoint decays with the current step",
+     "const double anext = t + 1 < L ? as[(t + 1) * N + n] : 0.0;",
+     "const double anext = as[t * N + n];"),
+    ("bwd: dC from the previous state", "dC_b[(k * N + n) * L + t] += g * hs[t * N + n];",
+     "dC_b[(k * N + n) * L + t] += g * hprev;"),
+    ("bwd: dB without delta", "dB_b[(k * N + n) * L + t] += lam[n] * delta[t] * u;",
+     "dB_b[(k * N + n) * L + t] += lam[n] * u;"),
+    ("bwd: decay derivative from the current state",
+     "const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;\n"
+     "                    const double a = as[t * N + n];",
+     "const double hprev = hs[t * N + n];\n"
+     "                    const double a = as[t * N + n];"),
+    ("bwd: ddelta without the decay term", "ddelta += da * a * A[n] + lam[n]",
+     "ddelta += lam[n]"),
+    ("bwd: softplus derivative without the bias", "sigmoid((double)dt[t] + bias)",
+     "sigmoid((double)dt[t])"),
+    ("bwd: dA_log without the chain factor A", "pA[(k * D + d) * N + n] += da * a * delta[t] * A[n];",
+     "pA[(k * D + d) * N + n] += da * a * delta[t];"),
+    ("bwd: du without the skip term", "double ddelta = 0.0, du = g * Dk;",
+     "double ddelta = 0.0, du = 0.0;"),
+    ("bwd: dx at the scan step", "dx_b[d * L + l] += du;", "dx_b[d * L + t] += du;"),
+    ("bwd: dDs from the output gradient alone", "pD[k * D + d] += g * u;", "pD[k * D + d] += g;"),
+    ("bwd: bias outside softplus", "delta[t] = softplus((double)dt[t] + bias);",
+     "delta[t] = (softplus((double)dt[t]) + bias);"),
+    ("bwd: delta read at the image position", "delta[t] = softplus((double)dt[t] + bias);",
+     "delta[t] = softplus((double)dt[route_position(K, k, t, H, W)] + bias);"),
+    ("bwd: A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]);\n            /* forward",
+     "A_log[(k * N + n) * D + d]);\n            /* forward"),
+    ("bwd: Ds indexed (D, K)", "\n            const double Dk = Ds[k * D + d];",
+     "\n            const double Dk = Ds[(d * K + k) % (K * D)];"),
+    ("bwd: dt_bias shared by routes", "\n            const double bias = dt_bias[k * D + d];",
+     "\n            const double bias = dt_bias[d];"),
+    ("bwd: x ignores batch", "const float *xc = x + (b * D + d) * L;\n        const float *gc",
+     "const float *xc = x + d * L;\n        const float *gc"),
+    ("bwd: Cs ignores batch", "\n            const float *Ck = Cs + (b * K + k) * N * L;",
+     "\n            const float *Ck = Cs + k * N * L;"),
+    ("bwd: dy ignores batch", "const float *gc = dy + (b * D + d) * L;",
+     "const float *gc = dy + d * L;"),
 ]
 
 
