@@ -44,6 +44,14 @@ ZOH_FLOPS_PER_UPDATE = 9
 ZOH_ISSUE_SLOTS_PER_UPDATE = 6 + 2
 ZOH_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / ZOH_ISSUE_SLOTS_PER_UPDATE * ZOH_FLOPS_PER_UPDATE
                           / 1e12)
+# Backward, per state update: the forward recompute (delta*A, (delta*u)*B, the h update: 4
+# flops, one exp) and the adjoint (g*C and the lambda update: 3; dC, dB: 2; lambda*h_prev*a:
+# 2; the sums over n for ddelta and du: 4; dA: 2): 17 flops in at least 12 VALU slots plus
+# the exp.
+BWD_FLOPS_PER_UPDATE = 17
+BWD_ISSUE_SLOTS_PER_UPDATE = 12 + 2
+BWD_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / BWD_ISSUE_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE
+                          / 1e12)
 HBM_PEAK_GBPS = 8000.0
 ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
 
@@ -78,6 +86,31 @@ def measured_traffic(workload: str):
     if d.get("source_hash") != kernel_source_hash():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
+    """The float64 oracle's backward, as it is, on all host cores, over a bounded sample of
+    whole images (its unit of work: dBs and dCs sum over every channel of an image)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.Oracle()
+
+    def run(n):
+        sl = [inp[k][:n] if k in ("x", "dt_raw", "Bs", "Cs") else inp[k] for k in ARGS]
+        t0 = time.perf_counter()
+        orc.backward(wl.K, *sl, dy[:n], threads=cores)
+        return time.perf_counter() - t0
+
+    n = min(wl.B, max(1, cores))
+    dt = run(n)
+    if n < wl.B and dt < target_s:
+        n = int(min(wl.B, max(n, n * target_s / max(dt, 1e-3))))
+        dt = run(n)
+    upd = n * wl.K * wl.D * wl.L * wl.N
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
+            "kind": "oracle",
+            "sample": f"backward of {n} of {wl.B} images of {wl.name} (all {wl.K} routes and "
+                      f"{wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
 
 
 def cpu_baseline(wl, inp, target_s: float, z=None, zoh=False) -> dict:
@@ -124,6 +157,8 @@ def main() -> int:
                     help="gated entry point: y * SiLU(z), z of the shape of x")
     ap.add_argument("--zoh", action="store_true",
                     help="zero-order-hold discretisation of B")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward entry point (gradients of sum(dy * y))")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 device-to-device copies of MIB "
                          "MiB (a plain copy kernel of known size, for scaling the HBM byte "
@@ -171,7 +206,16 @@ def main() -> int:
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    if args.gate or args.zoh:
+    if args.backward and (args.gate or args.zoh):
+        log("the backward entry point covers the plain operator only")
+        return 2
+    if args.backward:
+        g = workloads.make_output_grad(wl, 0)
+        dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
+              if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
+        fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
+        call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
+    elif args.gate or args.zoh:
         fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
         z = None
         if gate is not None:
@@ -211,26 +255,35 @@ def main() -> int:
     log(f"step {ms_step * 1e3:.1f} us, {upd_per_s:.4e} updates/s, algorithmic {gbps:.1f} GB/s")
 
     # Dominant kernel: the scan (with the chunked plan, both scan passes are counted).
-    scan_ms, scan_n = kernels["scan"]
-    agg_ms, _ = kernels["chunk_agg"]
+    if args.backward:
+        scan_ms, scan_n = kernels["scan_bwd"]
+        agg_ms = 0.0
+    else:
+        scan_ms, scan_n = kernels["scan"]
+        agg_ms, _ = kernels["chunk_agg"]
     scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
     flops, peak = ((ZOH_FLOPS_PER_UPDATE, ZOH_UPDATE_PEAK_TFLOPS) if args.zoh
+                   else (BWD_FLOPS_PER_UPDATE, BWD_UPDATE_PEAK_TFLOPS) if args.backward
                    else (FLOPS_PER_UPDATE, UPDATE_PEAK_TFLOPS))
     achieved = wl.updates * flops / scan_avg_s / 1e12
     traffic = measured_traffic(wl.name)
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
                 "peak": round(peak, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
-                "traffic": traffic if not (args.gate or args.zoh) else None,
-                "kernel": "k_scan", "kernel_avg_us": round(scan_avg_s * 1e6, 1),
+                "traffic": traffic if not (args.gate or args.zoh or args.backward) else None,
+                "kernel": "k_scan_bwd" if args.backward else "k_scan",
+                "kernel_avg_us": round(scan_avg_s * 1e6, 1),
                 "frac_of_fma_peak": round(achieved / FMA_PEAK_TFLOPS, 4),
                 "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
-                           zoh=args.zoh)
+        if args.backward:
+            cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
+                               zoh=args.zoh)
         log(f"  {cpu['sample']} on {cpu['cores']} threads: {cpu['value']:.3e} updates/s")
 
     out = {
@@ -249,7 +302,7 @@ def main() -> int:
         "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "H": wl.H, "W": wl.W,
                    "L": wl.L, "N": wl.N, "K": wl.K, "io_dtype": wl.dtype,
                    "state_dtype": "f32", "A_log": args.a_log, "gate": bool(args.gate),
-                   "zoh": bool(args.zoh)},
+                   "zoh": bool(args.zoh), "pass": "backward" if args.backward else "forward"},
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kernels.items() if n},

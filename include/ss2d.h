@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 2
+#define SS2D_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -128,6 +128,38 @@ int ss1d_bidir_forward_ex(const void *x, const void *dt_raw, const float *A_log,
                           const float *dt_bias, const void *z, void *y, int64_t B, int64_t D,
                           int64_t L, int64_t N, int dtype, int flags, void *stream);
 
+/* ---- backward ---------------------------------------------------------------------------
+ * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output
+ * of ss2d_forward (ss1d_bidir_forward) on the same inputs, with respect to every input:
+ *   dx (shape of x), ddt_raw (shape of dt_raw), dBs, dCs (shape of Bs, Cs): the data type
+ *     of x (dtype), each rounded once from an fp32 sum;
+ *   dA_log (K, D, N), dDs (K, D), ddt_bias (K, D): fp32.
+ * dy has the shape and data type of x.  Every output is written in full (not accumulated
+ * into) and must overlap neither an input nor another output.
+ *
+ * The gradients follow reverse-mode differentiation of the forward recurrence (the Vim
+ * summary, section 4.4: the backward pass recomputes the intermediate states instead of
+ * storing them): per route, the adjoint lambda_t = dy_t C_t + Abar_t+1 lambda_t+1 runs
+ * backwards from the end of the sequence; dC_t += dy_t h_t and dB_t += lambda_t delta_t u_t
+ * are summed over the channels that share Bs and Cs; delta's gradient passes softplus'
+ * derivative sigmoid(dt_raw + dt_bias).  States are recomputed from checkpoints taken every
+ * 32 steps (scratch, 4 B * B * K * D * ceil(L / 32) * N); sums over channels and images are
+ * taken in a fixed order, so results are deterministic.
+ *
+ * Supported: the plain operator (no gate, delta * B) with N in {4, 8, 16}; other N give
+ * SS2D_ERR_UNSUPPORTED.  Otherwise the conventions of ss2d_forward apply. */
+int ss2d_backward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                  const void *Cs, const float *Ds, const float *dt_bias, const void *dy,
+                  void *dx, void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
+                  float *ddt_bias, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                  int dtype, void *stream);
+
+int ss1d_bidir_backward(const void *x, const void *dt_raw, const float *A_log,
+                        const void *Bs, const void *Cs, const float *Ds,
+                        const float *dt_bias, const void *dy, void *dx, void *ddt_raw,
+                        float *dA_log, void *dBs, void *dCs, float *dDs, float *ddt_bias,
+                        int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *ss2d_status_string(int status);
 
@@ -148,8 +180,11 @@ int ss2d_last_hip_error(void);
 #define SS2D_KERNEL_SCAN 1      /* selective scan producing per-route outputs          */
 #define SS2D_KERNEL_CHUNK_AGG 2 /* chunked scan, first pass (chunk end states)         */
 #define SS2D_KERNEL_CARRY 3     /* chunk carries                                       */
-#define SS2D_KERNEL_MERGE 4     /* cross-merge into y                                  */
-#define SS2D_KERNEL_KINDS 5
+#define SS2D_KERNEL_MERGE 4     /* cross-merge into y (backward: route gradients into dx) */
+#define SS2D_KERNEL_CHECKPOINT 5 /* backward: forward pass storing states every 32 steps */
+#define SS2D_KERNEL_SCAN_BWD 6  /* backward: adjoint scan                               */
+#define SS2D_KERNEL_REDUCE 7    /* backward: sums over channel blocks and images         */
+#define SS2D_KERNEL_KINDS 8
 int ss2d_timing_enable(int enable);
 int ss2d_timing_read(double *ms, int64_t *launches);
 

@@ -33,6 +33,8 @@ SIGNATURES = {
     "ss1d_bidir_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 4 + [ctypes.c_int, _P]),
     "ss2d_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 5 + [ctypes.c_int, _P]),
+    "ss1d_bidir_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 4 + [ctypes.c_int, _P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -40,7 +42,8 @@ SIGNATURES = {
     "ss2d_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64)]),
 }
-KERNEL_KINDS = ("transpose", "scan", "chunk_agg", "carry", "merge")
+KERNEL_KINDS = ("transpose", "scan", "chunk_agg", "carry", "merge", "checkpoint", "scan_bwd",
+                "reduce")
 
 
 class SS2DError(RuntimeError):
@@ -236,6 +239,43 @@ def ss1d_bidir_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=Fal
                                        _stream_handle(x.device, stream))
     _check(status)
     return y
+
+
+GRAD_NAMES = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+
+
+def _backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, xshape, L):
+    torch = _torch()
+    lib = load_library()
+    B, D, N, _ = _common(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, L)
+    ins = (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+    grads = {name: torch.empty_like(t) for name, t in zip(GRAD_NAMES, ins)}
+    args = [t.data_ptr() for t in ins] + [dy.data_ptr()] + \
+        [grads[n].data_ptr() for n in GRAD_NAMES]
+    fn = lib.ss2d_backward if K == 4 else lib.ss1d_bidir_backward
+    dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
+    _check(fn(*args, *dims, N, _dtype_code(x), _stream_handle(x.device, stream)))
+    return grads
+
+
+def ss2d_backward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream=None):
+    """Gradients of sum(dy * y) for y = ss2d_forward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias).
+
+    dy has the shape and dtype of x.  Returns a dict with the gradient of every input under
+    its name (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias), each of that input's shape and dtype.
+    """
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    return _backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, H, W), H * W)
+
+
+def ss1d_bidir_backward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream=None):
+    """Gradients of sum(dy * y) for y = ss1d_bidir_forward(...); see ss2d_backward."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L)
 
 
 def timing_enable(enable: bool = True) -> bool:

@@ -185,7 +185,8 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
   const int64_t B = a.B;
   const int64_t per = a.chunks_in_launch > 0 ? a.chunks_in_launch : 1;
   const int64_t max_b = kMaxGridZ / per > 0 ? kMaxGridZ / per : 1;
-  const int64_t L = a.L, D = a.D, K = a.K, N = a.N, C = a.num_chunks;
+  const int64_t L = a.L, D = a.D, K = a.K, N = a.N;
+  const int64_t C = mode == ss2d::kModeCkpt ? a.ck_tiles : a.num_chunks;
   for (int64_t b0 = 0; b0 < B; b0 += max_b) {
     const int64_t nb = (B - b0 < max_b) ? (B - b0) : max_b;
     ss2d::ScanArgs s = a;
@@ -195,11 +196,13 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
     s.dt_raw = static_cast<const char*>(a.dt_raw) + b0 * K * D * L * e;
     s.Bs = static_cast<const char*>(a.Bs) + b0 * K * N * L * e;
     s.Cs = static_cast<const char*>(a.Cs) + b0 * K * N * L * e;
-    s.y_route = a.y_route + b0 * K * D * L;
+    s.y_route = a.y_route ? a.y_route + b0 * K * D * L : nullptr;
     if (a.h_end) s.h_end = a.h_end + b0 * K * D * C * N;
     if (a.delta_sum) s.delta_sum = a.delta_sum + b0 * K * D * C;
     if (a.h_in) s.h_in = a.h_in + b0 * K * D * C * N;
-    const int kind = mode == ss2d::kModeAgg ? SS2D_KERNEL_CHUNK_AGG : SS2D_KERNEL_SCAN;
+    const int kind = mode == ss2d::kModeAgg    ? SS2D_KERNEL_CHUNK_AGG
+                     : mode == ss2d::kModeCkpt ? SS2D_KERNEL_CHECKPOINT
+                                               : SS2D_KERNEL_SCAN;
     const int rc = timed(kind, st, [&] { return run_scan(s, dtype, p.split, p.vec, mode, st); });
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc));
   }
@@ -313,6 +316,183 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   return SS2D_OK;
 }
 
+// ---- backward ----------------------------------------------------------------------------
+int backward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+             const void* Cs, const float* Ds, const float* dt_bias, const void* dy, void* dx,
+             void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
+             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+  if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
+  if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
+  if (N != 4 && N != 8 && N != 16) return SS2D_ERR_UNSUPPORTED;
+  if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
+  const int64_t L = H * W;
+  if (D >= (int64_t(1) << 31) / 4 || B >= (int64_t(1) << 31)) return SS2D_ERR_SHAPE;
+  int64_t n_x, n_dt, n_bc, tmp;
+  if (!mul_ok(B, D, &tmp) || !mul_ok(tmp, L, &n_x)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
+  if (B == 0 || D == 0) return SS2D_OK;
+  const void* ins[] = {x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy};
+  const void* outs[] = {dx, ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias};
+  for (const void* ptr : ins)
+    if (!ptr) return SS2D_ERR_NULL;
+  for (const void* ptr : outs)
+    if (!ptr) return SS2D_ERR_NULL;
+  const int64_t e = dtype == SS2D_F32 ? 4 : 2;
+  const uintptr_t emask = static_cast<uintptr_t>(e - 1);
+  for (const void* ptr : {x, dt_raw, Bs, Cs, dy, static_cast<const void*>(dx),
+                          static_cast<const void*>(ddt_raw), static_cast<const void*>(dBs),
+                          static_cast<const void*>(dCs)})
+    if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
+  for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
+                          static_cast<const void*>(dt_bias), static_cast<const void*>(dA_log),
+                          static_cast<const void*>(dDs), static_cast<const void*>(ddt_bias)})
+    if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
+  const int64_t in_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
+                              int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e};
+  const int64_t out_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
+                               int64_t(K) * D * 4, int64_t(K) * D * 4};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SS2D_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SS2D_ERR_ALIAS;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0;
+  hipError_t he = hipGetDevice(&device);
+  if (he != hipSuccess) return hip_fail(he);
+  int rc = prepare_pool(device);
+  if (rc != SS2D_OK) return rc;
+
+  // Scratch: transposes of x and dy, checkpoints, per-route du, dB/dC block partials and the
+  // per-image parameter partials.
+  const int64_t tiles = (L + 31) / 32;
+  const int64_t n_cb = (D + 63) / 64;
+  const bool need_t = (K == 4) && H > 1 && W > 1;
+  size_t off = 0;
+  const size_t off_xt = off;
+  if (need_t) off = align256(off + size_t(n_x * e));
+  const size_t off_gt = off;
+  if (need_t) off = align256(off + size_t(n_x * e));
+  const size_t off_ck = off;
+  off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
+  const size_t off_du = off;
+  off = align256(off + size_t(n_dt) * 4);
+  const size_t off_bc = off;
+  off = align256(off + size_t(B * K * n_cb) * size_t(2 * N * L) * 4);
+  const size_t off_pa = off;
+  off = align256(off + size_t(B * K * D * N) * 4);
+  const size_t off_pd = off;
+  off = align256(off + size_t(B * K * D) * 4);
+  const size_t off_pb = off;
+  off = align256(off + size_t(B * K * D) * 4);
+  char* ws = nullptr;
+  he = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
+  if (he != hipSuccess) return hip_fail(he);
+
+  int err = 0;
+  const void* xt = need_t ? static_cast<const void*>(ws + off_xt) : x;
+  const void* gt = need_t ? static_cast<const void*>(ws + off_gt) : dy;
+  if (need_t) {
+    err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
+      return ss2d::launch_transpose(x, ws + off_xt, int(B), int(D), int(H), int(W), dtype, st);
+    });
+    if (!err)
+      err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
+        return ss2d::launch_transpose(dy, ws + off_gt, int(B), int(D), int(H), int(W), dtype,
+                                      st);
+      });
+  }
+  // Checkpoints: the forward scan storing the state before every 32-step tile.
+  if (!err) {
+    ss2d::ScanArgs a{};
+    a.x_row = x;
+    a.x_col = xt;
+    a.dt_raw = dt_raw;
+    a.Bs = Bs;
+    a.Cs = Cs;
+    a.A_log = A_log;
+    a.Ds = Ds;
+    a.dt_bias = dt_bias;
+    a.h_in = reinterpret_cast<float*>(ws + off_ck);
+    a.B = int(B);
+    a.K = K;
+    a.D = int(D);
+    a.L = int(L);
+    a.N = int(N);
+    a.num_chunks = 1;
+    a.chunk_len = int(tiles * 32);
+    a.chunk_base = 0;
+    a.chunks_in_launch = 1;
+    a.ck_tiles = int(tiles);
+    Plan p;
+    p.split = 4;
+    p.vec = ((L % (dtype == SS2D_F32 ? 4 : 8)) == 0) &&
+            (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+            (reinterpret_cast<uintptr_t>(dt_raw) % 16 == 0);
+    rc = scan_pass(a, dtype, p, ss2d::kModeCkpt, e, st);
+  }
+  // Adjoint scan, in batches of images that keep gridDim.z in range.
+  for (int64_t b0 = 0; !err && rc == SS2D_OK && b0 < B; b0 += kMaxGridZ) {
+    const int64_t nb = (B - b0 < kMaxGridZ) ? (B - b0) : kMaxGridZ;
+    ss2d::BwdArgs g{};
+    g.x_row = static_cast<const char*>(x) + b0 * D * L * e;
+    g.x_col = static_cast<const char*>(xt) + b0 * D * L * e;
+    g.g_row = static_cast<const char*>(dy) + b0 * D * L * e;
+    g.g_col = static_cast<const char*>(gt) + b0 * D * L * e;
+    g.dt_raw = static_cast<const char*>(dt_raw) + b0 * K * D * L * e;
+    g.Bs = static_cast<const char*>(Bs) + b0 * K * N * L * e;
+    g.Cs = static_cast<const char*>(Cs) + b0 * K * N * L * e;
+    g.A_log = A_log;
+    g.Ds = Ds;
+    g.dt_bias = dt_bias;
+    g.h_ck = reinterpret_cast<const float*>(ws + off_ck) + b0 * K * D * tiles * N;
+    g.du_route = reinterpret_cast<float*>(ws + off_du) + b0 * K * D * L;
+    g.ddt_raw = static_cast<char*>(ddt_raw) + b0 * K * D * L * e;
+    g.dbc_part = reinterpret_cast<float*>(ws + off_bc) + b0 * K * n_cb * 2 * N * L;
+    g.dA_part = reinterpret_cast<float*>(ws + off_pa) + b0 * K * D * N;
+    g.dD_part = reinterpret_cast<float*>(ws + off_pd) + b0 * K * D;
+    g.dbias_part = reinterpret_cast<float*>(ws + off_pb) + b0 * K * D;
+    g.B = int(nb);
+    g.K = K;
+    g.D = int(D);
+    g.L = int(L);
+    g.N = int(N);
+    g.ck_tiles = int(tiles);
+    g.n_cb = int(n_cb);
+    err = timed(SS2D_KERNEL_SCAN_BWD, st, [&] {
+      return dtype == SS2D_F32 ? ss2d::launch_scan_bwd_f32(g, st)
+                               : ss2d::launch_scan_bwd_bf16(g, st);
+    });
+  }
+  if (!err && rc == SS2D_OK)
+    err = timed(SS2D_KERNEL_REDUCE, st, [&] {
+      return ss2d::launch_bwd_reduce_bc(reinterpret_cast<const float*>(ws + off_bc), dBs, dCs,
+                                        int(B), K, int(N), int(L), int(n_cb), dtype, st);
+    });
+  if (!err && rc == SS2D_OK)
+    err = timed(SS2D_KERNEL_REDUCE, st, [&] {
+      return ss2d::launch_bwd_reduce_params(
+          reinterpret_cast<const float*>(ws + off_pa), reinterpret_cast<const float*>(ws + off_pd),
+          reinterpret_cast<const float*>(ws + off_pb), dA_log, dDs, ddt_bias, int(B), K, int(D),
+          int(N), st);
+    });
+  if (!err && rc == SS2D_OK)
+    err = timed(SS2D_KERNEL_MERGE, st, [&] {
+      const float* du = reinterpret_cast<const float*>(ws + off_du);
+      return (K == 4) ? ss2d::launch_merge4(du, nullptr, dx, int(B), int(D), int(H), int(W),
+                                            dtype, st)
+                      : ss2d::launch_merge2(du, nullptr, dx, int(B), int(D), int(L), dtype, st);
+    });
+  const hipError_t fe = hipFreeAsync(ws, st);
+  if (err) return hip_fail(static_cast<hipError_t>(err));
+  if (rc != SS2D_OK) return rc;
+  if (fe != hipSuccess) return hip_fail(fe);
+  return SS2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +525,24 @@ int ss1d_bidir_forward_ex(const void* x, const void* dt_raw, const float* A_log,
                           int64_t L, int64_t N, int dtype, int flags, void* stream) {
   return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype, flags,
                  stream);
+}
+
+int ss2d_backward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                  const void* Cs, const float* Ds, const float* dt_bias, const void* dy,
+                  void* dx, void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs,
+                  float* ddt_bias, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                  int dtype, void* stream) {
+  return backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream);
+}
+
+int ss1d_bidir_backward(const void* x, const void* dt_raw, const float* A_log,
+                        const void* Bs, const void* Cs, const float* Ds,
+                        const float* dt_bias, const void* dy, void* dx, void* ddt_raw,
+                        float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
+                        int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
+  return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream);
 }
 
 const char* ss2d_status_string(int status) {

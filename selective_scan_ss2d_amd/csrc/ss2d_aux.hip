@@ -397,7 +397,74 @@ k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restric
   }
 }
 
+// dBs[b, k, n, t] and dCs[b, k, n, t]: sums of the backward kernel's per-channel-block
+// partials (B, K, n_cb, 2N, L), over the channel blocks in order, rounded once.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_bwd_reduce_bc(const float* __restrict__ part, T* __restrict__ dBs, T* __restrict__ dCs,
+                int N, int L, int n_cb, int64_t total) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;                      // i = ((bk * 2N) + n2) * L + t
+  const int t = static_cast<int>(i % L);
+  const int64_t q = i / L;
+  const int n2 = static_cast<int>(q % (2 * N));
+  const int64_t bk = q / (2 * N);
+  const float* p = part + (bk * n_cb * 2 * N + n2) * static_cast<int64_t>(L) + t;
+  float v = 0.0f;
+  for (int c = 0; c < n_cb; ++c) v += p[static_cast<int64_t>(c) * 2 * N * L];
+  T* dst = n2 < N ? dBs : dCs;
+  dst[(bk * N + (n2 % N)) * static_cast<int64_t>(L) + t] = Elem<T>::from_f32(v);
+}
+
+// dA_log, dDs, ddt_bias: sums over images, in image order, of the per-image partials.
+__global__ void __launch_bounds__(256)
+k_bwd_reduce_params(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
+                    const float* __restrict__ dbias_part, float* __restrict__ dA_log,
+                    float* __restrict__ dDs, float* __restrict__ ddt_bias, int B, int KD, int N) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nA = static_cast<int64_t>(KD) * N;
+  if (i >= nA + 2 * KD) return;
+  const float* src;
+  int64_t stride;
+  float* dst;
+  if (i < nA) {
+    src = dA_part + i; stride = nA; dst = dA_log + i;
+  } else if (i < nA + KD) {
+    src = dD_part + (i - nA); stride = KD; dst = dDs + (i - nA);
+  } else {
+    src = dbias_part + (i - nA - KD); stride = KD; dst = ddt_bias + (i - nA - KD);
+  }
+  float v = 0.0f;
+  for (int b = 0; b < B; ++b) v += src[b * stride];
+  *dst = v;
+}
+
 }  // namespace
+
+int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, int N, int L,
+                         int n_cb, int dtype, hipStream_t st) {
+  const int64_t total = static_cast<int64_t>(B) * K * 2 * N * L;
+  const unsigned blocks = static_cast<unsigned>((total + 255) / 256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_bwd_reduce_bc<float>, dim3(blocks), dim3(256), 0, st, part,
+                       static_cast<float*>(dBs), static_cast<float*>(dCs), N, L, n_cb, total);
+  else
+    hipLaunchKernelGGL(k_bwd_reduce_bc<uint16_t>, dim3(blocks), dim3(256), 0, st, part,
+                       static_cast<uint16_t*>(dBs), static_cast<uint16_t*>(dCs), N, L, n_cb,
+                       total);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_bwd_reduce_params(const float* dA_part, const float* dD_part,
+                             const float* dbias_part, float* dA_log, float* dDs,
+                             float* ddt_bias, int B, int K, int D, int N, hipStream_t st) {
+  const int KD = K * D;
+  const int64_t total = static_cast<int64_t>(KD) * N + 2 * KD;
+  hipLaunchKernelGGL(k_bwd_reduce_params, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, st, dA_part, dD_part, dbias_part, dA_log, dDs, ddt_bias, B,
+                     KD, N);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st) {

@@ -85,6 +85,34 @@ __device__ __forceinline__ float quad_perm(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
 }
 
+// Value of `v` held by lane q of this lane's channel group (S lanes per channel).
+template <int S>
+__device__ __forceinline__ float from_owner(float v, int q) {
+  if constexpr (S == 1) {
+    return v;
+  } else if constexpr (S == 2) {
+    switch (q) {
+      case 0: return quad_perm<0, 0, 2, 2>(v);
+      default: return quad_perm<1, 1, 3, 3>(v);
+    }
+  } else {
+    switch (q) {
+      case 0: return quad_perm<0, 0, 0, 0>(v);
+      case 1: return quad_perm<1, 1, 1, 1>(v);
+      case 2: return quad_perm<2, 2, 2, 2>(v);
+      default: return quad_perm<3, 3, 3, 3>(v);
+    }
+  }
+}
+
+// Sum of `v` over the S lanes of this lane's channel group, in every one of them.
+template <int S>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (S >= 2) v += quad_perm<1, 0, 3, 2>(v);
+  if constexpr (S == 4) v += quad_perm<2, 3, 0, 1>(v);
+  return v;
+}
+
 // ---- launch arguments ------------------------------------------------------------------
 struct ScanArgs {
   const void* x_row;      // route source for routes 0 and 1: x, (B, D, L)
@@ -105,9 +133,34 @@ struct ScanArgs {
   int chunk_base;         // first chunk index covered by this launch
   int chunks_in_launch;   // chunks covered by this launch per (b, k)
   int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
+  int ck_tiles;           // kModeCkpt: 32-step tiles per sequence; h_in receives the states
 };
 
-enum ScanMode { kModeOut = 0, kModeAgg = 1 };
+enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2 };
+
+// Arguments of the backward scan kernel (gradients of sum(dy * y), plain operator).
+struct BwdArgs {
+  const void* x_row;      // x, (B, D, L)
+  const void* x_col;      // x transposed per plane (routes 2 and 3)
+  const void* g_row;      // dy, (B, D, L)
+  const void* g_col;      // dy transposed per plane
+  const void* dt_raw;     // (B, K, D, L)
+  const void* Bs;         // (B, K, N, L)
+  const void* Cs;         // (B, K, N, L)
+  const float* A_log;     // (K, D, N)
+  const float* Ds;        // (K, D)
+  const float* dt_bias;   // (K, D)
+  const float* h_ck;      // (B, K, D, ck_tiles, N) state before each 32-step tile (>= 1)
+  float* du_route;        // (B, K, D, L) fp32 dL/du per route, scan order
+  void* ddt_raw;          // (B, K, D, L) gradient of dt_raw, element type of the inputs
+  float* dbc_part;        // (B, K, n_cb, 2N, L) per channel-block sums of dB (rows < N), dC
+  float* dA_part;         // (B, K, D, N) per-image gradient of A_log
+  float* dD_part;         // (B, K, D) per-image gradient of Ds
+  float* dbias_part;      // (B, K, D) per-image gradient of dt_bias
+  int B, K, D, L, N;
+  int ck_tiles;           // ceil(L / 32)
+  int n_cb;               // channel blocks per (b, k): ceil(D / 64)
+};
 
 // Host-side launchers (defined in the .hip files).  The _zoh scan launchers run the
 // zero-order-hold discretisation of B (a.zoh set), the others delta * B.
@@ -118,6 +171,15 @@ int launch_scan_bf16_zoh(const ScanArgs& a, int split, bool vec, int mode, hipSt
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st);
 int launch_carry(const ScanArgs& a, hipStream_t st);
+int launch_scan_bwd_f32(const BwdArgs& a, hipStream_t st);
+int launch_scan_bwd_bf16(const BwdArgs& a, hipStream_t st);
+// Sums of the backward partials: dBs, dCs over channel blocks; dA_log, dDs, dt_bias over
+// images (fixed order).
+int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, int N, int L,
+                         int n_cb, int dtype, hipStream_t st);
+int launch_bwd_reduce_params(const float* dA_part, const float* dD_part,
+                             const float* dbias_part, float* dA_log, float* dDs,
+                             float* ddt_bias, int B, int K, int D, int N, hipStream_t st);
 // z: optional gate (NULL for none), same element type and layout as y.
 int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, int H, int W,
                   int dtype, hipStream_t st);

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 2
+    assert lib.ss2d_abi_version() == 3
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -163,6 +163,41 @@ def test_ex_gate_alignment_and_aliasing(lib):
     assert call2d_ex(lib, p, p[7] + 128) == bnd.SS2D_ERR_ALIAS        # gate inside y
     assert call1d_ex(lib, p, p[7] - 64, dtype=1) == bnd.SS2D_ERR_ALIAS  # y starts inside z
     assert call2d_ex(lib, [None] * 8, None, B=0) == bnd.SS2D_OK
+
+
+# ---- backward entry points ----------------------------------------------------------------
+def call_bwd(lib, ptrs, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4):
+    if K == 4:
+        return lib.ss2d_backward(*ptrs, B, D, H, W, N, dtype, None)
+    return lib.ss1d_bidir_backward(*ptrs, B, D, H * W, N, dtype, None)
+
+
+def test_backward_argument_errors(lib):
+    ptrs = fake_ptrs(15)
+    for K in (4, 2):
+        for i in range(15):
+            p = list(ptrs)
+            p[i] = None
+            assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        for N in (1, 2, 32, 3):
+            assert call_bwd(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
+        assert call_bwd(lib, [None] * 15, B=0, K=K) == bnd.SS2D_OK
+        for i in range(15):
+            p = list(ptrs)
+            p[i] += 1
+            assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
+        for i in range(8, 15):  # an output inside an input, or inside another output
+            p = list(ptrs)
+            p[i] = p[i - 8] + 4
+            assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i)
+        p = list(ptrs)
+        p[14] = p[8] + 128
+        assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
+    import torch
+    if not torch.cuda.is_available():
+        assert call_bwd(lib, ptrs) == bnd.SS2D_ERR_HIP
 
 
 def test_valid_call_without_gpu_reports_hip_error(lib):

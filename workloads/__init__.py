@@ -179,3 +179,18 @@ def make_gate(wl: Workload, seed: int = 0) -> dict:
         out["z_bf16"] = bits
         out["z"] = bf16_bits_to_f32(bits)
     return out
+
+
+def make_output_grad(wl: Workload, seed: int = 0) -> dict:
+    """Seeded output gradient dy for the backward entry points: standard normal, the shape of
+    x and y, from a generator of its own.  Returns dy (fp32, bf16-exact for bf16 workloads)
+    and, for bf16 workloads, its bit patterns under dy_bf16."""
+    rng = np.random.default_rng([seed, 0xd1])
+    xshape = (wl.B, wl.D, wl.L) if wl.K == 2 else (wl.B, wl.D, wl.H, wl.W)
+    dy = rng.standard_normal(xshape, dtype=np.float32)
+    out = dict(dy=dy)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(dy)
+        out["dy_bf16"] = bits
+        out["dy"] = bf16_bits_to_f32(bits)
+    return out
