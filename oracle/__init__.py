@@ -63,6 +63,11 @@ class Oracle:
         lib.oracle_forward_channels_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + \
             [ctypes.c_int] + [ctypes.c_int64] * 5 + [_i64p, _i64p, ctypes.c_int64, _f64p,
                                                    ctypes.c_int]
+        lib.oracle_forward_routes_ex.restype = ctypes.c_int
+        lib.oracle_forward_routes_ex.argtypes = lib.oracle_forward_ex.argtypes
+        lib.oracle_project.restype = ctypes.c_int
+        lib.oracle_project.argtypes = [ctypes.c_int] + [_f32p] * 5 + [_f64p] * 4 + \
+            [ctypes.c_int64] * 7 + [ctypes.c_int]
         lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [ctypes.c_int] + [_f32p] * 8 + [_f64p] * 7 + \
             [ctypes.c_int64] * 5 + [ctypes.c_int]
@@ -75,16 +80,18 @@ class Oracle:
         a = np.ascontiguousarray(a, dtype=np.float32)
         return a, a.ctypes.data_as(_f32p)
 
-    def _prep(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias):
-        x = np.asarray(x)
+    def _prep(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, xshape=None):
+        """Checks shapes against x's (or xshape's, when x is None) and returns the dims, the
+        float32 copies and their pointers (None for a missing x)."""
+        shape = tuple(np.shape(x)) if x is not None else tuple(xshape)
         if K == 4:
-            if x.ndim != 4:
+            if len(shape) != 4:
                 raise ValueError("x must be (B, D, H, W)")
-            B, D, H, W = x.shape
+            B, D, H, W = shape
         else:
-            if x.ndim != 3:
+            if len(shape) != 3:
                 raise ValueError("x must be (B, D, L)")
-            B, D, L = x.shape
+            B, D, L = shape
             H, W = 1, L
         L = H * W
         N = np.asarray(A_log).shape[-1]
@@ -96,7 +103,7 @@ class Oracle:
                 raise ValueError(f"{k} has shape {np.shape(arrs[k])}, expected {shp}")
         keep, ptrs = [], []
         for a in (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias):
-            a2, p = self._f32(a)
+            a2, p = self._f32(a) if a is not None else (None, None)
             keep.append(a2)
             ptrs.append(p)
         return (B, D, H, W, N), keep, ptrs
@@ -144,6 +151,69 @@ class Oracle:
         self.last_threads = rc
         return y.reshape((bi.size,) + tuple(np.shape(x)[2:]))
 
+    def forward_routes(self, K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, H, W, threads=0,
+                       z=None, zoh=False):
+        """y (B, D, H, W) when each route brings its own input u (B, K, D, L), in scan order
+        (K = 2: H = 1, y is (B, D, W))."""
+        u = np.asarray(u)
+        if u.ndim != 4 or u.shape[1] != K or u.shape[3] != H * W:
+            raise ValueError(f"u has shape {u.shape}, expected (B, {K}, D, {H * W})")
+        B, _, D, L = u.shape
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        (_, _, _, _, N), keep, ptrs = self._prep(K, None, dt_raw, A_log, Bs, Cs, Ds, dt_bias,
+                                                 xshape=xshape)
+        uk, up = self._f32(u)
+        zkeep, zp = self._gate(z, np.broadcast_to(np.float32(0), xshape))
+        y = np.empty((B, D, L), dtype=np.float64)
+        rc = self.lib.oracle_forward_routes_ex(K, up, *ptrs[1:], zp, ORACLE_ZOH if zoh else 0,
+                                               y.ctypes.data_as(_f64p), B, D, H, W, N,
+                                               int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_forward_routes_ex rejected its arguments")
+        self.last_threads = rc
+        return y.reshape(xshape)
+
+    def project(self, K, x, conv_w, conv_b, x_proj_w, dt_proj_w, threads=0):
+        """Per-route front end: dict of u, dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L) in scan
+        order, float64.  conv_w (K, D, KW), conv_b (K, D), x_proj_w (K, R + 2N, D),
+        dt_proj_w (K, D, R)."""
+        x = np.asarray(x)
+        if K == 4:
+            if x.ndim != 4:
+                raise ValueError("x must be (B, D, H, W)")
+            B, D, H, W = x.shape
+        else:
+            if x.ndim != 3:
+                raise ValueError("x must be (B, D, L)")
+            B, D, W = x.shape
+            H = 1
+        L = H * W
+        KW = np.shape(conv_w)[-1]
+        R = np.shape(dt_proj_w)[-1]
+        M = np.shape(x_proj_w)[1]
+        N = (M - R) // 2
+        if N <= 0 or M != R + 2 * N:
+            raise ValueError("x_proj_w must have R + 2N rows")
+        shapes = dict(conv_w=(K, D, KW), conv_b=(K, D), x_proj_w=(K, M, D), dt_proj_w=(K, D, R))
+        arrs = dict(conv_w=conv_w, conv_b=conv_b, x_proj_w=x_proj_w, dt_proj_w=dt_proj_w)
+        for k, shp in shapes.items():
+            if tuple(np.shape(arrs[k])) != shp:
+                raise ValueError(f"{k} has shape {np.shape(arrs[k])}, expected {shp}")
+        keep, ptrs = [], []
+        for a in (x, conv_w, conv_b, x_proj_w, dt_proj_w):
+            a2, p = self._f32(a)
+            keep.append(a2)
+            ptrs.append(p)
+        out = dict(u=np.empty((B, K, D, L)), dt_raw=np.empty((B, K, D, L)),
+                   Bs=np.empty((B, K, N, L)), Cs=np.empty((B, K, N, L)))
+        rc = self.lib.oracle_project(K, *ptrs,
+                                     *[out[k].ctypes.data_as(_f64p)
+                                       for k in ("u", "dt_raw", "Bs", "Cs")],
+                                     B, D, H, W, N, R, KW, int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_project rejected its arguments")
+        self.last_threads = rc
+        return out
 
     def backward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, threads=0):
         """Gradients of sum(dy * y) for the plain operator, float64, as a dict with keys
@@ -192,3 +262,13 @@ def forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx, thr
     """Output planes of the selected (b, d) channels only."""
     return default().forward_channels(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, b_idx, d_idx,
                                       threads, z=z, zoh=zoh)
+
+
+def ss2d_project(x, conv_w, conv_b, x_proj_w, dt_proj_w, threads=0):
+    """Per-route front end of the four-route operator (dict u, dt_raw, Bs, Cs), float64."""
+    return default().project(4, x, conv_w, conv_b, x_proj_w, dt_proj_w, threads)
+
+
+def ss1d_bidir_project(x, conv_w, conv_b, x_proj_w, dt_proj_w, threads=0):
+    """Per-path front end of the bidirectional 1D operator (dict u, dt_raw, Bs, Cs)."""
+    return default().project(2, x, conv_w, conv_b, x_proj_w, dt_proj_w, threads)

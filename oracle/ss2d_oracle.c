@@ -44,6 +44,10 @@
  *     Bbar = (delta A)^-1 (exp(delta A) - I) delta B).  Written with expm1 so that small
  *     |delta A| keeps its digits; A = 0 takes the limit delta * B.
  *
+ * A per-route front end (oracle_project: causal depthwise conv + SiLU, x_proj, dt_proj for
+ * each route) and the operator over its per-route inputs (oracle_forward_routes_ex) are
+ * described where they are defined, below.
+ *
  * Layouts (all contiguous, row-major):
  *   x, y      (B, D, H, W)    y written in full
  *   dt_raw    (B, K, D, L)    scan order of route k (position t is step t of that route)
@@ -93,14 +97,16 @@ static double silu(double z) {
     return z / (1.0 + exp(-z));
 }
 
-/* All K routes of one (b, d) channel, summed into out[0 .. L-1] (image order). */
-static void channel_forward(int K, const float *x, const float *dt_raw, const float *A_log,
-                            const float *Bs, const float *Cs, const float *Ds,
-                            const float *dt_bias, const float *z, int flags, int64_t D,
-                            int64_t H, int64_t W, int64_t N, int64_t b, int64_t d, double *out,
-                            double *h, double *A) {
+/* All K routes of one (b, d) channel, summed into out[0 .. L-1] (image order).  The input
+ * of step t of route k is x[b, d, pi_k(t)], or, when u_routes is given, u_routes[b, k, d, t]
+ * (each route's own input sequence, already in its scan order). */
+static void channel_forward(int K, const float *x, const float *u_routes, const float *dt_raw,
+                            const float *A_log, const float *Bs, const float *Cs,
+                            const float *Ds, const float *dt_bias, const float *z, int flags,
+                            int64_t D, int64_t H, int64_t W, int64_t N, int64_t b, int64_t d,
+                            double *out, double *h, double *A) {
     const int64_t L = H * W;
-    const float *xc = x + (b * D + d) * L;
+    const float *xc = u_routes ? NULL : x + (b * D + d) * L;
     const float *zc = z ? z + (b * D + d) * L : NULL;
     const int zoh = (flags & ORACLE_ZOH) != 0;
     for (int64_t l = 0; l < L; ++l)
@@ -115,9 +121,10 @@ static void channel_forward(int K, const float *x, const float *dt_raw, const fl
             A[n] = -exp((double)A_log[(k * D + d) * N + n]);
             h[n] = 0.0;
         }
+        const float *uk = u_routes ? u_routes + ((b * K + k) * D + d) * L : NULL;
         for (int64_t t = 0; t < L; ++t) {
             const int64_t l = route_position(K, k, t, H, W);
-            const double u = xc[l];
+            const double u = uk ? uk[t] : xc[l];
             const double delta = softplus((double)dt[t] + bias);
             double yk = 0.0;
             for (int64_t n = 0; n < N; ++n) {
@@ -146,10 +153,10 @@ static int pick_threads(int nthreads) {
 /* Full output y (B, D, H, W) in double.  K is 4 (SS2D) or 2 (bidirectional 1D, H = 1).
  * z (B, D, H, W) is the optional gate (NULL: none); flags is 0 or ORACLE_ZOH.
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
-int oracle_forward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
-                      const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
-                      const float *z, int flags, double *y, int64_t B, int64_t D, int64_t H,
-                      int64_t W, int64_t N, int nthreads) {
+static int forward_all(int K, const float *x, const float *u_routes, const float *dt_raw,
+                       const float *A_log, const float *Bs, const float *Cs, const float *Ds,
+                       const float *dt_bias, const float *z, int flags, double *y, int64_t B,
+                       int64_t D, int64_t H, int64_t W, int64_t N, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
         return -1;
     if (flags & ~ORACLE_ZOH)
@@ -173,13 +180,34 @@ int oracle_forward_ex(int K, const float *x, const float *dt_raw, const float *A
 #endif
             for (int64_t i = 0; i < total; ++i) {
                 const int64_t b = i / D, d = i % D;
-                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D, H, W,
-                                N, b, d, y + i * L, h, h + N);
+                channel_forward(K, x, u_routes, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags,
+                                D, H, W, N, b, d, y + i * L, h, h + N);
             }
             free(h);
         }
     }
     return failed ? -1 : threads;
+}
+
+int oracle_forward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
+                      const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                      const float *z, int flags, double *y, int64_t B, int64_t D, int64_t H,
+                      int64_t W, int64_t N, int nthreads) {
+    return forward_all(K, x, NULL, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, y, B, D, H, W,
+                       N, nthreads);
+}
+
+/* The same operator when every route brings its own input sequence: u (B, K, D, L), step t
+ * of route k reading u[b, k, d, t] (the per-route conv + SiLU output of oracle_project) in
+ * place of x at the position visited.  Outputs are still added at the visited positions, in
+ * route order, with the optional gate z (B, D, H, W) at those positions. */
+int oracle_forward_routes_ex(int K, const float *u, const float *dt_raw, const float *A_log,
+                             const float *Bs, const float *Cs, const float *Ds,
+                             const float *dt_bias, const float *z, int flags, double *y,
+                             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                             int nthreads) {
+    return forward_all(K, NULL, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, y, B, D, H, W,
+                       N, nthreads);
 }
 
 /* Output planes y[b_idx[i], d_idx[i], :, :] for i < nsel, written to y_sel (nsel, H, W).
@@ -212,8 +240,8 @@ int oracle_forward_channels_ex(int K, const float *x, const float *dt_raw, const
 #pragma omp for schedule(dynamic, 1)
 #endif
             for (int64_t i = 0; i < nsel; ++i)
-                channel_forward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D, H, W,
-                                N, b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
+                channel_forward(K, x, NULL, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D,
+                                H, W, N, b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
             free(h);
         }
     }
@@ -236,6 +264,91 @@ int oracle_forward_channels(int K, const float *x, const float *dt_raw, const fl
                             int64_t nsel, double *y_sel, int nthreads) {
     return oracle_forward_channels_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, 0, B, D,
                                       H, W, N, b_idx, d_idx, nsel, y_sel, nthreads);
+}
+
+/* ---- per-route front end -----------------------------------------------------------------
+ * What feeds each route's scan when every direction carries its own input layers, as in the
+ * explainer's CrossScanModule (four independent SelectiveSSM modules, one per scan direction)
+ * and in the Vim block (section 4.3: inside the forward and the backward path, a Conv1d, a
+ * SiLU, and Delta, B, C generated from the activated output).  For route k of image b, with
+ * s_t = x[b, d, pi_k(t)] the route's input sequence and s_t = 0 for t < 0:
+ *   c[d, t]      = conv_b[k, d] + sum_{j < KW} conv_w[k, d, j] * s_{t - (KW - 1) + j}
+ *                  (the explainer's depthwise Conv1d with padding d_conv - 1, of which the first
+ *                  L outputs are kept: causal, cross-correlation order of the taps)
+ *   u[d, t]      = SiLU(c[d, t])
+ *   xd[m, t]     = sum_d x_proj_w[k, m, d] * u[d, t]          m < R + 2N (x_proj, no bias)
+ *   dt_raw[d, t] = sum_{r < R} dt_proj_w[k, d, r] * xd[r, t]   (dt_proj without its bias:
+ *                  the bias is dt_bias, added inside the softplus by the scan)
+ *   Bs[n, t]     = xd[R + n, t],   Cs[n, t] = xd[R + N + n, t]
+ * (the explainer splits x_proj's output as [dt, B, C] = [1, N, N]; R is that first width).
+ * Layouts: x (B, D, H, W); conv_w (K, D, KW); conv_b (K, D); x_proj_w (K, R + 2N, D);
+ * dt_proj_w (K, D, R); outputs u, dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L) in scan order.
+ * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
+int oracle_project(int K, const float *x, const float *conv_w, const float *conv_b,
+                   const float *x_proj_w, const float *dt_proj_w, double *u, double *dt_raw,
+                   double *Bs, double *Cs, int64_t B, int64_t D, int64_t H, int64_t W,
+                   int64_t N, int64_t R, int64_t KW, int nthreads) {
+    if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0 || R <= 0 || KW <= 0)
+        return -1;
+    if (K == 2 && H != 1)
+        return -1;
+    const int threads = pick_threads(nthreads);
+    const int64_t L = H * W;
+    const int64_t M = R + 2 * N;
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+#endif
+    {
+        double *xd = (double *)malloc(sizeof(double) * (size_t)M);
+        if (!xd) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t i = 0; i < B * K; ++i) {
+                const int64_t b = i / K;
+                const int k = (int)(i % K);
+                double *uk = u + i * D * L;
+                /* causal depthwise conv along the route, then SiLU */
+                for (int64_t d = 0; d < D; ++d) {
+                    const float *xc = x + (b * D + d) * L;
+                    const float *w = conv_w + ((int64_t)k * D + d) * KW;
+                    for (int64_t t = 0; t < L; ++t) {
+                        double c = conv_b[(int64_t)k * D + d];
+                        for (int64_t j = 0; j < KW; ++j) {
+                            const int64_t tau = t - (KW - 1) + j;
+                            if (tau >= 0)
+                                c += (double)w[j] * (double)xc[route_position(K, k, tau, H, W)];
+                        }
+                        uk[d * L + t] = silu(c);
+                    }
+                }
+                /* x_proj, then dt_proj, one step at a time */
+                for (int64_t t = 0; t < L; ++t) {
+                    for (int64_t m = 0; m < M; ++m) {
+                        double acc = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            acc += (double)x_proj_w[((int64_t)k * M + m) * D + d] * uk[d * L + t];
+                        xd[m] = acc;
+                    }
+                    for (int64_t d = 0; d < D; ++d) {
+                        double acc = 0.0;
+                        for (int64_t r = 0; r < R; ++r)
+                            acc += (double)dt_proj_w[((int64_t)k * D + d) * R + r] * xd[r];
+                        dt_raw[(i * D + d) * L + t] = acc;
+                    }
+                    for (int64_t n = 0; n < N; ++n) {
+                        Bs[(i * N + n) * L + t] = xd[R + n];
+                        Cs[(i * N + n) * L + t] = xd[R + N + n];
+                    }
+                }
+            }
+            free(xd);
+        }
+    }
+    return failed ? -1 : threads;
 }
 
 /* ---- backward ----------------------------------------------------------------------------

@@ -28,6 +28,13 @@ What pins what:
                     held constant (Vim summary, sec. 4.1, defines the ZOH discretisation)
   backward fd       every gradient against central finite differences of the forward
   backward adjoint  <dy, y(v) - y(0)> = <grad, v> for the inputs y is affine in; dDs closed form
+  project impulse   a unit impulse through the per-route causal conv gives the reversed taps
+                    on the KW steps from the one that visits it, the bias elsewhere
+  project brute     numpy.convolve, scipy.special.expit and matrix products on tiny inputs
+  project select    one-hot x_proj / dt_proj rows pick single channels: split order [dt|B|C]
+                    and the weight layouts
+  routes variant    per-route inputs: the gathered x reproduces the plain operator; four
+                    different inputs give the route-order sum of single-route operators
 """
 from __future__ import annotations
 
@@ -496,7 +503,145 @@ def pin_backward_adjoint(orc):
         _close(got["Ds"], np.broadcast_to(want, (K, D)), 1e-12, 1e-13, f"dDs closed form, K={K}")
 
 
+# ---- per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj) -----------------
+def _front_weights(rng, K, D, N, R, KW):
+    conv_w = rng.standard_normal((K, D, KW)).astype(np.float32)
+    conv_b = (0.5 * rng.standard_normal((K, D))).astype(np.float32)
+    x_proj_w = (rng.standard_normal((K, R + 2 * N, D)) / np.sqrt(D)).astype(np.float32)
+    dt_proj_w = rng.standard_normal((K, D, R)).astype(np.float32)
+    return conv_w, conv_b, x_proj_w, dt_proj_w
+
+
+def pin_project_impulse(orc):
+    """A unit impulse in one channel: the route's conv output holds the taps in reverse order
+    at the KW steps from the one that visits the impulse on (cross-correlation with left
+    padding KW - 1, cut to the first L outputs: causal), the bias everywhere.  Taps and
+    biases are >= 36, where SiLU(c) = c to 1e-15 relative, and SiLU(0) = 0 exactly."""
+    for K, H, W in ((4, 3, 5), (2, 1, 7)):
+        D, N, R, KW = 3, 2, 2, 4
+        L = H * W
+        k_, d_, j_ = np.meshgrid(np.arange(K), np.arange(D), np.arange(KW), indexing="ij")
+        conv_w = (36.0 + 8.0 * j_ + 2.0 * k_ + d_).astype(np.float32)
+        routes = _routes(H, W, K)
+        rng = _rng(40)
+        _, _, x_proj_w, dt_proj_w = _front_weights(rng, K, D, N, R, KW)
+        for with_bias in (False, True):
+            conv_b = (40.0 + k_[:, :, 0] + 0.25 * d_[:, :, 0]).astype(np.float32) if with_bias \
+                else np.zeros((K, D), np.float32)
+            for p0 in (0, L - 1, L // 2 + 1):
+                x = np.zeros((1, D, L), np.float32)
+                x[0, 1, p0] = 1.0
+                xs = x.reshape((1, D, H, W)) if K == 4 else x
+                got = orc.project(K, xs, conv_w, conv_b, x_proj_w, dt_proj_w)["u"]
+                want = np.broadcast_to(conv_b.astype(np.float64)[None, :, :, None],
+                                       (1, K, D, L)).copy()
+                for k in range(K):
+                    t0 = int(np.nonzero(routes[k] == p0)[0][0])
+                    for j in range(KW):
+                        if t0 + j < L:
+                            want[0, k, 1, t0 + j] += conv_w[k, 1, KW - 1 - j]
+                _close(got, want, 1e-13, 0.0, f"impulse K={K} p0={p0} bias={with_bias}")
+        # x = 0: u = SiLU(bias).  SiLU(c) - SiLU(-c) = c, and SiLU(c) = c (1 + tanh(c / 2)) / 2
+        c = rng.uniform(-4.0, 4.0, size=(K, D)).astype(np.float32)
+        x = np.zeros((1, D, H, W) if K == 4 else (1, D, L), np.float32)
+        up = orc.project(K, x, conv_w, c, x_proj_w, dt_proj_w)["u"]
+        um = orc.project(K, x, conv_w, -c, x_proj_w, dt_proj_w)["u"]
+        c64 = np.broadcast_to(c.astype(np.float64)[None, :, :, None], up.shape)
+        _close(up - um, c64, 1e-14, 1e-15, f"SiLU odd part, K={K}")
+        _close(up, c64 * (1.0 + np.tanh(c64 / 2.0)) / 2.0, 1e-14, 1e-15, f"SiLU, K={K}")
+
+
+def _causal_xcorr(s, w):
+    """sum_j w[j] s[t - (KW - 1) + j] for t < len(s), zeros before the start: numpy's full
+    convolution with the reversed taps, cut to the first len(s) outputs."""
+    return np.convolve(s, w[::-1])[: len(s)]
+
+
+def pin_project_brute(orc):
+    """Random tiny cases against numpy.convolve, scipy.special.expit and matrix products."""
+    import scipy.special
+    for K, H, W, KW in ((4, 3, 4, 4), (4, 2, 5, 3), (2, 1, 7, 4), (2, 1, 3, 5)):
+        B, D, N, R = 2, 5, 2, 3
+        L = H * W
+        rng = _rng(41 + KW + K)
+        x = rng.standard_normal((B, D, L)).astype(np.float32)
+        conv_w, conv_b, x_proj_w, dt_proj_w = _front_weights(rng, K, D, N, R, KW)
+        xs = x.reshape((B, D, H, W)) if K == 4 else x
+        got = orc.project(K, xs, conv_w, conv_b, x_proj_w, dt_proj_w)
+        routes = _routes(H, W, K)
+        u = np.zeros((B, K, D, L))
+        for b in range(B):
+            for k in range(K):
+                for d in range(D):
+                    c = _causal_xcorr(x[b, d, routes[k]].astype(np.float64),
+                                      conv_w[k, d].astype(np.float64)) + float(conv_b[k, d])
+                    u[b, k, d] = c * scipy.special.expit(c)
+        xd = np.matmul(x_proj_w.astype(np.float64)[None], u)        # (B, K, R + 2N, L)
+        dt = np.matmul(dt_proj_w.astype(np.float64)[None], xd[:, :, :R])
+        _close(got["u"], u, 1e-12, 1e-14, f"u K={K} KW={KW}")
+        _close(got["dt_raw"], dt, 1e-11, 1e-13, f"dt_raw K={K} KW={KW}")
+        _close(got["Bs"], xd[:, :, R:R + N], 1e-11, 1e-13, f"Bs K={K} KW={KW}")
+        _close(got["Cs"], xd[:, :, R + N:], 1e-11, 1e-13, f"Cs K={K} KW={KW}")
+
+
+def pin_project_select(orc):
+    """One-hot x_proj and dt_proj rows pick single channels of u: the split of x_proj's
+    output is [dt (R rows), B (N rows), C (N rows)], x_proj is (K, R + 2N, D) with rows as
+    outputs, dt_proj is (K, D, R).  Every value is a single product with 1.0: exact."""
+    K, B, D, H, W, N, R, KW = 4, 2, 6, 3, 4, 2, 3, 4
+    M = R + 2 * N
+    rng = _rng(45)
+    x = rng.standard_normal((B, D, H, W)).astype(np.float32)
+    conv_w, conv_b, _, _ = _front_weights(rng, K, D, N, R, KW)
+    sel = np.array([[(m * 5 + k) % D for m in range(M)] for k in range(K)])
+    x_proj_w = np.zeros((K, M, D), np.float32)
+    dt_proj_w = np.zeros((K, D, R), np.float32)
+    for k in range(K):
+        x_proj_w[k, np.arange(M), sel[k]] = 1.0
+        dt_proj_w[k, np.arange(D), (np.arange(D) + k) % R] = 1.0
+    got = orc.project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w)
+    u = got["u"]
+    for k in range(K):
+        _close(got["Bs"][:, k], u[:, k, sel[k][R:R + N]], 0.0, 0.0, f"Bs rows, route {k}")
+        _close(got["Cs"][:, k], u[:, k, sel[k][R + N:]], 0.0, 0.0, f"Cs rows, route {k}")
+        pick = sel[k][(np.arange(D) + k) % R]
+        _close(got["dt_raw"][:, k], u[:, k, pick], 0.0, 0.0, f"dt_raw rows, route {k}")
+
+
+def pin_routes_variant(orc):
+    """The operator over per-route inputs: fed every route's gather of one x it is the
+    plain operator on x (same double arithmetic: equal), and fed four different inputs it is
+    the sum, in route order, of the plain operator run on each input with the other routes'
+    C and D set to zero (their terms are exact zeros)."""
+    for K, H, W in ((4, 3, 5), (2, 1, 9)):
+        B, D, N = 2, 3, 2
+        L = H * W
+        rng = _rng(46 + K)
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        routes = _routes(H, W, K)
+        x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, xshape=xshape)
+        z = rng.standard_normal(xshape).astype(np.float32)
+        xf = x.reshape(B, D, L)
+        u = np.stack([xf[:, :, routes[k]] for k in range(K)], axis=1)
+        for zoh, gate in ((False, None), (True, z)):
+            want = orc.forward(K, x, dt, A_log, Bs, Cs, Ds, bias, z=gate, zoh=zoh)
+            got = orc.forward_routes(K, u, dt, A_log, Bs, Cs, Ds, bias, H, W, z=gate, zoh=zoh)
+            _close(got, want, 0.0, 0.0, f"gathered x, K={K}, zoh={zoh}")
+        u = rng.standard_normal((B, K, D, L)).astype(np.float32)
+        want = np.zeros(xshape)
+        for k in range(K):
+            xk = np.empty((B, D, L), np.float32)
+            xk[:, :, routes[k]] = u[:, k]
+            Cs_k, Ds_k = np.zeros_like(Cs), np.zeros_like(Ds)
+            Cs_k[:, k], Ds_k[k] = Cs[:, k], Ds[k]
+            want = want + orc.forward(K, xk.reshape(xshape), dt, A_log, Bs, Cs_k, Ds_k, bias,
+                                      z=z)
+        got = orc.forward_routes(K, u, dt, A_log, Bs, Cs, Ds, bias, H, W, z=z)
+        _close(got, want, 0.0, 0.0, f"four inputs, K={K}")
+
+
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
             pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
-            pin_backward_adjoint]
+            pin_backward_adjoint, pin_project_impulse, pin_project_brute, pin_project_select,
+            pin_routes_variant]

@@ -61,8 +61,8 @@ MUTATIONS = [
      "\n        const double Dk = Ds[(d * K + k) % (K * D)];"),
     ("dt_bias shared by routes", "\n        const double bias = dt_bias[k * D + d];",
      "\n        const double bias = dt_bias[d];"),
-    ("x ignores batch", "const float *xc = x + (b * D + d) * L;\n    const float *zc",
-     "const float *xc = x + d * L;\n    const float *zc"),
+    ("x ignores batch", "const float *xc = u_routes ? NULL : x + (b * D + d) * L;",
+     "const float *xc = u_routes ? NULL : x + d * L;"),
     ("Cs ignores batch", "\n        const float *Ck = Cs + (b * K + k) * N * L;",
      "\n        const float *Ck = Cs + k * N * L;"),
     ("state not reset per route", "            h[n] = 0.0;\n", "\n"),
@@ -115,6 +115,29 @@ MUTATIONS = [
      "\n            const float *Ck = Cs + k * N * L;"),
     ("bwd: dy ignores batch", "const float *gc = dy + (b * D + d) * L;",
      "const float *gc = dy + d * L;"),
+    ("project: conv taps in convolution order", "c += (double)w[j] * ",
+     "c += (double)w[KW - 1 - j] * "),
+    ("project: conv one step late", "const int64_t tau = t - (KW - 1) + j;",
+     "const int64_t tau = t - KW + j;"),
+    ("project: conv bias shared by routes", "double c = conv_b[(int64_t)k * D + d];",
+     "double c = conv_b[d];"),
+    ("project: conv taps shared by channels", "conv_w + ((int64_t)k * D + d) * KW;",
+     "conv_w + ((int64_t)k * D) * KW;"),
+    ("project: no SiLU", "uk[d * L + t] = silu(c);", "uk[d * L + t] = c;"),
+    ("project: conv along route 0 for every route",
+     "(double)xc[route_position(K, k, tau, H, W)];",
+     "(double)xc[route_position(K, 0, tau, H, W)];"),
+    ("project: x_proj weight read (K, D, M)", "x_proj_w[((int64_t)k * M + m) * D + d]",
+     "x_proj_w[((int64_t)k * D + d) * M + m]"),
+    ("project: dt_proj weight read (K, R, D)", "dt_proj_w[((int64_t)k * D + d) * R + r]",
+     "dt_proj_w[((int64_t)k * R + r) * D + d]"),
+    ("project: dt from the B rows", "* R + r] * xd[r];", "* R + r] * xd[R + r];"),
+    ("project: B and C swapped", "Bs[(i * N + n) * L + t] = xd[R + n];",
+     "Bs[(i * N + n) * L + t] = xd[R + N + n];"),
+    ("routes: every route reads route 0's input",
+     "u_routes + ((b * K + k) * D + d) * L : NULL;", "u_routes + ((b * K) * D + d) * L : NULL;"),
+    ("routes: input read in reverse", "const double u = uk ? uk[t] : xc[l];",
+     "const double u = uk ? uk[L - 1 - t] : xc[l];"),
 ]
 
 

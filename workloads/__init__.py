@@ -194,3 +194,42 @@ def make_output_grad(wl: Workload, seed: int = 0) -> dict:
         out["dy_bf16"] = bits
         out["dy"] = bf16_bits_to_f32(bits)
     return out
+
+
+def make_front_weights(wl: Workload, seed: int = 0, R: int = 1, KW: int = 4) -> dict:
+    """Seeded weights of the per-route front end, fp32, from a generator of their own, each
+    uniform in (-1/sqrt(fan_in), 1/sqrt(fan_in)) (the default initialisation of the conv and
+    linear layers the pages' listings build without an initialiser of their own):
+      conv_w    (K, D, KW)      depthwise causal conv taps, fan_in = KW
+      conv_b    (K, D)          conv bias, fan_in = KW
+      x_proj_w  (K, R + 2N, D)  x_proj rows [dt (R) | B (N) | C (N)], fan_in = D
+      dt_proj_w (K, D, R)       dt_proj weight, fan_in = R
+    R = 1 and KW = 4 are the explainer's SelectiveSSM sizes (x_proj to 2N + 1 outputs,
+    dt_proj from 1 input, d_conv = 4)."""
+    rng = np.random.default_rng([seed, 0xf0])
+    K, D, N = wl.K, wl.D, wl.N
+
+    def unif(shape, fan_in):
+        bound = 1.0 / np.sqrt(fan_in)
+        return rng.uniform(-bound, bound, size=shape).astype(np.float32)
+
+    conv_w = unif((K, D, KW), KW)
+    conv_b = unif((K, D), KW)
+    x_proj_w = unif((K, R + 2 * N, D), D)
+    dt_proj_w = unif((K, D, R), R)
+    return dict(conv_w=conv_w, conv_b=conv_b, x_proj_w=x_proj_w, dt_proj_w=dt_proj_w)
+
+
+def make_route_inputs(wl: Workload, seed: int = 0) -> dict:
+    """Seeded per-route input u (B, K, D, L) for the operator whose routes each bring their
+    own input (scan order of each route, time innermost): standard normal, from a generator
+    of its own.  Returns u (fp32, bf16-exact for bf16 workloads) and, for bf16 workloads, its
+    bit patterns under u_bf16."""
+    rng = np.random.default_rng([seed, 0x0e])
+    u = rng.standard_normal((wl.B, wl.K, wl.D, wl.L), dtype=np.float32)
+    out = dict(u=u)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(u)
+        out["u_bf16"] = bits
+        out["u"] = bf16_bits_to_f32(bits)
+    return out
