@@ -113,6 +113,37 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
                       f"{wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
 
 
+def cpu_baseline_front(wl, inp, w, target_s: float, z=None, zoh=False) -> dict:
+    """The float64 oracle's per-route front end followed by its operator over per-route
+    inputs, as they are, on all host cores, over a bounded sample of whole images."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.Oracle()
+    cores = len(os.sched_getaffinity(0))
+    front = [w[k] for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")]
+
+    def run(n):
+        t0 = time.perf_counter()
+        pr = orc.project(wl.K, inp["x"][:n], *front, threads=cores)
+        f32 = {k: v.astype(np.float32) for k, v in pr.items()}
+        orc.forward_routes(wl.K, f32["u"], f32["dt_raw"], inp["A_log"], f32["Bs"], f32["Cs"],
+                           inp["Ds"], inp["dt_bias"], wl.H, wl.W, threads=cores,
+                           z=None if z is None else z[:n], zoh=zoh)
+        return time.perf_counter() - t0
+
+    n = min(wl.B, max(1, cores // 4))
+    dt = run(n)
+    if n < wl.B and dt < target_s:
+        n = int(min(wl.B, max(n, n * target_s / max(dt, 1e-3))))
+        dt = run(n)
+    upd = n * wl.K * wl.D * wl.L * wl.N
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
+            "kind": "oracle",
+            "sample": f"front end + scan of {n} of {wl.B} images of {wl.name} (all {wl.K} "
+                      f"routes and {wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
+
+
 def cpu_baseline(wl, inp, target_s: float, z=None, zoh=False) -> dict:
     """The float64 oracle, as it is, on all host cores, over a bounded sample of channels."""
     import numpy as np
@@ -159,6 +190,13 @@ def main() -> int:
                     help="zero-order-hold discretisation of B")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward entry point (gradients of sum(dy * y))")
+    ap.add_argument("--front", action="store_true",
+                    help="per-route front end: time ss2d_project (causal conv + SiLU, x_proj, "
+                         "dt_proj) followed by ss2d_forward_routes on its outputs")
+    ap.add_argument("--front-r", type=int, default=1, metavar="R",
+                    help="dt rank R of the front end (x_proj rows R + 2N)")
+    ap.add_argument("--front-kw", type=int, default=4, metavar="KW",
+                    help="conv length of the front end")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 device-to-device copies of MIB "
                          "MiB (a plain copy kernel of known size, for scaling the HBM byte "
@@ -206,10 +244,27 @@ def main() -> int:
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    if args.backward and (args.gate or args.zoh):
+    if args.backward and (args.gate or args.zoh or args.front):
         log("the backward entry point covers the plain operator only")
         return 2
-    if args.backward:
+    z = None
+    if gate is not None:
+        z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
+             if wl.dtype == "bf16" else torch.from_numpy(gate["z"])).to("cuda:0")
+    front_w = None
+    if args.front:
+        front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw)
+        fw = [torch.from_numpy(front_w[k]).to("cuda:0")
+              for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")]
+        proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
+        fwd = ss.ss2d_forward_routes if wl.K == 4 else ss.ss1d_bidir_forward_routes
+        hw = (wl.H, wl.W) if wl.K == 4 else ()
+
+        def call():
+            o = proj(dev["x"], *fw)
+            return fwd(o["u"], o["dt_raw"], dev["A_log"], o["Bs"], o["Cs"], dev["Ds"],
+                       dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
+    elif args.backward:
         g = workloads.make_output_grad(wl, 0)
         dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
               if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
@@ -217,10 +272,6 @@ def main() -> int:
         call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
     elif args.gate or args.zoh:
         fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
-        z = None
-        if gate is not None:
-            z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
-                 if wl.dtype == "bf16" else torch.from_numpy(gate["z"])).to("cuda:0")
         call = lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)  # noqa: E731
     else:
         fn = ss.ss2d_forward if wl.K == 4 else ss.ss1d_bidir_forward
@@ -248,6 +299,14 @@ def main() -> int:
     ms_step = ms_total / args.steps
     upd_per_s = wl.updates / (ms_step / 1e3)
     alg_bytes = wl.algorithmic_bytes() + (wl.elem_bytes * wl.B * wl.D * wl.L if args.gate else 0)
+    e, M = wl.elem_bytes, args.front_r + 2 * wl.N
+    # front end, per launch: x read once; u and dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L)
+    # written once; the fp32 weights read once
+    proj_bytes = (e * (wl.B * wl.D * wl.L + 2 * wl.B * wl.K * wl.D * wl.L
+                       + 2 * wl.B * wl.K * wl.N * wl.L)
+                  + 4 * wl.K * wl.D * (args.front_kw + 1 + M + args.front_r))
+    if args.front:  # the scan then reads u (B, K, D, L) in place of x (B, D, L)
+        alg_bytes += proj_bytes + e * (wl.K - 1) * wl.B * wl.D * wl.L
     gbps = alg_bytes / (ms_step / 1e3) / 1e9
     for name, (ms, n) in kernels.items():
         if n:
@@ -270,16 +329,32 @@ def main() -> int:
     roofline = {"bound": "alu", "achieved": round(achieved, 3),
                 "peak": round(peak, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
-                "traffic": traffic if not (args.gate or args.zoh or args.backward) else None,
+                "traffic": (traffic if not (args.gate or args.zoh or args.backward
+                                            or args.front) else None),
                 "kernel": "k_scan_bwd" if args.backward else "k_scan",
                 "kernel_avg_us": round(scan_avg_s * 1e6, 1),
                 "frac_of_fma_peak": round(achieved / FMA_PEAK_TFLOPS, 4),
                 "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
 
+    roofline_front = None
+    if args.front:
+        p_ms, p_n = kernels["project"]
+        p_avg_s = p_ms / max(p_n, 1) / 1e3
+        p_gbps = proj_bytes / p_avg_s / 1e9
+        roofline_front = {"bound": "hbm", "achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(p_gbps / HBM_PEAK_GBPS, 4),
+                          "traffic": None, "kernel": "k_project",
+                          "kernel_avg_us": round(p_avg_s * 1e6, 1),
+                          "algorithmic_bytes_per_launch": proj_bytes,
+                          "R": args.front_r, "KW": args.front_kw}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        if args.backward:
+        if args.front:
+            cpu = cpu_baseline_front(wl, inp, front_w, args.cpu_seconds,
+                                     z=gate["z"] if gate else None, zoh=args.zoh)
+        elif args.backward:
             cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds)
         else:
             cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
@@ -302,13 +377,17 @@ def main() -> int:
         "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "H": wl.H, "W": wl.W,
                    "L": wl.L, "N": wl.N, "K": wl.K, "io_dtype": wl.dtype,
                    "state_dtype": "f32", "A_log": args.a_log, "gate": bool(args.gate),
-                   "zoh": bool(args.zoh), "pass": "backward" if args.backward else "forward"},
+                   "zoh": bool(args.zoh),
+                   "pass": ("backward" if args.backward else
+                            "front+forward" if args.front else "forward")},
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kernels.items() if n},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if roofline_front is not None:
+        out["roofline_front"] = roofline_front
     print(json.dumps(out), flush=True)
     return 0
 

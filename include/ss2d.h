@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 3
+#define SS2D_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -76,10 +76,11 @@ extern "C" {
 #define SS2D_ERR_SHAPE 2       /* a negative dimension, H/W/L/N < 1, or a size beyond the
                                   kernels' index range (L >= 2^30, or any tensor with
                                   2^62 elements or more)                                   */
-#define SS2D_ERR_UNSUPPORTED 3 /* N not in {1, 2, 4, 8, 16, 32}, or an unknown dtype        */
+#define SS2D_ERR_UNSUPPORTED 3 /* N not in {1, 2, 4, 8, 16, 32}, an unknown dtype or flag, or
+                                  a size an entry point documents as unsupported          */
 #define SS2D_ERR_ALIGN 4       /* a pointer not aligned to its element size                 */
 #define SS2D_ERR_HIP 5         /* a HIP runtime call failed (see ss2d_last_hip_error)       */
-#define SS2D_ERR_ALIAS 6       /* y overlaps an input                                        */
+#define SS2D_ERR_ALIAS 6       /* an output overlaps an input (or another output)            */
 
 /* Data types of x, dt_raw, Bs, Cs and y. */
 #define SS2D_F32 0
@@ -160,6 +161,61 @@ int ss1d_bidir_backward(const void *x, const void *dt_raw, const float *A_log,
                         float *dA_log, void *dBs, void *dCs, float *dDs, float *ddt_bias,
                         int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void *stream);
 
+/* ---- per-route front end and the operator over per-route inputs ---------------------------
+ * In the pages' per-direction modules every scan direction carries its own input layers: the
+ * explainer's CrossScanModule holds one SelectiveSSM per direction (a depthwise Conv1d with
+ * kernel d_conv and padding d_conv - 1 cut to the first L outputs, a SiLU, x_proj to
+ * [dt, B, C] and dt_proj), and in the Vim block (Vim summary, section 4.3) each path runs a
+ * Conv1d and a SiLU on its own copy of the sequence and generates delta, B and C from the
+ * activated output, which is also the input of that path's scan.
+ *
+ * ss2d_project computes, for every route k and image b, from the shared input x (B, D, H, W)
+ * [ss1d_bidir_project: (B, D, L), routes forward and reversed], with s_t = x[b, d, pi_k(t)]
+ * and s_t = 0 for t < 0:
+ *   u[b,k,d,t]      = SiLU(conv_b[k,d] + sum_{j<KW} conv_w[k,d,j] * s_{t-KW+1+j})
+ *   xd[m,t]         = sum_d x_proj_w[k,m,d] * u[b,k,d,t]        m < R + 2N (no bias)
+ *   dt_raw[b,k,d,t] = sum_{r<R} dt_proj_w[k,d,r] * xd[r,t]      (dt_proj's bias is dt_bias,
+ *                                                               added inside the softplus)
+ *   Bs[b,k,n,t]     = xd[R+n,t],   Cs[b,k,n,t] = xd[R+N+n,t]
+ * i.e. a causal conv along each route (route 1 is causal in reversed raster order, routes 2
+ * and 3 along columns), x_proj's output split [dt (R) | B (N) | C (N)].  Outputs, in the
+ * scan order of each route, are exactly the inputs of ss2d_forward_routes:
+ *   u, dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L) in dtype;
+ *   weights conv_w (K, D, KW), conv_b (K, D), x_proj_w (K, R + 2N, D), dt_proj_w (K, D, R):
+ *   fp32, read only.
+ * Supported: 1 <= KW <= 8, R >= 1, R + 2N <= 96 (else SS2D_ERR_UNSUPPORTED).  Every output is
+ * written in full and must overlap neither an input nor another output (SS2D_ERR_ALIAS).
+ * The conv and dt_proj are computed in fp32; x_proj accumulates in fp32 on the matrix cores
+ * from u as stored (for bf16, the stored bf16 u, with each fp32 weight split into two bf16
+ * parts whose sum carries 16 significant bits).  Scratch: a transposed copy of x for the
+ * column routes (stream-ordered, as in ss2d_forward).
+ *
+ * ss2d_forward_routes is ss2d_forward_ex with each route's own input u (B, K, D, L), in scan
+ * order, in place of the gathered x: step t of route k reads u[b,k,d,t] for both the update
+ * (delta * B * u) and the skip term (Ds * u); outputs are added at the visited positions in
+ * route order, optionally gated by z (B, D, H, W), with flags as in ss2d_forward_ex.
+ * Every other argument, error and convention is that of ss2d_forward_ex. */
+int ss2d_project(const void *x, const float *conv_w, const float *conv_b,
+                 const float *x_proj_w, const float *dt_proj_w, void *u, void *dt_raw, void *Bs,
+                 void *Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+                 int64_t KW, int dtype, void *stream);
+
+int ss1d_bidir_project(const void *x, const float *conv_w, const float *conv_b,
+                       const float *x_proj_w, const float *dt_proj_w, void *u, void *dt_raw,
+                       void *Bs, void *Cs, int64_t B, int64_t D, int64_t L, int64_t N,
+                       int64_t R, int64_t KW, int dtype, void *stream);
+
+int ss2d_forward_routes(const void *u, const void *dt_raw, const float *A_log, const void *Bs,
+                        const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                        void *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                        int dtype, int flags, void *stream);
+
+int ss1d_bidir_forward_routes(const void *u, const void *dt_raw, const float *A_log,
+                              const void *Bs, const void *Cs, const float *Ds,
+                              const float *dt_bias, const void *z, void *y, int64_t B,
+                              int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                              void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *ss2d_status_string(int status);
 
@@ -184,7 +240,8 @@ int ss2d_last_hip_error(void);
 #define SS2D_KERNEL_CHECKPOINT 5 /* backward: forward pass storing states every 32 steps */
 #define SS2D_KERNEL_SCAN_BWD 6  /* backward: adjoint scan                               */
 #define SS2D_KERNEL_REDUCE 7    /* backward: sums over channel blocks and images         */
-#define SS2D_KERNEL_KINDS 8
+#define SS2D_KERNEL_PROJECT 8   /* per-route front end: conv + SiLU, x_proj, dt_proj      */
+#define SS2D_KERNEL_KINDS 9
 int ss2d_timing_enable(int enable);
 int ss2d_timing_read(double *ms, int64_t *launches);
 

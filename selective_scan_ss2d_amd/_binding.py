@@ -35,6 +35,11 @@ SIGNATURES = {
     "ss1d_bidir_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 5 + [ctypes.c_int, _P]),
     "ss1d_bidir_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 4 + [ctypes.c_int, _P]),
+    "ss2d_project": (ctypes.c_int, [_P] * 9 + [_I64] * 7 + [ctypes.c_int, _P]),
+    "ss1d_bidir_project": (ctypes.c_int, [_P] * 9 + [_I64] * 6 + [ctypes.c_int, _P]),
+    "ss2d_forward_routes": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_forward_routes": (ctypes.c_int,
+                                  [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -43,7 +48,7 @@ SIGNATURES = {
                                         ctypes.POINTER(ctypes.c_int64)]),
 }
 KERNEL_KINDS = ("transpose", "scan", "chunk_agg", "carry", "merge", "checkpoint", "scan_bwd",
-                "reduce")
+                "reduce", "project")
 
 
 class SS2DError(RuntimeError):
@@ -239,6 +244,108 @@ def ss1d_bidir_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=Fal
                                        _stream_handle(x.device, stream))
     _check(status)
     return y
+
+
+def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream, xshape):
+    torch = _torch()
+    lib = load_library()
+    if u.device.type != "cuda":
+        raise ValueError("u must be a GPU tensor")
+    B, D, L = xshape[0], xshape[1], u.shape[-1]
+    N = A_log.shape[-1] if A_log.dim() == 3 else -1
+    dt, dev = u.dtype, u.device
+    _dtype_code(u)
+    _expect("u", u, (B, K, D, L), dt, dev)
+    _expect("dt_raw", dt_raw, (B, K, D, L), dt, dev)
+    _expect("A_log", A_log, (K, D, N), torch.float32, dev)
+    _expect("Bs", Bs, (B, K, N, L), dt, dev)
+    _expect("Cs", Cs, (B, K, N, L), dt, dev)
+    _expect("Ds", Ds, (K, D), torch.float32, dev)
+    _expect("dt_bias", dt_bias, (K, D), torch.float32, dev)
+    if y is None:
+        y = torch.empty(xshape, dtype=dt, device=dev)
+    else:
+        _expect("y", y, xshape, dt, dev)
+    zp = _gate_ptr(z, xshape, u)
+    fn = lib.ss2d_forward_routes if K == 4 else lib.ss1d_bidir_forward_routes
+    status = fn(u.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(), Bs.data_ptr(),
+                Cs.data_ptr(), Ds.data_ptr(), dt_bias.data_ptr(), zp, y.data_ptr(),
+                *xshape[:2], *xshape[2:], N, _dtype_code(u), SS2D_FLAG_ZOH if zoh else 0,
+                _stream_handle(dev, stream))
+    _check(status)
+    return y
+
+
+def ss2d_forward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, H, W, z=None, zoh=False,
+                        y=None, stream=None):
+    """ss2d_forward_ex with each route's own input u (B, 4, D, L), in scan order, in place of
+    the gathered x.  Returns y (B, D, H, W)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 4, D, L)")
+    if u.shape[-1] != H * W:
+        raise ValueError(f"u has {u.shape[-1]} steps, expected H * W = {H * W}")
+    return _routes_forward(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (u.shape[0], u.shape[2], H, W))
+
+
+def ss1d_bidir_forward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False,
+                              y=None, stream=None):
+    """ss1d_bidir_forward_ex with each path's own input u (B, 2, D, L).  Returns y (B, D, L)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 2, D, L)")
+    return _routes_forward(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (u.shape[0], u.shape[2], u.shape[3]))
+
+
+def _project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, xshape):
+    torch = _torch()
+    lib = load_library()
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    B, D = xshape[0], xshape[1]
+    L = 1
+    for v in xshape[2:]:
+        L *= v
+    dt, dev = x.dtype, x.device
+    _dtype_code(x)
+    if conv_w.dim() != 3 or dt_proj_w.dim() != 3 or x_proj_w.dim() != 3:
+        raise ValueError("conv_w, x_proj_w and dt_proj_w must be 3-D")
+    KW, R, M = conv_w.shape[-1], dt_proj_w.shape[-1], x_proj_w.shape[1]
+    N = (M - R) // 2
+    if N < 1 or M != R + 2 * N:
+        raise ValueError(f"x_proj_w has {M} rows, expected R + 2N with R = {R}")
+    _expect("x", x, xshape, dt, dev)
+    _expect("conv_w", conv_w, (K, D, KW), torch.float32, dev)
+    _expect("conv_b", conv_b, (K, D), torch.float32, dev)
+    _expect("x_proj_w", x_proj_w, (K, M, D), torch.float32, dev)
+    _expect("dt_proj_w", dt_proj_w, (K, D, R), torch.float32, dev)
+    out = dict(u=torch.empty((B, K, D, L), dtype=dt, device=dev),
+               dt_raw=torch.empty((B, K, D, L), dtype=dt, device=dev),
+               Bs=torch.empty((B, K, N, L), dtype=dt, device=dev),
+               Cs=torch.empty((B, K, N, L), dtype=dt, device=dev))
+    fn = lib.ss2d_project if K == 4 else lib.ss1d_bidir_project
+    status = fn(x.data_ptr(), conv_w.data_ptr(), conv_b.data_ptr(), x_proj_w.data_ptr(),
+                dt_proj_w.data_ptr(), *[out[k].data_ptr() for k in ("u", "dt_raw", "Bs", "Cs")],
+                *xshape, N, R, KW, _dtype_code(x), _stream_handle(dev, stream))
+    _check(status)
+    return out
+
+
+def ss2d_project(x, conv_w, conv_b, x_proj_w, dt_proj_w, stream=None):
+    """Per-route front end on the GPU: causal depthwise conv + SiLU, x_proj and dt_proj of
+    each of the four routes.  x (B, D, H, W) float32 or bfloat16; conv_w (4, D, KW),
+    conv_b (4, D), x_proj_w (4, R + 2N, D), dt_proj_w (4, D, R) fp32.  Returns a dict of
+    u, dt_raw (B, 4, D, L) and Bs, Cs (B, 4, N, L) in each route's scan order, dtype of x."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    return _project(4, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, tuple(x.shape))
+
+
+def ss1d_bidir_project(x, conv_w, conv_b, x_proj_w, dt_proj_w, stream=None):
+    """ss2d_project for the two paths (forward, reversed) of a 1D sequence x (B, D, L)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    return _project(2, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, tuple(x.shape))
 
 
 GRAD_NAMES = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")

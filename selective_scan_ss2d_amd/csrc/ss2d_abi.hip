@@ -115,7 +115,7 @@ struct Plan {
 // chains them, and a second pass rescans each chunk from its true start state, so chunking
 // roughly doubles the work and is used only for short, long-sequence batches.
 Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
-               const void* x, const void* dt_raw) {
+               const void* x, const void* dt_raw, bool routes) {
   Plan p;
   const int64_t L = H * W;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
@@ -150,7 +150,7 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
   const int vec_elems = dtype == SS2D_F32 ? 4 : 8;
   p.vec = (L % vec_elems == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
           (reinterpret_cast<uintptr_t>(dt_raw) % 16 == 0);
-  p.need_xt = (K == 4) && H > 1 && W > 1;
+  p.need_xt = !routes && (K == 4) && H > 1 && W > 1;
   size_t off = 0;
   if (p.need_xt) {
     p.off_xt = off;
@@ -191,8 +191,9 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
     const int64_t nb = (B - b0 < max_b) ? (B - b0) : max_b;
     ss2d::ScanArgs s = a;
     s.B = static_cast<int>(nb);
-    s.x_row = static_cast<const char*>(a.x_row) + b0 * D * L * e;
-    s.x_col = static_cast<const char*>(a.x_col) + b0 * D * L * e;
+    const int64_t x_per_b = (a.x_routes ? K : 1) * D * L * e;  // per-route inputs: (B, K, D, L)
+    s.x_row = static_cast<const char*>(a.x_row) + b0 * x_per_b;
+    s.x_col = static_cast<const char*>(a.x_col) + b0 * x_per_b;
     s.dt_raw = static_cast<const char*>(a.dt_raw) + b0 * K * D * L * e;
     s.Bs = static_cast<const char*>(a.Bs) + b0 * K * N * L * e;
     s.Cs = static_cast<const char*>(a.Cs) + b0 * K * N * L * e;
@@ -209,10 +210,11 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
   return SS2D_OK;
 }
 
-int forward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
-            const void* Cs, const float* Ds, const float* dt_bias, const void* z, void* y,
-            int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
-            void* stream) {
+// routes: x is every route's own input u (B, K, D, L) in scan order instead of the image x.
+int forward(int K, bool routes, const void* x, const void* dt_raw, const float* A_log,
+            const void* Bs, const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+            void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+            int flags, void* stream) {
   // ---- validation (nothing is enqueued before all of it passes) -------------------------
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
@@ -235,7 +237,8 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
                           static_cast<const void*>(dt_bias)})
     if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
   const int64_t y_bytes = n_x * e;
-  if (overlaps(y, y_bytes, x, n_x * e) || overlaps(y, y_bytes, dt_raw, n_dt * e) ||
+  if (overlaps(y, y_bytes, x, (routes ? n_dt : n_x) * e) ||
+      overlaps(y, y_bytes, dt_raw, n_dt * e) ||
       overlaps(y, y_bytes, Bs, n_bc * e) || overlaps(y, y_bytes, Cs, n_bc * e) ||
       overlaps(y, y_bytes, A_log, int64_t(K) * D * N * 4) ||
       overlaps(y, y_bytes, Ds, int64_t(K) * D * 4) ||
@@ -250,7 +253,7 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   if (he != hipSuccess) return hip_fail(he);
   int rc = prepare_pool(device);
   if (rc != SS2D_OK) return rc;
-  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, dt_raw);
+  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, dt_raw, routes);
   char* ws = nullptr;
   he = hipMallocAsync(reinterpret_cast<void**>(&ws), p.bytes, st);
   if (he != hipSuccess) return hip_fail(he);
@@ -273,6 +276,7 @@ int forward(int K, const void* x, const void* dt_raw, const float* A_log, const 
   a.num_chunks = p.num_chunks;
   a.chunk_len = p.chunk_len;
   a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
+  a.x_routes = routes ? 1 : 0;
 
   int err = 0;
   if (p.need_xt)
@@ -493,6 +497,94 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   return SS2D_OK;
 }
 
+// ---- per-route front end -----------------------------------------------------------------
+int project(int K, const void* x, const float* conv_w, const float* conv_b,
+            const float* x_proj_w, const float* dt_proj_w, void* u, void* dt_raw, void* Bs,
+            void* Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+            int64_t KW, int dtype, void* stream) {
+  if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
+  if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1 || R < 1 || KW < 1) return SS2D_ERR_SHAPE;
+  if (KW > ss2d::kProjMaxKW || R + 2 * N > ss2d::kProjMaxM) return SS2D_ERR_UNSUPPORTED;
+  if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
+  if ((R + 2 * N) * D * 4 >= (int64_t(1) << 32)) return SS2D_ERR_SHAPE;  // 32-bit offsets
+  const int64_t L = H * W;
+  if (D >= (int64_t(1) << 31) / 4 || B >= (int64_t(1) << 31)) return SS2D_ERR_SHAPE;
+  int64_t n_x, n_dt, n_bc, tmp;
+  if (!mul_ok(B, D, &tmp) || !mul_ok(tmp, L, &n_x)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
+  if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
+  if (B == 0 || D == 0) return SS2D_OK;
+  const void* ins[] = {x, conv_w, conv_b, x_proj_w, dt_proj_w};
+  const void* outs[] = {u, dt_raw, Bs, Cs};
+  for (const void* ptr : ins)
+    if (!ptr) return SS2D_ERR_NULL;
+  for (const void* ptr : outs)
+    if (!ptr) return SS2D_ERR_NULL;
+  const int64_t e = dtype == SS2D_F32 ? 4 : 2;
+  const uintptr_t emask = static_cast<uintptr_t>(e - 1);
+  for (const void* ptr : {x, static_cast<const void*>(u), static_cast<const void*>(dt_raw),
+                          static_cast<const void*>(Bs), static_cast<const void*>(Cs)})
+    if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
+  for (const void* ptr : {static_cast<const void*>(conv_w), static_cast<const void*>(conv_b),
+                          static_cast<const void*>(x_proj_w),
+                          static_cast<const void*>(dt_proj_w)})
+    if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
+  const int64_t in_bytes[] = {n_x * e, int64_t(K) * D * KW * 4, int64_t(K) * D * 4,
+                              int64_t(K) * (R + 2 * N) * D * 4, int64_t(K) * D * R * 4};
+  const int64_t out_bytes[] = {n_dt * e, n_dt * e, n_bc * e, n_bc * e};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SS2D_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SS2D_ERR_ALIAS;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool need_t = (K == 4) && H > 1 && W > 1;
+  char* ws = nullptr;
+  if (need_t) {
+    int device = 0;
+    hipError_t he = hipGetDevice(&device);
+    if (he != hipSuccess) return hip_fail(he);
+    const int rc = prepare_pool(device);
+    if (rc != SS2D_OK) return rc;
+    he = hipMallocAsync(reinterpret_cast<void**>(&ws), size_t(n_x * e), st);
+    if (he != hipSuccess) return hip_fail(he);
+  }
+  int err = 0;
+  if (need_t)
+    err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
+      return ss2d::launch_transpose(x, ws, int(B), int(D), int(H), int(W), dtype, st);
+    });
+  for (int64_t b0 = 0; !err && b0 < B; b0 += kMaxGridZ) {
+    const int64_t nb = (B - b0 < kMaxGridZ) ? (B - b0) : kMaxGridZ;
+    ss2d::ProjArgs a{};
+    a.x_row = static_cast<const char*>(x) + b0 * D * L * e;
+    a.x_col = need_t ? static_cast<const void*>(ws + b0 * D * L * e) : a.x_row;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.x_proj_w = x_proj_w;
+    a.dt_proj_w = dt_proj_w;
+    a.u = static_cast<char*>(u) + b0 * K * D * L * e;
+    a.dt_raw = static_cast<char*>(dt_raw) + b0 * K * D * L * e;
+    a.Bs = static_cast<char*>(Bs) + b0 * K * N * L * e;
+    a.Cs = static_cast<char*>(Cs) + b0 * K * N * L * e;
+    a.B = int(nb);
+    a.K = K;
+    a.D = int(D);
+    a.L = int(L);
+    a.N = int(N);
+    a.R = int(R);
+    a.KW = int(KW);
+    err = timed(SS2D_KERNEL_PROJECT, st, [&] { return ss2d::launch_project(a, dtype, st); });
+  }
+  hipError_t fe = hipSuccess;
+  if (ws) fe = hipFreeAsync(ws, st);
+  if (err) return hip_fail(static_cast<hipError_t>(err));
+  if (fe != hipSuccess) return hip_fail(fe);
+  return SS2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -500,14 +592,14 @@ extern "C" {
 int ss2d_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
                  const void* Cs, const float* Ds, const float* dt_bias, void* y, int64_t B,
                  int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
-  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, H, W, N, dtype, 0,
+  return forward(4, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, H, W, N, dtype, 0,
                  stream);
 }
 
 int ss1d_bidir_forward(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
                        const void* Cs, const float* Ds, const float* dt_bias, void* y,
                        int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
-  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, 1, L, N, dtype, 0,
+  return forward(2, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, nullptr, y, B, D, 1, L, N, dtype, 0,
                  stream);
 }
 
@@ -515,7 +607,7 @@ int ss2d_forward_ex(const void* x, const void* dt_raw, const float* A_log, const
                     const void* Cs, const float* Ds, const float* dt_bias, const void* z,
                     void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                     int flags, void* stream) {
-  return forward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype, flags,
+  return forward(4, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype, flags,
                  stream);
 }
 
@@ -523,7 +615,7 @@ int ss1d_bidir_forward_ex(const void* x, const void* dt_raw, const float* A_log,
                           const void* Bs, const void* Cs, const float* Ds,
                           const float* dt_bias, const void* z, void* y, int64_t B, int64_t D,
                           int64_t L, int64_t N, int dtype, int flags, void* stream) {
-  return forward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype, flags,
+  return forward(2, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype, flags,
                  stream);
 }
 
@@ -543,6 +635,39 @@ int ss1d_bidir_backward(const void* x, const void* dt_raw, const float* A_log,
                         int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
   return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream);
+}
+
+int ss2d_project(const void* x, const float* conv_w, const float* conv_b,
+                 const float* x_proj_w, const float* dt_proj_w, void* u, void* dt_raw, void* Bs,
+                 void* Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+                 int64_t KW, int dtype, void* stream) {
+  return project(4, x, conv_w, conv_b, x_proj_w, dt_proj_w, u, dt_raw, Bs, Cs, B, D, H, W, N,
+                 R, KW, dtype, stream);
+}
+
+int ss1d_bidir_project(const void* x, const float* conv_w, const float* conv_b,
+                       const float* x_proj_w, const float* dt_proj_w, void* u, void* dt_raw,
+                       void* Bs, void* Cs, int64_t B, int64_t D, int64_t L, int64_t N,
+                       int64_t R, int64_t KW, int dtype, void* stream) {
+  return project(2, x, conv_w, conv_b, x_proj_w, dt_proj_w, u, dt_raw, Bs, Cs, B, D, 1, L, N,
+                 R, KW, dtype, stream);
+}
+
+int ss2d_forward_routes(const void* u, const void* dt_raw, const float* A_log, const void* Bs,
+                        const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                        void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                        int dtype, int flags, void* stream) {
+  return forward(4, true, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype,
+                 flags, stream);
+}
+
+int ss1d_bidir_forward_routes(const void* u, const void* dt_raw, const float* A_log,
+                              const void* Bs, const void* Cs, const float* Ds,
+                              const float* dt_bias, const void* z, void* y, int64_t B,
+                              int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                              void* stream) {
+  return forward(2, true, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype,
+                 flags, stream);
 }
 
 const char* ss2d_status_string(int status) {

@@ -115,7 +115,8 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // ---- launch arguments ------------------------------------------------------------------
 struct ScanArgs {
-  const void* x_row;      // route source for routes 0 and 1: x, (B, D, L)
+  const void* x_row;      // route source for routes 0 and 1: x, (B, D, L); with x_routes set,
+                          // every route's own input u, (B, K, D, L) in scan order
   const void* x_col;      // route source for routes 2 and 3: x transposed per plane, (B, D, L)
   const void* dt_raw;     // (B, K, D, L)
   const void* Bs;         // (B, K, N, L)
@@ -134,6 +135,7 @@ struct ScanArgs {
   int chunks_in_launch;   // chunks covered by this launch per (b, k)
   int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
   int ck_tiles;           // kModeCkpt: 32-step tiles per sequence; h_in receives the states
+  int x_routes;           // nonzero: x_row holds each route's own input sequence
 };
 
 enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2 };
@@ -162,6 +164,23 @@ struct BwdArgs {
   int n_cb;               // channel blocks per (b, k): ceil(D / 64)
 };
 
+// Arguments of the per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj).
+struct ProjArgs {
+  const void* x_row;        // x, (B, D, L): the source of routes 0 and 1 (K = 2: both)
+  const void* x_col;        // x transposed per plane: the source of routes 2 and 3
+  const float* conv_w;      // (K, D, KW)
+  const float* conv_b;      // (K, D)
+  const float* x_proj_w;    // (K, R + 2N, D)
+  const float* dt_proj_w;   // (K, D, R)
+  void* u;                  // (B, K, D, L) conv + SiLU output, scan order
+  void* dt_raw;             // (B, K, D, L)
+  void* Bs;                 // (B, K, N, L)
+  void* Cs;                 // (B, K, N, L)
+  int B, K, D, L, N, R, KW;
+};
+constexpr int kProjMaxKW = 8;   // longest conv supported
+constexpr int kProjMaxM = 96;   // most x_proj rows (R + 2N) supported
+
 // Host-side launchers (defined in the .hip files).  The _zoh scan launchers run the
 // zero-order-hold discretisation of B (a.zoh set), the others delta * B.
 int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
@@ -185,5 +204,6 @@ int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, in
                   int dtype, hipStream_t st);
 int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L,
                   int dtype, hipStream_t st);
+int launch_project(const ProjArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ss2d

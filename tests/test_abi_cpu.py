@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 3
+    assert lib.ss2d_abi_version() == 4
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -198,6 +198,71 @@ def test_backward_argument_errors(lib):
     import torch
     if not torch.cuda.is_available():
         assert call_bwd(lib, ptrs) == bnd.SS2D_ERR_HIP
+
+
+# ---- per-route front end and the operator over per-route inputs ---------------------------
+def call_proj(lib, ptrs, B=1, D=8, H=8, W=8, N=4, R=2, KW=4, dtype=0, K=4):
+    if K == 4:
+        return lib.ss2d_project(*ptrs, B, D, H, W, N, R, KW, dtype, None)
+    return lib.ss1d_bidir_project(*ptrs, B, D, H * W, N, R, KW, dtype, None)
+
+
+def test_project_argument_errors(lib):
+    ptrs = fake_ptrs(9)
+    for K in (4, 2):
+        for i in range(9):
+            p = list(ptrs)
+            p[i] = None
+            assert call_proj(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        assert call_proj(lib, ptrs, KW=9, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_proj(lib, ptrs, R=65, N=16, K=K) == bnd.SS2D_ERR_UNSUPPORTED  # R + 2N > 96
+        assert call_proj(lib, ptrs, dtype=2, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        for bad in (dict(KW=0), dict(R=0), dict(N=0), dict(B=-1), dict(H=0)):
+            assert call_proj(lib, ptrs, K=K, **bad) == bnd.SS2D_ERR_SHAPE, bad
+        assert call_proj(lib, [None] * 9, B=0, K=K) == bnd.SS2D_OK
+        for i in range(9):
+            p = list(ptrs)
+            p[i] += 1
+            assert call_proj(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
+        for i in range(5, 9):  # an output inside an input, or inside another output
+            for j in range(0, i):
+                p = list(ptrs)
+                p[i] = p[j] + 4
+                assert call_proj(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i, j)
+    import torch
+    if not torch.cuda.is_available():
+        assert call_proj(lib, ptrs) == bnd.SS2D_ERR_HIP
+        assert call_proj(lib, ptrs, K=2, R=64, N=16) == bnd.SS2D_ERR_HIP  # R + 2N = 96
+        assert call_proj(lib, ptrs, R=64, N=12, KW=8) == bnd.SS2D_ERR_HIP  # R + 2N = 88
+
+
+def call_routes(lib, ptrs, z=None, flags=0, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4):
+    if K == 4:
+        return lib.ss2d_forward_routes(*ptrs[:7], z, ptrs[7], B, D, H, W, N, dtype, flags,
+                                       None)
+    return lib.ss1d_bidir_forward_routes(*ptrs[:7], z, ptrs[7], B, D, H * W, N, dtype, flags,
+                                         None)
+
+
+def test_forward_routes_argument_errors(lib):
+    z = (1 << 40) + 9 * (1 << 32)
+    for K in (4, 2):
+        for i in range(8):
+            p = fake_ptrs()
+            p[i] = None
+            assert call_routes(lib, p, z, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        assert call_routes(lib, fake_ptrs(), z, flags=2, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_routes(lib, fake_ptrs(), z, N=3, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        p = fake_ptrs()
+        # y must not overlap u anywhere in its K planes per image (u is K times the size
+        # of x): y placed after the first x-sized stretch of u still overlaps it
+        p[7] = p[0] + 8 * 8 * 8 * 4 + 64
+        assert call_routes(lib, p, z, K=K) == bnd.SS2D_ERR_ALIAS
+        assert call_routes(lib, fake_ptrs(), fake_ptrs()[7] + 64, K=K) == bnd.SS2D_ERR_ALIAS
+        assert call_routes(lib, [None] * 8, None, B=0, K=K) == bnd.SS2D_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call_routes(lib, fake_ptrs(), None) == bnd.SS2D_ERR_HIP
 
 
 def test_valid_call_without_gpu_reports_hip_error(lib):

@@ -1,0 +1,207 @@
+"""GPU parity of the per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj) and of
+the operator over per-route inputs against the float64 oracle, through the C ABI: small
+shapes element by element (ragged step tiles, channel counts across the 64-channel chunks,
+every conv length and x_proj width the kernel supports, both element types, both route
+sets, degenerate maps), the chain of both entry points, and sampled images at the VMamba-T
+stage-1 size."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, assert_parity, env_override, log, to_device, to_numpy_f64
+
+pytestmark = pytest.mark.gpu
+
+ARGS = ("dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+FRONT = ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")
+OUTS = ("u", "dt_raw", "Bs", "Cs")
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def _dev(a, dtype):
+    import torch
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(np.ascontiguousarray(a, np.float32))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda:0")
+
+
+def _weights_dev(w):
+    import torch
+    return {k: torch.from_numpy(np.ascontiguousarray(w[k], np.float32)).to("cuda:0")
+            for k in FRONT}
+
+
+def run_project(x_dev, wd, K):
+    import selective_scan_ss2d_amd as ss
+    fn = ss.ss2d_project if K == 4 else ss.ss1d_bidir_project
+    return fn(x_dev, *[wd[k] for k in FRONT])
+
+
+def check_project(orc, wl, R, KW, seed=0):
+    import torch
+    what = f"project B{wl.B} D{wl.D} {wl.H}x{wl.W} N{wl.N} K{wl.K} R{R} KW{KW} {wl.dtype}"
+    log(f"case {what}")
+    inp = workloads.make_inputs(wl, seed=seed)
+    w = workloads.make_front_weights(wl, seed, R=R, KW=KW)
+    ref = orc.project(wl.K, inp["x"], *[w[k] for k in FRONT])
+    got = run_project(to_device(inp, wl)["x"], _weights_dev(w), wl.K)
+    torch.cuda.synchronize()
+    for k in OUTS:
+        assert_parity(to_numpy_f64(got[k]), ref[k], wl.dtype, f"{what} {k}")
+
+
+PROJ_SHAPES = [  # B, D, H, W, N, K, dtype, R, KW
+    (1, 8, 8, 8, 4, 4, "f32", 1, 4),
+    (2, 70, 5, 27, 4, 4, "f32", 3, 4),
+    (2, 70, 5, 27, 4, 4, "bf16", 3, 4),
+    (2, 130, 9, 11, 16, 4, "bf16", 1, 4),
+    (1, 64, 7, 9, 16, 4, "f32", 6, 4),
+    (1, 40, 6, 13, 16, 4, "bf16", 64, 4),     # 96 x_proj rows: the most supported
+    (1, 40, 6, 13, 8, 4, "f32", 5, 1),         # KW = 1: a pointwise conv
+    (1, 40, 6, 13, 8, 4, "bf16", 2, 8),        # KW = 8: the longest conv
+    (1, 24, 1, 150, 4, 4, "f32", 2, 4),        # H = 1: every route along the one row
+    (1, 24, 150, 1, 4, 4, "bf16", 2, 4),       # W = 1
+    (1, 24, 1, 3, 4, 4, "f32", 2, 4),          # fewer steps than taps
+    (2, 48, 1, 197, 16, 2, "bf16", 1, 4),      # Vim paths: 196 patches + class token
+    (3, 33, 1, 65, 8, 2, "f32", 4, 3),
+]
+
+
+@pytest.mark.parametrize("case", PROJ_SHAPES,
+                         ids=lambda c: "B{}D{}_{}x{}_N{}_K{}_{}_R{}_KW{}".format(*c))
+def test_project_small(orc, case):
+    B, D, H, W, N, K, dt, R, KW = case
+    check_project(orc, workloads.custom(B, D, H, W, N, K, dt), R, KW, seed=31)
+
+
+def test_project_impulse_taps(orc):
+    """A unit impulse through the conv alone (x_proj, dt_proj zero): the reversed taps at the
+    KW steps from the one that visits the impulse, on every route."""
+    import torch
+    wl = workloads.custom(1, 64, 6, 10, 4, 4, "f32")
+    D, L = wl.D, wl.L
+    x = np.zeros((1, D, wl.H, wl.W), np.float32)
+    x[0, 5, 2, 3] = 1.0
+    x[0, 63, 0, 0] = 1.0
+    x[0, 17, 5, 9] = 1.0
+    w = workloads.make_front_weights(wl, 5, R=2, KW=4)
+    w["conv_w"] = (3.0 + np.arange(4 * D * 4, dtype=np.float32).reshape(4, D, 4) % 7)
+    ref = orc.project(4, x, *[w[k] for k in FRONT])
+    got = run_project(_dev(x, "f32"), _weights_dev(w), 4)
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(got["u"]), ref["u"], "f32", "impulse u")
+
+
+def route_inputs_to_device(ri, wl):
+    import torch
+    if wl.dtype == "bf16":
+        return torch.from_numpy(ri["u_bf16"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(ri["u"]).to("cuda:0")
+
+
+def run_routes(u_dev, dev, wl, z=None, zoh=False):
+    import selective_scan_ss2d_amd as ss
+    if wl.K == 4:
+        return ss.ss2d_forward_routes(u_dev, *[dev[k] for k in ARGS], wl.H, wl.W, z=z, zoh=zoh)
+    return ss.ss1d_bidir_forward_routes(u_dev, *[dev[k] for k in ARGS], z=z, zoh=zoh)
+
+
+def check_routes(orc, wl, gate, zoh, seed=0, **overrides):
+    import torch
+    what = (f"routes B{wl.B} D{wl.D} {wl.H}x{wl.W} N{wl.N} K{wl.K} {wl.dtype} gate={gate} "
+            f"zoh={zoh} {overrides}")
+    log(f"case {what}")
+    inp = workloads.make_inputs(wl, seed=seed, a_log="random")
+    ri = workloads.make_route_inputs(wl, seed)
+    g = workloads.make_gate(wl, seed) if gate else None
+    ref = orc.forward_routes(wl.K, ri["u"], *[inp[k] for k in ARGS], wl.H, wl.W,
+                             z=g["z"] if gate else None, zoh=zoh)
+    dev = to_device(inp, wl)
+    z = _dev(g["z"], wl.dtype) if gate else None
+    with env_override(**overrides):
+        y = run_routes(route_inputs_to_device(ri, wl), dev, wl, z=z, zoh=zoh)
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(y), ref.reshape(y.shape), wl.dtype, what)
+
+
+ROUTE_SHAPES = [  # B, D, H, W, N, K, dtype
+    (1, 8, 8, 8, 4, 4, "f32"),
+    (2, 70, 5, 7, 16, 4, "f32"),
+    (2, 70, 5, 7, 16, 4, "bf16"),
+    (2, 130, 24, 24, 16, 4, "bf16"),
+    (3, 100, 1, 197, 16, 2, "bf16"),
+    (2, 64, 1, 320, 16, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("gate,zoh", [(False, False), (True, True)], ids=["plain", "gate_zoh"])
+@pytest.mark.parametrize("case", ROUTE_SHAPES,
+                         ids=lambda c: "B{}D{}_{}x{}_N{}_K{}_{}".format(*c))
+def test_routes_small(orc, case, gate, zoh):
+    B, D, H, W, N, K, dt = case
+    check_routes(orc, workloads.custom(B, D, H, W, N, K, dt), gate, zoh, seed=32)
+
+
+@pytest.mark.parametrize("var", [dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
+                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96),
+                                 dict(SS2D_SPLIT=2, SS2D_CHUNK_LEN=0)],
+                         ids=["S1_C64", "S4_C96", "S2_C0"])
+def test_routes_launch_variants(orc, var):
+    """Chunked passes (chunk states and carries) and the lane splits on per-route inputs."""
+    check_routes(orc, workloads.custom(2, 72, 13, 11, 16, 4, "f32"), True, False, seed=33,
+                 **var)
+
+
+@pytest.mark.parametrize("K,H,W", [(4, 9, 14), (2, 1, 130)])
+def test_chain_f32(orc, K, H, W):
+    """project then forward_routes on the GPU against the same chain in the oracle (the
+    oracle's front-end outputs, as fp32, fed to its routes operator)."""
+    import torch
+    wl = workloads.custom(2, 80, H, W, 16, K, "f32")
+    log(f"case chain K={K} {H}x{W}")
+    inp = workloads.make_inputs(wl, seed=34, a_log="random")
+    w = workloads.make_front_weights(wl, 34, R=2, KW=4)
+    g = workloads.make_gate(wl, 34)
+    pr = orc.project(K, inp["x"], *[w[k] for k in FRONT])
+    ref = orc.forward_routes(K, pr["u"].astype(np.float32), pr["dt_raw"].astype(np.float32),
+                             inp["A_log"], pr["Bs"].astype(np.float32),
+                             pr["Cs"].astype(np.float32), inp["Ds"], inp["dt_bias"], H, W,
+                             z=g["z"])
+    dev = to_device(inp, wl)
+    out = run_project(dev["x"], _weights_dev(w), K)
+    dev2 = dict(dev, dt_raw=out["dt_raw"], Bs=out["Bs"], Cs=out["Cs"])
+    y = run_routes(out["u"], dev2, wl, z=_dev(g["z"], "f32"))
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(y), ref.reshape(y.shape), "f32", f"chain K={K}")
+
+
+@pytest.mark.parametrize("name,R", [("vmamba_t_stage1_bf16", 1), ("vim_bidir_bf16", 1)])
+def test_full_size_sampled_images(orc, name, R):
+    """The full benchmark shapes: both entry points at full size, checked on two images
+    against the oracle run on those images alone."""
+    import torch
+    wl = workloads.workload(name)
+    log(f"case full size {name}")
+    inp = workloads.make_inputs(wl, seed=35)
+    w = workloads.make_front_weights(wl, 35, R=R, KW=4)
+    dev = to_device(inp, wl)
+    out = run_project(dev["x"], _weights_dev(w), wl.K)
+    ri = workloads.make_route_inputs(wl, 35)
+    y = run_routes(route_inputs_to_device(ri, wl), dev, wl)
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        ref = orc.project(wl.K, inp["x"][b:b + 1], *[w[k] for k in FRONT])
+        for k in OUTS:
+            assert_parity(to_numpy_f64(out[k][b:b + 1]), ref[k], wl.dtype,
+                          f"full {name} b={b} project {k}")
+        sl = {k: inp[k][b:b + 1] for k in ("dt_raw", "Bs", "Cs")}
+        refy = orc.forward_routes(wl.K, ri["u"][b:b + 1], sl["dt_raw"], inp["A_log"], sl["Bs"],
+                                  sl["Cs"], inp["Ds"], inp["dt_bias"], wl.H, wl.W)
+        assert_parity(to_numpy_f64(y[b:b + 1]), refy.reshape(y[b:b + 1].shape), wl.dtype,
+                      f"full {name} b={b} routes")
