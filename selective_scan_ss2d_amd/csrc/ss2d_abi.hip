@@ -506,7 +506,10 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1 || R < 1 || KW < 1) return SS2D_ERR_SHAPE;
   if (KW > ss2d::kProjMaxKW || R + 2 * N > ss2d::kProjMaxM) return SS2D_ERR_UNSUPPORTED;
   if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
-  if ((R + 2 * N) * D * 4 >= (int64_t(1) << 32)) return SS2D_ERR_SHAPE;  // 32-bit offsets
+  // the kernel addresses a plane set (D rows of L elements) and the weights with 32-bit
+  // byte offsets
+  if ((R + 2 * N) * D * 4 >= (int64_t(1) << 31) || D * H * W * 4 >= (int64_t(1) << 31))
+    return SS2D_ERR_SHAPE;
   const int64_t L = H * W;
   if (D >= (int64_t(1) << 31) / 4 || B >= (int64_t(1) << 31)) return SS2D_ERR_SHAPE;
   int64_t n_x, n_dt, n_bc, tmp;
@@ -539,16 +542,21 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SS2D_ERR_ALIAS;
   }
 
+  // Scratch: the transposed copy of x for the column routes, then the prepared weight
+  // images (x_proj and conv weights in the kernel's LDS layout, per route and chunk).
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool need_t = (K == 4) && H > 1 && W > 1;
+  const size_t off_prep = need_t ? align256(size_t(n_x * e)) : 0;
+  const size_t ws_bytes =
+      off_prep + ss2d::project_prep_bytes(K, int(D), int(N), int(R), dtype);
   char* ws = nullptr;
-  if (need_t) {
+  {
     int device = 0;
     hipError_t he = hipGetDevice(&device);
     if (he != hipSuccess) return hip_fail(he);
     const int rc = prepare_pool(device);
     if (rc != SS2D_OK) return rc;
-    he = hipMallocAsync(reinterpret_cast<void**>(&ws), size_t(n_x * e), st);
+    he = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, st);
     if (he != hipSuccess) return hip_fail(he);
   }
   int err = 0;
@@ -569,6 +577,7 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
     a.dt_raw = static_cast<char*>(dt_raw) + b0 * K * D * L * e;
     a.Bs = static_cast<char*>(Bs) + b0 * K * N * L * e;
     a.Cs = static_cast<char*>(Cs) + b0 * K * N * L * e;
+    a.wprep = ws + off_prep;
     a.B = int(nb);
     a.K = K;
     a.D = int(D);
@@ -578,8 +587,7 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
     a.KW = int(KW);
     err = timed(SS2D_KERNEL_PROJECT, st, [&] { return ss2d::launch_project(a, dtype, st); });
   }
-  hipError_t fe = hipSuccess;
-  if (ws) fe = hipFreeAsync(ws, st);
+  const hipError_t fe = hipFreeAsync(ws, st);
   if (err) return hip_fail(static_cast<hipError_t>(err));
   if (fe != hipSuccess) return hip_fail(fe);
   return SS2D_OK;

@@ -176,7 +176,11 @@ struct ProjArgs {
   void* dt_raw;             // (B, K, D, L)
   void* Bs;                 // (B, K, N, L)
   void* Cs;                 // (B, K, N, L)
+  const void* wprep;        // per (k, 64-channel chunk): x_proj weights and conv taps laid
+                            // out as the kernel's LDS image, img_bytes each
   int B, K, D, L, N, R, KW;
+  int nchunks;              // ceil(D / 64)
+  int img_bytes;
 };
 constexpr int kProjMaxKW = 8;   // longest conv supported
 constexpr int kProjMaxM = 96;   // most x_proj rows (R + 2N) supported
@@ -204,6 +208,10 @@ int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, in
                   int dtype, hipStream_t st);
 int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L,
                   int dtype, hipStream_t st);
+// Bytes of the prepared weight images of one call (K * ceil(D / 64) images).
+size_t project_prep_bytes(int K, int D, int N, int R, int dtype);
+// Fills a.wprep (which must hold project_prep_bytes) from the weights, then runs the front
+// end; both on `st`.
 int launch_project(const ProjArgs& a, int dtype, hipStream_t st);
 
 }  // namespace ss2d

@@ -48,16 +48,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
 }
-template <typename T> __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r,
-                                                                uint32_t index);
-template <> __device__ __forceinline__ float buf_load<uint16_t>(__amdgpu_buffer_rsrc_t r,
-                                                                uint32_t index) {
-  return Elem<uint16_t>::to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, index * 2u, 0, 0));
-}
-template <> __device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r,
-                                                             uint32_t index) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, index * 4u, 0, 0));
-}
 // fp32 -> bf16 bits, round to nearest even, by the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -67,13 +57,15 @@ template <typename T> __device__ __forceinline__ T out_elem(float x);
 template <> __device__ __forceinline__ uint16_t out_elem<uint16_t>(float x) { return bf16_bits(x); }
 template <> __device__ __forceinline__ float out_elem<float>(float x) { return x; }
 
-// Store of element `index` (per lane) of a resource; at or past its size the store is
-// dropped, which discards the lanes past the last step and whole absent rows.
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t index, uint16_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, r, index * 2u, 0, 0);
+// Store at byte offset voff (per lane) + soff (uniform) of the resource; dropped by the
+// hardware when voff is at or past the resource's size.
+__device__ __forceinline__ void buf_store_at(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                             uint32_t soff, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
 }
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t index, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, index * 4u, 0, 0);
+__device__ __forceinline__ void buf_store_at(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                             uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
 // Element at byte offset voff (per lane) + soff (uniform) of the resource.
@@ -97,6 +89,62 @@ template <> __device__ __forceinline__ float buf_load_at<float>(__amdgpu_buffer_
 // l % 16; the same channel goes to the same operand slot on both sides.
 template <typename T> struct ProjOps;
 
+// Four consecutive elements of a row by one 8-byte (bf16) or 16-byte (fp32) buffer access;
+// `rev` reverses their order (the backward routes walk rows downwards).
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+template <typename T> struct Quad;
+template <> struct Quad<uint16_t> {
+  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff, bool rev, float (&x)[4]) {
+    const v2u p = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const float a0 = __uint_as_float(p.x << 16), a1 = __uint_as_float(p.x & 0xffff0000u);
+    const float a2 = __uint_as_float(p.y << 16), a3 = __uint_as_float(p.y & 0xffff0000u);
+    x[0] = rev ? a3 : a0;
+    x[1] = rev ? a2 : a1;
+    x[2] = rev ? a1 : a2;
+    x[3] = rev ? a0 : a3;
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, const float (&u)[4]);
+};
+template <> struct Quad<float> {
+  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff, bool rev, float (&x)[4]) {
+    const v4u p = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const float a[4] = {__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z),
+                        __uint_as_float(p.w)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = rev ? a[3 - j] : a[j];
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff, const float (&u)[4]) {
+    const v4u p = {__float_as_uint(u[0]), __float_as_uint(u[1]), __float_as_uint(u[2]),
+                   __float_as_uint(u[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(p, r, voff, soff, 0);
+  }
+};
+
+// Two fp32 values to packed bf16 high parts (returned) and low parts (lo): hi = bf16(x),
+// lo = bf16(x - hi), each pair by one v_cvt_pk_bf16_f32.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t split2(float x0, float x1, uint32_t& lo) {
+  const v2f x = {x0, x1};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
+  const v2f h = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xffff0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - h, v2bf));
+  return hb;
+}
+
+__device__ __forceinline__ void Quad<uint16_t>::store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                      uint32_t soff, const float (&u)[4]) {
+  const v2f u01 = {u[0], u[1]}, u23 = {u[2], u[3]};
+  const v2u p = {__builtin_bit_cast(uint32_t, __builtin_convertvector(u01, v2bf)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(u23, v2bf))};
+  __builtin_amdgcn_raw_buffer_store_b64(p, r, voff, soff, 0);
+}
+
 // bf16 I/O: both operands split into bf16 high and low parts (v = hi + lo to about 16
 // significant bits), three products Whi uhi + Whi ulo + Wlo uhi per k-step on
 // v_mfma_f32_16x16x32_bf16, so x_proj sees u and the weights at close to fp32 accuracy.
@@ -111,21 +159,22 @@ template <> struct ProjOps<uint16_t> {
                                               const float (&v)[4]) {
     uint32_t hi[2], lo[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t h2 = 0, l2 = 0;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float x = v[2 * j + q];
-        const uint16_t h = bf16_bits(x);
-        const uint16_t l = bf16_bits(x - Elem<uint16_t>::to_f32(h));
-        h2 |= uint32_t(h) << (16 * q);
-        l2 |= uint32_t(l) << (16 * q);
-      }
-      hi[j] = h2;
-      lo[j] = l2;
-    }
+    for (int j = 0; j < 2; ++j) hi[j] = split2(v[2 * j], v[2 * j + 1], lo[j]);
     *reinterpret_cast<uint2*>(&base[row * kRowE + col]) = make_uint2(hi[0], hi[1]);
     *reinterpret_cast<uint2*>(&base[(rows + row) * kRowE + col]) = make_uint2(lo[0], lo[1]);
+  }
+  // v[j] to column col of rows row0 + j (four steps of one channel)
+  static __device__ __forceinline__ void put_col4(E* base, int rows, int row0, int col,
+                                                  const float (&v)[4]) {
+    uint32_t lo01, lo23;
+    const uint32_t hi01 = split2(v[0], v[1], lo01), hi23 = split2(v[2], v[3], lo23);
+    const uint32_t hs[4] = {hi01 & 0xffffu, hi01 >> 16, hi23 & 0xffffu, hi23 >> 16};
+    const uint32_t ls[4] = {lo01 & 0xffffu, lo01 >> 16, lo23 & 0xffffu, lo23 >> 16};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      base[(row0 + j) * kRowE + col] = static_cast<E>(hs[j]);
+      base[(rows + row0 + j) * kRowE + col] = static_cast<E>(ls[j]);
+    }
   }
   static __device__ __forceinline__ v4f product(const E* w, int wrows, const E* u, int urows,
                                                 v4f acc) {
@@ -149,29 +198,74 @@ template <> struct ProjOps<float> {
                                               const float (&v)[4]) {
     *reinterpret_cast<float4*>(&base[row * kRowE + col]) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  static __device__ __forceinline__ void put_col4(E* base, int, int row0, int col,
+                                                  const float (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) base[(row0 + j) * kRowE + col] = v[j];
+  }
   static __device__ __forceinline__ v4f product(const E* w, int, const E* u, int, v4f acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(w[0], u[0], acc, 0, 0, 0);
   }
 };
 
-// Dynamic LDS: the u operand (kTT rows), the weight operand (MP rows, MP = R + 2N rounded
-// up to 16), then the conv taps of the chunk's channels, sCW [kDC][kCW] fp32: entry sh < 8
-// is the tap applied to the value sh steps back (w[KW - 1 - sh], 0 from sh = KW on), entry
-// 8 the bias.  After the chunk loop the x_proj outputs, sXd [MP][kTT] fp32, take the space
-// of the operands (MP * 64 * 4 bytes <= (64 + MP) * kRowE * 4 for both element types).
+// The per-chunk weight image: the weight operand (MP rows, MP = R + 2N rounded up to 16) in
+// the operand layout, then the conv taps of the chunk's channels, [kDC][kCW] fp32 (entry
+// sh < 8: the tap applied to the value sh steps back, w[KW - 1 - sh], 0 from sh = KW on;
+// entry 8: the bias), padded to a multiple of 1 KB.  k_project_prep writes one image per
+// (route, chunk) to memory; k_project copies the chunk's image to LDS with memory-to-LDS
+// loads (1 KB per wave instruction).
 constexpr int kCW = 12;  // 48-byte rows: two 16-byte reads fetch the eight taps
+template <typename T> __host__ __device__ constexpr int proj_img_bytes(int MP) {
+  return (int(sizeof(typename ProjOps<T>::E)) * ProjOps<T>::elems(MP) + 4 * kDC * kCW +
+          1023) / 1024 * 1024;
+}
+// Dynamic LDS: the u operand (kTT rows), then the weight image.  After the chunk loop the
+// x_proj outputs, sXd [MP][kTT] fp32, take the space of both (MP * 64 * 4 bytes is less).
 template <typename T> __host__ __device__ constexpr size_t proj_lds_bytes(int MP) {
-  return sizeof(typename ProjOps<T>::E) * size_t(ProjOps<T>::elems(kTT + MP)) +
-         sizeof(float) * kDC * kCW;
+  return sizeof(typename ProjOps<T>::E) * size_t(ProjOps<T>::elems(kTT)) +
+         size_t(proj_img_bytes<T>(MP));
 }
 
-// Everything a chunk of 64 channels loads from memory.
+// One block per (chunk, route): the weight image of that chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void k_project_prep(ProjArgs a) {
+  using Ops = ProjOps<T>;
+  using E = typename Ops::E;
+  const int ch = blockIdx.x, k = blockIdx.y;
+  const int D = a.D, N = a.N, R = a.R, KW = a.KW;
+  const int M = R + 2 * N, MP = 16 * ((M + 15) / 16);
+  const int d0 = ch * kDC;
+  char* img = static_cast<char*>(const_cast<void*>(a.wprep)) +
+              (int64_t(k) * a.nchunks + ch) * a.img_bytes;
+  E* w = reinterpret_cast<E*>(img);
+  const float* wx = a.x_proj_w + int64_t(k) * M * D;
+  const int plane = MP * Ops::kRowE;  // elements of one operand plane
+  for (int e = threadIdx.x; e < plane; e += blockDim.x) {
+    const int m = e / Ops::kRowE, c = e % Ops::kRowE;
+    const float v = (m < M && c < kDC && d0 + c < D) ? wx[int64_t(m) * D + d0 + c] : 0.0f;
+    if constexpr (sizeof(E) == 2) {  // high part, then low part
+      const uint16_t h = bf16_bits(v);
+      w[e] = h;
+      w[plane + e] = bf16_bits(v - Elem<uint16_t>::to_f32(h));
+    } else {
+      w[e] = v;
+    }
+  }
+  float* taps = reinterpret_cast<float*>(img + sizeof(E) * Ops::elems(MP));
+  for (int e = threadIdx.x; e < kDC * kCW; e += blockDim.x) {
+    const int c = e / kCW, j = e % kCW, d = d0 + c;
+    float v = 0.0f;
+    if (d < D && j < kProjMaxKW && j < KW) v = a.conv_w[(int64_t(k) * D + d) * KW + KW - 1 - j];
+    if (d < D && j == kProjMaxKW) v = a.conv_b[int64_t(k) * D + d];
+    taps[e] = v;
+  }
+}
+
+// Everything a chunk of 64 channels loads into registers.
 struct ProjStage {
   float v[16];       // the wave's 16 input rows at this lane's step
   float h[2];        // halos, packed: element e = i (KW - 1) + m is row i's value m + 1 steps
                      // before the tile, in lane e % 64 of h[e / 64]
-  float cw[3];       // taps and biases (kDC x kCW entries over 256 threads)
-  float wv[kMT][4];  // x_proj weight slice: row idx / 16, channels 4 (idx % 16) .. + 3
 };
 
 // KWC > 0 fixes the conv length at compile time (the common d_conv = 4); KWC = 0 reads it
@@ -193,8 +287,9 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
   const int M = R + 2 * N;
   const int MT = (M + 15) / 16, MP = 16 * MT;
   E* sU = reinterpret_cast<E*>(smem);
-  E* sW = sU + Ops::elems(kTT);
+  E* sW = sU + Ops::elems(kTT);  // the weight image: operand, then the taps
   float (*sCW)[kCW] = reinterpret_cast<float (*)[kCW]>(sW + Ops::elems(MP));
+  const int img_bytes = a.img_bytes;
   float (*sXd)[kTT] = reinterpret_cast<float (*)[kTT]>(smem);
 
   const int t0 = blockIdx.x * kTT;
@@ -204,26 +299,29 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
   const T* xplanes = static_cast<const T*>(col ? a.x_col : a.x_row) + int64_t(b) * D * L;
   const int64_t bk = int64_t(b) * a.K + k;
   T* u_out = static_cast<T*>(a.u) + bk * D * L;
-  const float* wx = a.x_proj_w + int64_t(k) * M * D;
-  const float* wc = a.conv_w + int64_t(k) * D * KW;
-  const float* bc = a.conv_b + int64_t(k) * D;
   const int n16 = lane & 15, g = lane >> 4;
 
-  // Step s of a row sits at element (rev ? L - 1 - s : s) of the row.  Row loads go through
-  // one buffer resource per row, sized 0 for rows past D: lanes past the last step and
-  // absent rows read 0 from the buffer's range check, with no select or branch that would
-  // make the compiler wait for each load before issuing the next.
-  const uint32_t xo = uint32_t(rev ? L - 1 - t : t);  // past the row when t >= L
+  // Memory goes through buffer resources over whole planes (the host keeps each plane set
+  // below 2^31 bytes): a scalar byte offset selects the row, a per-lane one the step.
+  // Step s of a row sits at element (rev ? L - 1 - s : s).  Loads read clamped, in-range
+  // addresses (the rows past D and steps past L - 1 repeat the last ones, whose values are
+  // never stored; the u of rows past D is set to 0 before it reaches the contraction), so
+  // no select or branch sits between a load and the next one and all stay in flight.
+  // Stores use an offset past the resource for lanes past the last step: the hardware
+  // drops them.
   const uint32_t row_bytes = uint32_t(L) * sizeof(T);
-  const __amdgpu_buffer_rsrc_t wx_r = make_rsrc(wx, uint32_t(M) * D * 4u);
+  const uint32_t xo = uint32_t(rev ? L - 1 - min(t, L - 1) : min(t, L - 1)) * sizeof(T);
+  const uint32_t so_t = t < L ? uint32_t(t) * sizeof(T) : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t x_r = make_rsrc(xplanes, uint32_t(D) * row_bytes);
+  const __amdgpu_buffer_rsrc_t u_r = make_rsrc(u_out, uint32_t(D) * row_bytes);
 
   auto load_stage = [&](int d0, ProjStage& st) {
     const int nrows = min(kDC, D - d0);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xplanes + int64_t(d0) * L, nrows * row_bytes);
-    const T* rp = xplanes + int64_t(d0 + wave * 16) * L;  // absent rows: size 0, no access
 #pragma unroll
-    for (int i = 0; i < 16; ++i, rp += L)
-      st.v[i] = buf_load<T>(make_rsrc(rp, wave * 16 + i < nrows ? row_bytes : 0u), xo);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t row = uint32_t(min(d0 + wave * 16 + i, D - 1));
+      st.v[i] = buf_load_at<T>(x_r, xo, row * row_bytes);
+    }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int e = 64 * p + lane;
@@ -233,28 +331,8 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
       const int sc = ok ? s : 0, cc = ok ? c : 0;
       const uint32_t off = (uint32_t(cc) * uint32_t(L) + uint32_t(rev ? L - 1 - sc : sc)) *
                            sizeof(T);
-      const float hv = buf_load_at<T>(xr, off, 0);
+      const float hv = buf_load_at<T>(x_r, off, uint32_t(d0) * row_bytes);
       st.h[p] = ok ? hv : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int idx = tid + 256 * i, c = idx / kCW, j = idx % kCW;
-      const bool row_ok = idx < kDC * kCW && c < nrows;
-      const bool is_tap = row_ok && j < kProjMaxKW && j < KW, is_bias = row_ok && j == 8;
-      // one load from a selected address (no branch): the tap, the bias, or a dummy
-      const float* src = is_tap ? wc + int64_t(d0 + c) * KW + (KW - 1 - j)
-                                : (is_bias ? bc + d0 + c : wc);
-      const float val = *src;
-      st.cw[i] = (is_tap || is_bias) ? val : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < kMT; ++i) {
-      const int idx = tid + 256 * i, m = idx / 16, c = d0 + 4 * (idx % 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float w = buf_load<float>(wx_r, uint32_t(m * D + c + j));  // m >= M reads 0
-        st.wv[i][j] = c + j < D ? w : 0.0f;
-      }
     }
   };
 
@@ -267,15 +345,15 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
     ProjStage nx;
     load_stage(d0, nx);
     __syncthreads();  // the previous chunk's products have read sW
-#pragma unroll
-    for (int i = 0; i < kMT; ++i) {
-      const int idx = tid + 256 * i;
-      if (i < MT) Ops::put4(sW, MP, idx / 16, 4 * (idx % 16), nx.wv[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < kDC * kCW) sCW[idx / kCW][idx % kCW] = nx.cw[i];
+    {
+      typedef __attribute__((address_space(3))) void lds_void;
+      const char* img = static_cast<const char*>(a.wprep) +
+                        (int64_t(k) * a.nchunks + d0 / kDC) * img_bytes;
+      for (int j = wave; j < img_bytes / 1024; j += 4)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(img + j * 1024 + lane * 16),
+                                         (lds_void*)(reinterpret_cast<char*>(sW) + j * 1024),
+                                         16, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0);  // the image and this chunk's rows have arrived
     }
     float v[16], h[2];
 #pragma unroll
@@ -285,7 +363,6 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
     __syncthreads();
 
     // ---- 2. conv + SiLU in registers, four rows at a time --------------------------------
-    T* up = u_out + int64_t(d0 + wave * 16) * L;  // this row's u; absent rows: size 0
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float uv[4];
@@ -312,8 +389,7 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
           }
         }
         uv[i4] = d < D ? silu_f32(cv) : 0.0f;
-        buf_store(make_rsrc(up, d < D ? row_bytes : 0u), uint32_t(t), out_elem<T>(uv[i4]));
-        up += L;
+        if (d < D) buf_store_at(u_r, so_t, uint32_t(d) * row_bytes, out_elem<T>(uv[i4]));
       }
       Ops::put4(sU, kTT, lane, wave * 16 + 4 * q, uv);
     }
@@ -346,40 +422,274 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
 
   // ---- 5. dt_proj (wave w: channels 16 w .. 16 w + 15 of each chunk of 64), then B, C ---
   T* dt_out = static_cast<T*>(a.dt_raw) + bk * D * L;
+  const __amdgpu_buffer_rsrc_t dt_r = make_rsrc(dt_out, uint32_t(D) * row_bytes);
   cfloat* wdt = (cfloat*)(a.dt_proj_w + int64_t(k) * D * R);
 #pragma unroll 1
   for (int d0 = wave * 16; d0 < D; d0 += kDC) {
     float dv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) dv[i] = 0.0f;
-    for (int r = 0; r < R; ++r) {
-      const float xr = sXd[r][lane];
+    if (d0 + 16 <= D) {  // whole group: weights of the 16 rows by stride-R scalar loads
+      for (int r = 0; r < R; ++r) {
+        const float xr = sXd[r][lane];
+        cfloat* w = wdt + int64_t(d0) * R + r;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        dv[i] = fmaf(wdt[int64_t(min(d0 + i, D - 1)) * R + r], xr, dv[i]);
+        for (int i = 0; i < 16; ++i) dv[i] = fmaf(w[i * R], xr, dv[i]);
+      }
+    } else {
+      for (int r = 0; r < R; ++r) {
+        const float xr = sXd[r][lane];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          dv[i] = fmaf(wdt[int64_t(min(d0 + i, D - 1)) * R + r], xr, dv[i]);
+      }
     }
-    T* dp = dt_out + int64_t(d0) * L;
 #pragma unroll
-    for (int i = 0; i < 16; ++i, dp += L)
-      buf_store(make_rsrc(dp, d0 + i < D ? row_bytes : 0u), uint32_t(t), out_elem<T>(dv[i]));
+    for (int i = 0; i < 16; ++i)
+      if (d0 + i < D) buf_store_at(dt_r, so_t, uint32_t(d0 + i) * row_bytes, out_elem<T>(dv[i]));
   }
   // B and C: wave w stores rows w, w + 4, ... of the 2N rows (B first), one step per lane
-  T* Bo = static_cast<T*>(a.Bs) + bk * N * L;
-  T* Co = static_cast<T*>(a.Cs) + bk * N * L;
+  const __amdgpu_buffer_rsrc_t b_r = make_rsrc(static_cast<T*>(a.Bs) + bk * N * L,
+                                               uint32_t(N) * row_bytes);
+  const __amdgpu_buffer_rsrc_t c_r = make_rsrc(static_cast<T*>(a.Cs) + bk * N * L,
+                                               uint32_t(N) * row_bytes);
   for (int row = wave; row < 2 * N; row += 4) {
-    T* dst = row < N ? Bo + int64_t(row) * L : Co + int64_t(row - N) * L;
-    buf_store(make_rsrc(dst, row_bytes), uint32_t(t), out_elem<T>(sXd[R + row][lane]));
+    const T v = out_elem<T>(sXd[R + row][lane]);
+    if (row < N)
+      buf_store_at(b_r, so_t, uint32_t(row) * row_bytes, v);
+    else
+      buf_store_at(c_r, so_t, uint32_t(row - N) * row_bytes, v);
+  }
+}
+
+// The same front end with four steps per lane, for KW = 4 and L a multiple of 4 (the
+// common case): a 16-lane row of a wave covers the 64 steps of one channel, so a wave holds
+// four channels per register.  Rows move with 8-byte (bf16) or 16-byte (fp32) accesses, and
+// the conv needs the three values before a lane's first step only once per four outputs:
+// three DPP row shifts (lane l takes lane l - 1's value within its 16-lane row; lane 0 of a
+// row takes the halo), then 16 FMAs for the four outputs.
+constexpr int kRowShr1 = 0x111;  // DPP row_shr:1
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
+  using Ops = ProjOps<T>;
+  using E = typename Ops::E;
+  constexpr int KS = Ops::kK;
+  constexpr int CJ = KS / 4;
+  extern __shared__ __align__(16) float smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = blockIdx.y, b = blockIdx.z;
+  const int L = a.L, D = a.D, N = a.N, R = a.R;
+  const int M = R + 2 * N;
+  const int MT = (M + 15) / 16, MP = 16 * MT;
+  E* sU = reinterpret_cast<E*>(smem);
+  E* sW = sU + Ops::elems(kTT);
+  float (*sCW)[kCW] = reinterpret_cast<float (*)[kCW]>(sW + Ops::elems(MP));
+  const int img_bytes = a.img_bytes;
+  float (*sXd)[kTT] = reinterpret_cast<float (*)[kTT]>(smem);
+
+  const int t0 = blockIdx.x * kTT;
+  const bool col = (a.K == 4) && (k >= 2);
+  const bool rev = (k & 1) != 0;
+  const T* xplanes = static_cast<const T*>(col ? a.x_col : a.x_row) + int64_t(b) * D * L;
+  const int64_t bk = int64_t(b) * a.K + k;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int sr = lane >> 4, q4 = lane & 15;  // this lane's channel of the four, step group
+  const int ts = t0 + 4 * q4;                // first of this lane's four steps
+  const bool ok4 = ts < L;                   // L % 4 == 0: all four steps exist, or none
+
+  // Offsets in bytes (the host keeps each plane set below 2^31 bytes).  Loads read clamped,
+  // in-range addresses; stores of absent steps or channels get an offset past the
+  // resource, which the hardware drops.
+  const uint32_t row_bytes = uint32_t(L) * sizeof(T);
+  const int tsc = ok4 ? ts : L - 4;
+  const uint32_t xo4 = uint32_t(rev ? L - 4 - tsc : tsc) * sizeof(T);
+  const uint32_t st4 = uint32_t(ts) * sizeof(T);
+  constexpr uint32_t kDrop = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t x_r = make_rsrc(xplanes, uint32_t(D) * row_bytes);
+  const __amdgpu_buffer_rsrc_t u_r =
+      make_rsrc(static_cast<T*>(a.u) + bk * D * L, uint32_t(D) * row_bytes);
+
+  v4f acc[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // four steps of the wave's 16 channels of a chunk (lane group G: channels 4 G .. 4 G + 3),
+  // and the three steps before the tile
+  float xv[4][4], hv[4][3];
+  auto load_rows = [&](int d0) {
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int rb = min(d0 + wave * 16 + 4 * G, D - 1);
+      const uint32_t rel = uint32_t(min(d0 + wave * 16 + 4 * G + sr, D - 1) - rb) * row_bytes;
+      const uint32_t so = uint32_t(rb) * row_bytes;
+      Quad<T>::load(x_r, rel + xo4, so, rev, xv[G]);
+#pragma unroll
+      for (int sh = 1; sh < 4; ++sh) {
+        const int s = max(t0 - sh, 0);
+        const float h = buf_load_at<T>(x_r, rel + uint32_t(rev ? L - 1 - s : s) * sizeof(T), so);
+        hv[G][sh - 1] = t0 - sh >= 0 ? h : 0.0f;
+      }
+    }
+  };
+  load_rows(0);
+
+  for (int d0 = 0; d0 < D; d0 += kDC) {
+    // ---- 1. this chunk's weight image to LDS (its rows were loaded a chunk ahead) --------
+    __syncthreads();  // the previous chunk's products have read sW
+    {
+      typedef __attribute__((address_space(3))) void lds_void;
+      const char* img = static_cast<const char*>(a.wprep) +
+                        (int64_t(k) * a.nchunks + d0 / kDC) * img_bytes;
+      for (int j = wave; j < img_bytes / 1024; j += 4)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(img + j * 1024 + lane * 16),
+                                         (lds_void*)(reinterpret_cast<char*>(sW) + j * 1024),
+                                         16, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0);  // the image and this chunk's rows have arrived
+    }
+    __syncthreads();
+    float xc[4][4], hc[4][3];
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xc[G][j] = xv[G][j];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) hc[G][j] = hv[G][j];
+    }
+    if (d0 + kDC < D) load_rows(d0 + kDC);  // before this chunk's stores
+
+    // ---- 2. conv + SiLU, four outputs per lane and group ---------------------------------
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int c = wave * 16 + 4 * G + sr, d = d0 + c;
+      const float4 w = *reinterpret_cast<const float4*>(&sCW[c][0]);  // taps by shift 0..3
+      const float bias = sCW[c][8];
+      const float* x = xc[G];
+      // the values 1, 2 and 3 steps before this lane's first step
+      const float p1 = __int_as_float(__builtin_amdgcn_update_dpp(
+          __float_as_int(hc[G][0]), __float_as_int(x[3]), kRowShr1, 0xf, 0xf, false));
+      const float p2 = __int_as_float(__builtin_amdgcn_update_dpp(
+          __float_as_int(hc[G][1]), __float_as_int(x[2]), kRowShr1, 0xf, 0xf, false));
+      const float p3 = __int_as_float(__builtin_amdgcn_update_dpp(
+          __float_as_int(hc[G][2]), __float_as_int(x[1]), kRowShr1, 0xf, 0xf, false));
+      const float cv[4] = {
+          fmaf(w.w, p3, fmaf(w.z, p2, fmaf(w.y, p1, fmaf(w.x, x[0], bias)))),
+          fmaf(w.w, p2, fmaf(w.z, p1, fmaf(w.y, x[0], fmaf(w.x, x[1], bias)))),
+          fmaf(w.w, p1, fmaf(w.z, x[0], fmaf(w.y, x[1], fmaf(w.x, x[2], bias)))),
+          fmaf(w.w, x[0], fmaf(w.z, x[1], fmaf(w.y, x[2], fmaf(w.x, x[3], bias))))};
+      float u[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[j] = d < D ? silu_f32(cv[j]) : 0.0f;
+      const int rb = min(d0 + wave * 16 + 4 * G, D - 1);
+      Quad<T>::store(u_r, (d < D && ok4) ? uint32_t(sr) * row_bytes + st4 : kDrop,
+                     uint32_t(rb) * row_bytes, u);
+      Ops::put_col4(sU, kTT, 4 * q4, c, u);
+    }
+    __syncthreads();
+
+    // ---- 3. x_proj on the matrix cores: wave w owns steps 16 w .. 16 w + 15 --------------
+    const E* urow = sU + (wave * 16 + n16) * Ops::kRowE + CJ * g;
+    const E* wrow = sW + n16 * Ops::kRowE + CJ * g;
+#pragma unroll 1
+    for (int kk = 0; kk < kDC / KS; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        if (mt < MT)
+          acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP, urow + kk * KS,
+                                 kTT, acc[mt]);
+      }
+    }
+  }
+  __syncthreads();  // the last products have read sU and sW
+
+  // ---- 4. x_proj outputs to LDS: lane holds rows 4 (l / 16) + j of column l % 16 -------
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    if (mt < MT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sXd[mt * 16 + 4 * g + j][wave * 16 + n16] = acc[mt][j];
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. dt_proj: wave w covers channels 16 w .. 16 w + 15 of each chunk of 64, four
+  //         per lane group; then the B and C rows, four rows per wave instruction --------
+  const __amdgpu_buffer_rsrc_t dt_r =
+      make_rsrc(static_cast<T*>(a.dt_raw) + bk * D * L, uint32_t(D) * row_bytes);
+  const float* wdt = a.dt_proj_w + int64_t(k) * D * R;
+#pragma unroll 1
+  for (int dc = wave * 16; dc < D; dc += kDC) {
+    float dv[4][4];
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dv[G][j] = 0.0f;
+    for (int r = 0; r < R; ++r) {
+      const float4 x4 = *reinterpret_cast<const float4*>(&sXd[r][4 * q4]);
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const int d = dc + 4 * G + sr;
+        const float w = wdt[int64_t(min(d, D - 1)) * R + r];
+        dv[G][0] = fmaf(w, x4.x, dv[G][0]);
+        dv[G][1] = fmaf(w, x4.y, dv[G][1]);
+        dv[G][2] = fmaf(w, x4.z, dv[G][2]);
+        dv[G][3] = fmaf(w, x4.w, dv[G][3]);
+      }
+    }
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int d = dc + 4 * G + sr;
+      const uint32_t off = (d < D && ok4) ? uint32_t(d) * row_bytes + st4 : kDrop;
+      Quad<T>::store(dt_r, off, 0, dv[G]);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t b_r =
+      make_rsrc(static_cast<T*>(a.Bs) + bk * N * L, uint32_t(N) * row_bytes);
+  const __amdgpu_buffer_rsrc_t c_r =
+      make_rsrc(static_cast<T*>(a.Cs) + bk * N * L, uint32_t(N) * row_bytes);
+  for (int rg = wave; 4 * rg < 2 * N; rg += 4) {
+    const int row = 4 * rg + sr;  // 0 .. 2N - 1: B rows, then C rows
+    const float4 x4 = *reinterpret_cast<const float4*>(&sXd[R + min(row, 2 * N - 1)][4 * q4]);
+    const float v[4] = {x4.x, x4.y, x4.z, x4.w};
+    if (4 * rg < N)
+      Quad<T>::store(b_r, (row < N && ok4) ? uint32_t(row) * row_bytes + st4 : kDrop, 0, v);
+    if (4 * rg + 3 >= N)
+      Quad<T>::store(c_r, (row >= N && row < 2 * N && ok4)
+                              ? uint32_t(row - N) * row_bytes + st4 : kDrop, 0, v);
   }
 }
 
 }  // namespace
 
-int launch_project(const ProjArgs& a, int dtype, hipStream_t st) {
-  if (a.B <= 0 || a.D <= 0 || a.L <= 0) return 0;
-  const dim3 grid((a.L + kTT - 1) / kTT, a.K, a.B);
+size_t project_prep_bytes(int K, int D, int N, int R, int dtype) {
+  const int MP = 16 * ((R + 2 * N + 15) / 16);
+  const int img = dtype == 0 ? proj_img_bytes<float>(MP) : proj_img_bytes<uint16_t>(MP);
+  return size_t(K) * size_t((D + kDC - 1) / kDC) * size_t(img);
+}
+
+int launch_project(const ProjArgs& a0, int dtype, hipStream_t st) {
+  if (a0.B <= 0 || a0.D <= 0 || a0.L <= 0) return 0;
+  ProjArgs a = a0;
   const int MP = 16 * ((a.R + 2 * a.N + 15) / 16);
+  a.nchunks = (a.D + kDC - 1) / kDC;
+  a.img_bytes = dtype == 0 ? proj_img_bytes<float>(MP) : proj_img_bytes<uint16_t>(MP);
+  const dim3 pgrid(a.nchunks, a.K);
+  if (dtype == 0)
+    k_project_prep<float><<<pgrid, 256, 0, st>>>(a);
+  else
+    k_project_prep<uint16_t><<<pgrid, 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  const dim3 grid((a.L + kTT - 1) / kTT, a.K, a.B);
   const bool kw4 = a.KW == 4;
-  if (dtype == 0) {
+  if (kw4 && a.L % 4 == 0) {
+    if (dtype == 0)
+      k_project4<float><<<grid, 256, proj_lds_bytes<float>(MP), st>>>(a);
+    else
+      k_project4<uint16_t><<<grid, 256, proj_lds_bytes<uint16_t>(MP), st>>>(a);
+  } else if (dtype == 0) {
     if (kw4)
       k_project<float, 4><<<grid, 256, proj_lds_bytes<float>(MP), st>>>(a);
     else
