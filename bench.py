@@ -73,17 +73,34 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per scan launch from the committed counter summary, if it was taken on the
-    current kernel sources; else None."""
-    f = ROOT / "profiles" / f"traffic_{workload}.json"
+FRONT_SOURCES = ("ss2d_proj.hip", "ss2d_device.h")
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        f = ROOT / "selective_scan_ss2d_amd" / "csrc" / name
+        h.update(name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4):
+    """HBM bytes per launch of the scan kernel (or, with front, of k_project for the given
+    R and KW) from the committed counter summary, if it was taken on the current kernel
+    sources; else None."""
+    f = ROOT / "profiles" / (f"traffic_front_{workload}.json" if front
+                             else f"traffic_{workload}.json")
     if not f.exists():
         return None
     try:
         d = json.loads(f.read_text())
     except ValueError:
         return None
-    if d.get("source_hash") != kernel_source_hash():
+    want = source_hash(FRONT_SOURCES) if front else kernel_source_hash()
+    if d.get("source_hash") != want:
+        return None
+    if front and (d.get("R") != R or d.get("KW") != KW):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -343,7 +360,9 @@ def main() -> int:
         p_gbps = proj_bytes / p_avg_s / 1e9
         roofline_front = {"bound": "hbm", "achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(p_gbps / HBM_PEAK_GBPS, 4),
-                          "traffic": None, "kernel": "k_project",
+                          "traffic": measured_traffic(wl.name, front=True, R=args.front_r,
+                                                      KW=args.front_kw),
+                          "kernel": "k_project",
                           "kernel_avg_us": round(p_avg_s * 1e6, 1),
                           "algorithmic_bytes_per_launch": proj_bytes,
                           "R": args.front_r, "KW": args.front_kw}
