@@ -65,6 +65,13 @@ class Oracle:
                                                    ctypes.c_int]
         lib.oracle_forward_routes_ex.restype = ctypes.c_int
         lib.oracle_forward_routes_ex.argtypes = lib.oracle_forward_ex.argtypes
+        lib.oracle_forward_routes_lr_ex.restype = ctypes.c_int
+        lib.oracle_forward_routes_lr_ex.argtypes = [ctypes.c_int] + [_f32p] * 3 + \
+            [ctypes.c_int64] + [_f32p] * 6 + [ctypes.c_int, _f64p] + [ctypes.c_int64] * 5 + \
+            [ctypes.c_int]
+        lib.oracle_project_lr.restype = ctypes.c_int
+        lib.oracle_project_lr.argtypes = [ctypes.c_int] + [_f32p] * 4 + [_f64p] * 4 + \
+            [ctypes.c_int64] * 7 + [ctypes.c_int]
         lib.oracle_project.restype = ctypes.c_int
         lib.oracle_project.argtypes = [ctypes.c_int] + [_f32p] * 5 + [_f64p] * 4 + \
             [ctypes.c_int64] * 7 + [ctypes.c_int]
@@ -173,7 +180,44 @@ class Oracle:
         self.last_threads = rc
         return y.reshape(xshape)
 
-    def project(self, K, x, conv_w, conv_b, x_proj_w, dt_proj_w, threads=0):
+    def forward_routes_lr(self, K, u, dt_lr, dt_w, A_log, Bs, Cs, Ds, dt_bias, H, W,
+                          threads=0, z=None, zoh=False):
+        """forward_routes with dt_proj folded in: dt_raw = dt_w[k] @ dt_lr[b, k] per step,
+        dt_lr (B, K, R, L) the first R rows of x_proj's output, dt_w (K, D, R)."""
+        u = np.asarray(u)
+        if u.ndim != 4 or u.shape[1] != K or u.shape[3] != H * W:
+            raise ValueError(f"u has shape {u.shape}, expected (B, {K}, D, {H * W})")
+        B, _, D, L = u.shape
+        R = np.shape(dt_w)[-1]
+        if tuple(np.shape(dt_w)) != (K, D, R) or tuple(np.shape(dt_lr)) != (B, K, R, L):
+            raise ValueError("dt_w must be (K, D, R) and dt_lr (B, K, R, L)")
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        dt_stand_in = np.broadcast_to(np.float32(0), (B, K, D, L))
+        (_, _, _, _, N), keep, ptrs = self._prep(K, None, dt_stand_in, A_log, Bs, Cs, Ds,
+                                                 dt_bias, xshape=xshape)
+        uk, up = self._f32(u)
+        lk, lp = self._f32(dt_lr)
+        wk, wp = self._f32(dt_w)
+        zkeep, zp = self._gate(z, np.broadcast_to(np.float32(0), xshape))
+        y = np.empty((B, D, L), dtype=np.float64)
+        rc = self.lib.oracle_forward_routes_lr_ex(K, up, lp, wp, R, *ptrs[2:], zp,
+                                                  ORACLE_ZOH if zoh else 0,
+                                                  y.ctypes.data_as(_f64p), B, D, H, W, N,
+                                                  int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_forward_routes_lr_ex rejected its arguments")
+        self.last_threads = rc
+        return y.reshape(xshape)
+
+    def project_lr(self, K, x, conv_w, conv_b, x_proj_w, R, threads=0):
+        """project without dt_proj: dict of u (B, K, D, L), dt_lr (B, K, R, L) = the first R
+        rows of x_proj's output, Bs, Cs (B, K, N, L)."""
+        dt_w_dummy = np.zeros((K, np.shape(x)[1], R), np.float32)
+        full = self.project(K, x, conv_w, conv_b, x_proj_w, dt_w_dummy, threads=threads,
+                            _lr=True)
+        return full
+
+    def project(self, K, x, conv_w, conv_b, x_proj_w, dt_proj_w, threads=0, _lr=False):
         """Per-route front end: dict of u, dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L) in scan
         order, float64.  conv_w (K, D, KW), conv_b (K, D), x_proj_w (K, R + 2N, D),
         dt_proj_w (K, D, R)."""
@@ -204,12 +248,20 @@ class Oracle:
             a2, p = self._f32(a)
             keep.append(a2)
             ptrs.append(p)
-        out = dict(u=np.empty((B, K, D, L)), dt_raw=np.empty((B, K, D, L)),
-                   Bs=np.empty((B, K, N, L)), Cs=np.empty((B, K, N, L)))
-        rc = self.lib.oracle_project(K, *ptrs,
-                                     *[out[k].ctypes.data_as(_f64p)
-                                       for k in ("u", "dt_raw", "Bs", "Cs")],
-                                     B, D, H, W, N, R, KW, int(threads))
+        if _lr:
+            out = dict(u=np.empty((B, K, D, L)), dt_lr=np.empty((B, K, R, L)),
+                       Bs=np.empty((B, K, N, L)), Cs=np.empty((B, K, N, L)))
+            rc = self.lib.oracle_project_lr(K, *ptrs[:4],
+                                            *[out[k].ctypes.data_as(_f64p)
+                                              for k in ("u", "dt_lr", "Bs", "Cs")],
+                                            B, D, H, W, N, R, KW, int(threads))
+        else:
+            out = dict(u=np.empty((B, K, D, L)), dt_raw=np.empty((B, K, D, L)),
+                       Bs=np.empty((B, K, N, L)), Cs=np.empty((B, K, N, L)))
+            rc = self.lib.oracle_project(K, *ptrs,
+                                         *[out[k].ctypes.data_as(_f64p)
+                                           for k in ("u", "dt_raw", "Bs", "Cs")],
+                                         B, D, H, W, N, R, KW, int(threads))
         if rc < 0:
             raise RuntimeError("oracle_project rejected its arguments")
         self.last_threads = rc

@@ -45,8 +45,9 @@
  *     |delta A| keeps its digits; A = 0 takes the limit delta * B.
  *
  * A per-route front end (oracle_project: causal depthwise conv + SiLU, x_proj, dt_proj for
- * each route) and the operator over its per-route inputs (oracle_forward_routes_ex) are
- * described where they are defined, below.
+ * each route; oracle_project_lr: the same without dt_proj) and the operator over its
+ * per-route inputs (oracle_forward_routes_ex; oracle_forward_routes_lr_ex with dt_proj
+ * applied per step) are described where they are defined, below.
  *
  * Layouts (all contiguous, row-major):
  *   x, y      (B, D, H, W)    y written in full
@@ -101,6 +102,7 @@ static double silu(double z) {
  * of step t of route k is x[b, d, pi_k(t)], or, when u_routes is given, u_routes[b, k, d, t]
  * (each route's own input sequence, already in its scan order). */
 static void channel_forward(int K, const float *x, const float *u_routes, const float *dt_raw,
+                            const float *dt_lr, const float *dt_w, int64_t R,
                             const float *A_log, const float *Bs, const float *Cs,
                             const float *Ds, const float *dt_bias, const float *z, int flags,
                             int64_t D, int64_t H, int64_t W, int64_t N, int64_t b, int64_t d,
@@ -114,7 +116,9 @@ static void channel_forward(int K, const float *x, const float *u_routes, const 
     for (int k = 0; k < K; ++k) {
         const double bias = dt_bias[k * D + d];
         const double Dk = Ds[k * D + d];
-        const float *dt = dt_raw + ((b * K + k) * D + d) * L;
+        const float *dt = dt_lr ? NULL : dt_raw + ((b * K + k) * D + d) * L;
+        const float *lr = dt_lr ? dt_lr + (b * K + k) * R * L : NULL;
+        const float *wr = dt_lr ? dt_w + (k * D + d) * R : NULL;
         const float *Bk = Bs + (b * K + k) * N * L;
         const float *Ck = Cs + (b * K + k) * N * L;
         for (int64_t n = 0; n < N; ++n) {
@@ -125,7 +129,14 @@ static void channel_forward(int K, const float *x, const float *u_routes, const 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t l = route_position(K, k, t, H, W);
             const double u = uk ? uk[t] : xc[l];
-            const double delta = softplus((double)dt[t] + bias);
+            double dtv = 0.0;
+            if (lr) {
+                for (int64_t r = 0; r < R; ++r)
+                    dtv += (double)wr[r] * (double)lr[r * L + t];
+            } else {
+                dtv = dt[t];
+            }
+            const double delta = softplus(dtv + bias);
             double yk = 0.0;
             for (int64_t n = 0; n < N; ++n) {
                 const double a = exp(delta * A[n]);
@@ -154,6 +165,7 @@ static int pick_threads(int nthreads) {
  * z (B, D, H, W) is the optional gate (NULL: none); flags is 0 or ORACLE_ZOH.
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
 static int forward_all(int K, const float *x, const float *u_routes, const float *dt_raw,
+                       const float *dt_lr, const float *dt_w, int64_t R,
                        const float *A_log, const float *Bs, const float *Cs, const float *Ds,
                        const float *dt_bias, const float *z, int flags, double *y, int64_t B,
                        int64_t D, int64_t H, int64_t W, int64_t N, int nthreads) {
@@ -180,8 +192,8 @@ static int forward_all(int K, const float *x, const float *u_routes, const float
 #endif
             for (int64_t i = 0; i < total; ++i) {
                 const int64_t b = i / D, d = i % D;
-                channel_forward(K, x, u_routes, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags,
-                                D, H, W, N, b, d, y + i * L, h, h + N);
+                channel_forward(K, x, u_routes, dt_raw, dt_lr, dt_w, R, A_log, Bs, Cs, Ds,
+                                dt_bias, z, flags, D, H, W, N, b, d, y + i * L, h, h + N);
             }
             free(h);
         }
@@ -193,8 +205,8 @@ int oracle_forward_ex(int K, const float *x, const float *dt_raw, const float *A
                       const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
                       const float *z, int flags, double *y, int64_t B, int64_t D, int64_t H,
                       int64_t W, int64_t N, int nthreads) {
-    return forward_all(K, x, NULL, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, y, B, D, H, W,
-                       N, nthreads);
+    return forward_all(K, x, NULL, dt_raw, NULL, NULL, 0, A_log, Bs, Cs, Ds, dt_bias, z, flags,
+                       y, B, D, H, W, N, nthreads);
 }
 
 /* The same operator when every route brings its own input sequence: u (B, K, D, L), step t
@@ -206,8 +218,23 @@ int oracle_forward_routes_ex(int K, const float *u, const float *dt_raw, const f
                              const float *dt_bias, const float *z, int flags, double *y,
                              int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                              int nthreads) {
-    return forward_all(K, NULL, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, y, B, D, H, W,
-                       N, nthreads);
+    return forward_all(K, NULL, u, dt_raw, NULL, NULL, 0, A_log, Bs, Cs, Ds, dt_bias, z, flags,
+                       y, B, D, H, W, N, nthreads);
+}
+
+/* The same with dt_proj folded in: step t of route k takes
+ *   dt_raw = sum_{r < R} dt_w[k, d, r] * dt_lr[b, k, r, t]
+ * from the R-row x_proj output dt_lr (B, K, R, L) and the dt_proj weight dt_w (K, D, R)
+ * (the [Explainer]'s dt_proj(dt) before the softplus; its bias is dt_bias). */
+int oracle_forward_routes_lr_ex(int K, const float *u, const float *dt_lr, const float *dt_w,
+                                int64_t R, const float *A_log, const float *Bs,
+                                const float *Cs, const float *Ds, const float *dt_bias,
+                                const float *z, int flags, double *y, int64_t B, int64_t D,
+                                int64_t H, int64_t W, int64_t N, int nthreads) {
+    if (R <= 0)
+        return -1;
+    return forward_all(K, NULL, u, NULL, dt_lr, dt_w, R, A_log, Bs, Cs, Ds, dt_bias, z, flags,
+                       y, B, D, H, W, N, nthreads);
 }
 
 /* Output planes y[b_idx[i], d_idx[i], :, :] for i < nsel, written to y_sel (nsel, H, W).
@@ -240,8 +267,9 @@ int oracle_forward_channels_ex(int K, const float *x, const float *dt_raw, const
 #pragma omp for schedule(dynamic, 1)
 #endif
             for (int64_t i = 0; i < nsel; ++i)
-                channel_forward(K, x, NULL, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, D,
-                                H, W, N, b_idx[i], d_idx[i], y_sel + i * L, h, h + N);
+                channel_forward(K, x, NULL, dt_raw, NULL, NULL, 0, A_log, Bs, Cs, Ds, dt_bias,
+                                z, flags, D, H, W, N, b_idx[i], d_idx[i], y_sel + i * L, h,
+                                h + N);
             free(h);
         }
     }
@@ -284,10 +312,10 @@ int oracle_forward_channels(int K, const float *x, const float *dt_raw, const fl
  * Layouts: x (B, D, H, W); conv_w (K, D, KW); conv_b (K, D); x_proj_w (K, R + 2N, D);
  * dt_proj_w (K, D, R); outputs u, dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L) in scan order.
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
-int oracle_project(int K, const float *x, const float *conv_w, const float *conv_b,
-                   const float *x_proj_w, const float *dt_proj_w, double *u, double *dt_raw,
-                   double *Bs, double *Cs, int64_t B, int64_t D, int64_t H, int64_t W,
-                   int64_t N, int64_t R, int64_t KW, int nthreads) {
+static int project_all(int K, const float *x, const float *conv_w, const float *conv_b,
+                       const float *x_proj_w, const float *dt_proj_w, double *u, double *dt_raw,
+                       double *dt_lr, double *Bs, double *Cs, int64_t B, int64_t D, int64_t H,
+                       int64_t W, int64_t N, int64_t R, int64_t KW, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0 || R <= 0 || KW <= 0)
         return -1;
     if (K == 2 && H != 1)
@@ -333,12 +361,14 @@ int oracle_project(int K, const float *x, const float *conv_w, const float *conv
                             acc += (double)x_proj_w[((int64_t)k * M + m) * D + d] * uk[d * L + t];
                         xd[m] = acc;
                     }
-                    for (int64_t d = 0; d < D; ++d) {
+                    for (int64_t d = 0; dt_raw && d < D; ++d) {
                         double acc = 0.0;
                         for (int64_t r = 0; r < R; ++r)
                             acc += (double)dt_proj_w[((int64_t)k * D + d) * R + r] * xd[r];
                         dt_raw[(i * D + d) * L + t] = acc;
                     }
+                    for (int64_t r = 0; dt_lr && r < R; ++r)
+                        dt_lr[(i * R + r) * L + t] = xd[r];
                     for (int64_t n = 0; n < N; ++n) {
                         Bs[(i * N + n) * L + t] = xd[R + n];
                         Cs[(i * N + n) * L + t] = xd[R + N + n];
@@ -349,6 +379,24 @@ int oracle_project(int K, const float *x, const float *conv_w, const float *conv
         }
     }
     return failed ? -1 : threads;
+}
+
+int oracle_project(int K, const float *x, const float *conv_w, const float *conv_b,
+                   const float *x_proj_w, const float *dt_proj_w, double *u, double *dt_raw,
+                   double *Bs, double *Cs, int64_t B, int64_t D, int64_t H, int64_t W,
+                   int64_t N, int64_t R, int64_t KW, int nthreads) {
+    return project_all(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, u, dt_raw, NULL, Bs, Cs, B,
+                       D, H, W, N, R, KW, nthreads);
+}
+
+/* The front end without dt_proj: the first R rows of x_proj's output, dt_lr (B, K, R, L),
+ * in place of dt_raw (for the operator with dt_proj folded into the scan). */
+int oracle_project_lr(int K, const float *x, const float *conv_w, const float *conv_b,
+                      const float *x_proj_w, double *u, double *dt_lr, double *Bs, double *Cs,
+                      int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+                      int64_t KW, int nthreads) {
+    return project_all(K, x, conv_w, conv_b, x_proj_w, NULL, u, NULL, dt_lr, Bs, Cs, B, D, H,
+                       W, N, R, KW, nthreads);
 }
 
 /* ---- backward ----------------------------------------------------------------------------

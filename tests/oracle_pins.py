@@ -35,6 +35,8 @@ What pins what:
                     and the weight layouts
   routes variant    per-route inputs: the gathered x reproduces the plain operator; four
                     different inputs give the route-order sum of single-route operators
+  routes low rank   dt_proj folded in equals dt_raw = dt_w @ dt_lr (exact in fp32); the
+                    front end without dt_proj returns x_proj's first R rows
 """
 from __future__ import annotations
 
@@ -640,8 +642,44 @@ def pin_routes_variant(orc):
         _close(got, want, 0.0, 0.0, f"four inputs, K={K}")
 
 
+def pin_routes_lowrank(orc):
+    """dt_proj folded into the routes operator: fed dt_lr and dt_w it equals the routes
+    operator fed dt_raw = dt_w @ dt_lr, with values chosen so that every product and sum is
+    exact in fp32 (dt_lr on a 1/64 grid, dt_w in {±1/2, ±1, ±2}): equal results.  And the
+    front end without dt_proj returns x_proj's first R rows: with dt_proj the identity on
+    those rows, the full front end's dt_raw rows 0..R-1 are the same numbers."""
+    rng = _rng(50)
+    for K, H, W in ((4, 3, 5), (2, 1, 11)):
+        B, D, N, R = 2, 3, 2, 3
+        L = H * W
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        x, _, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, xshape=xshape)
+        u = rng.standard_normal((B, K, D, L)).astype(np.float32)
+        dt_lr = (rng.integers(-40, 40, size=(B, K, R, L)) / 64.0).astype(np.float32)
+        dt_w = rng.choice(np.array([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], np.float32),
+                          size=(K, D, R))
+        dt_raw = np.einsum("kdr,bkrl->bkdl", dt_w.astype(np.float64),
+                           dt_lr.astype(np.float64)).astype(np.float32)
+        z = rng.standard_normal(xshape).astype(np.float32)
+        for zoh, gate in ((False, None), (True, z)):
+            want = orc.forward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, bias, H, W, z=gate,
+                                      zoh=zoh)
+            got = orc.forward_routes_lr(K, u, dt_lr, dt_w, A_log, Bs, Cs, Ds, bias, H, W,
+                                        z=gate, zoh=zoh)
+            _close(got, want, 0.0, 0.0, f"routes low rank, K={K}, zoh={zoh}")
+        conv_w, conv_b, x_proj_w, _ = _front_weights(rng, K, D, N, R, 4)
+        eye = np.zeros((K, D, R), np.float32)
+        for r in range(min(R, D)):
+            eye[:, r, r] = 1.0
+        full = orc.project(K, x, conv_w, conv_b, x_proj_w, eye)
+        lr = orc.project_lr(K, x, conv_w, conv_b, x_proj_w, R)
+        for key in ("u", "Bs", "Cs"):
+            _close(lr[key], full[key], 0.0, 0.0, f"project without dt_proj: {key}, K={K}")
+        _close(lr["dt_lr"], full["dt_raw"][:, :, :R], 0.0, 0.0, f"dt rows, K={K}")
+
+
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
             pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
             pin_backward_adjoint, pin_project_impulse, pin_project_brute, pin_project_select,
-            pin_routes_variant]
+            pin_routes_variant, pin_routes_lowrank]

@@ -46,14 +46,13 @@ MUTATIONS = [
     ("column route transposed", "return (t % H) * W + t / H;", "return (t % W) * H + t / W;"),
     ("route 1 not reversed", "case 1:\n        return L - 1 - t;", "case 1:\n        return t;"),
     ("route 3 not reversed", "s = L - 1 - t;", "s = t;"),
-    ("bias outside softplus", "const double delta = softplus((double)dt[t] + bias);",
-     "const double delta = (softplus((double)dt[t]) + bias);"),
+    ("bias outside softplus", "const double delta = softplus(dtv + bias);",
+     "const double delta = (softplus(dtv) + bias);"),
     ("no delta on B", "double bbar = delta;", "double bbar = 1.0;"),
     ("softplus wrong", "return m + log1p(exp(-fabs(z)));", "return m + log1p(exp(fabs(z)));"),
     ("C replaced by B", "yk += (double)Ck[n * L + t]", "yk += (double)Bk[n * L + t]"),
     ("B layout (L, N)", "bbar * (double)Bk[n * L + t] * u", "bbar * (double)Bk[t * N + n] * u"),
-    ("delta read at image position", "const double delta = softplus((double)dt[t] + bias);",
-     "const double delta = softplus((double)dt[l] + bias);"),
+    ("delta read at image position", "                dtv = dt[t];", "                dtv = dt[l];"),
     ("backward 1D route not reversed", "return k == 0 ? t : L - 1 - t;", "return t;"),
     ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;",
      "A_log[(k * N + n) * D + d]);\n            h[n] = 0.0;"),
@@ -138,6 +137,12 @@ MUTATIONS = [
      "u_routes + ((b * K + k) * D + d) * L : NULL;", "u_routes + ((b * K) * D + d) * L : NULL;"),
     ("routes: input read in reverse", "const double u = uk ? uk[t] : xc[l];",
      "const double u = uk ? uk[L - 1 - t] : xc[l];"),
+    ("low rank: dt_w's first column for every r", "dtv += (double)wr[r] * (double)lr[r * L + t];",
+     "dtv += (double)wr[0] * (double)lr[r * L + t];"),
+    ("low rank: dt_lr of route 0", "const float *lr = dt_lr ? dt_lr + (b * K + k) * R * L : NULL;",
+     "const float *lr = dt_lr ? dt_lr + (b * K) * R * L : NULL;"),
+    ("low rank: dt rows from the B rows", "dt_lr[(i * R + r) * L + t] = xd[r];",
+     "dt_lr[(i * R + r) * L + t] = xd[R + r];"),
 ]
 
 
