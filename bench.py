@@ -130,23 +130,34 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
                       f"{wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
 
 
-def cpu_baseline_front(wl, inp, w, target_s: float, z=None, zoh=False) -> dict:
+def cpu_baseline_front(wl, inp, w, target_s: float, z=None, zoh=False,
+                       lowrank=False) -> dict:
     """The float64 oracle's per-route front end followed by its operator over per-route
-    inputs, as they are, on all host cores, over a bounded sample of whole images."""
+    inputs (with lowrank, its variants with dt_proj folded into the operator), as they are,
+    on all host cores, over a bounded sample of whole images."""
     import numpy as np
 
     import oracle
     orc = oracle.Oracle()
     cores = len(os.sched_getaffinity(0))
     front = [w[k] for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")]
+    R = w["dt_proj_w"].shape[-1]
 
     def run(n):
         t0 = time.perf_counter()
-        pr = orc.project(wl.K, inp["x"][:n], *front, threads=cores)
-        f32 = {k: v.astype(np.float32) for k, v in pr.items()}
-        orc.forward_routes(wl.K, f32["u"], f32["dt_raw"], inp["A_log"], f32["Bs"], f32["Cs"],
-                           inp["Ds"], inp["dt_bias"], wl.H, wl.W, threads=cores,
-                           z=None if z is None else z[:n], zoh=zoh)
+        zn = None if z is None else z[:n]
+        if lowrank:
+            pr = orc.project_lr(wl.K, inp["x"][:n], *front[:3], R, threads=cores)
+            f32 = {k: v.astype(np.float32) for k, v in pr.items()}
+            orc.forward_routes_lr(wl.K, f32["u"], f32["dt_lr"], front[3], inp["A_log"],
+                                  f32["Bs"], f32["Cs"], inp["Ds"], inp["dt_bias"], wl.H, wl.W,
+                                  threads=cores, z=zn, zoh=zoh)
+        else:
+            pr = orc.project(wl.K, inp["x"][:n], *front, threads=cores)
+            f32 = {k: v.astype(np.float32) for k, v in pr.items()}
+            orc.forward_routes(wl.K, f32["u"], f32["dt_raw"], inp["A_log"], f32["Bs"],
+                               f32["Cs"], inp["Ds"], inp["dt_bias"], wl.H, wl.W,
+                               threads=cores, z=zn, zoh=zoh)
         return time.perf_counter() - t0
 
     n = min(wl.B, max(1, cores // 4))
@@ -214,6 +225,9 @@ def main() -> int:
                     help="dt rank R of the front end (x_proj rows R + 2N)")
     ap.add_argument("--front-kw", type=int, default=4, metavar="KW",
                     help="conv length of the front end")
+    ap.add_argument("--front-lowrank", action="store_true",
+                    help="with --front: dt_proj folded into the scan (ss2d_project_lr, then "
+                         "ss2d_forward_routes_lr on its R dt rows)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 device-to-device copies of MIB "
                          "MiB (a plain copy kernel of known size, for scaling the HBM byte "
@@ -269,18 +283,30 @@ def main() -> int:
         z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
              if wl.dtype == "bf16" else torch.from_numpy(gate["z"])).to("cuda:0")
     front_w = None
+    if args.front_lowrank and not args.front:
+        log("--front-lowrank needs --front")
+        return 2
     if args.front:
         front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw)
         fw = [torch.from_numpy(front_w[k]).to("cuda:0")
               for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")]
-        proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
-        fwd = ss.ss2d_forward_routes if wl.K == 4 else ss.ss1d_bidir_forward_routes
         hw = (wl.H, wl.W) if wl.K == 4 else ()
+        if args.front_lowrank:
+            proj = ss.ss2d_project_lr if wl.K == 4 else ss.ss1d_bidir_project_lr
+            fwd = ss.ss2d_forward_routes_lr if wl.K == 4 else ss.ss1d_bidir_forward_routes_lr
 
-        def call():
-            o = proj(dev["x"], *fw)
-            return fwd(o["u"], o["dt_raw"], dev["A_log"], o["Bs"], o["Cs"], dev["Ds"],
-                       dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
+            def call():
+                o = proj(dev["x"], *fw[:3], args.front_r)
+                return fwd(o["u"], o["dt_lr"], fw[3], dev["A_log"], o["Bs"], o["Cs"],
+                           dev["Ds"], dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
+        else:
+            proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
+            fwd = ss.ss2d_forward_routes if wl.K == 4 else ss.ss1d_bidir_forward_routes
+
+            def call():
+                o = proj(dev["x"], *fw)
+                return fwd(o["u"], o["dt_raw"], dev["A_log"], o["Bs"], o["Cs"], dev["Ds"],
+                           dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
     elif args.backward:
         g = workloads.make_output_grad(wl, 0)
         dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
@@ -316,14 +342,18 @@ def main() -> int:
     ms_step = ms_total / args.steps
     upd_per_s = wl.updates / (ms_step / 1e3)
     alg_bytes = wl.algorithmic_bytes() + (wl.elem_bytes * wl.B * wl.D * wl.L if args.gate else 0)
-    e, M = wl.elem_bytes, args.front_r + 2 * wl.N
+    e, M, R = wl.elem_bytes, args.front_r + 2 * wl.N, args.front_r
     # front end, per launch: x read once; u and dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L)
-    # written once; the fp32 weights read once
-    proj_bytes = (e * (wl.B * wl.D * wl.L + 2 * wl.B * wl.K * wl.D * wl.L
-                       + 2 * wl.B * wl.K * wl.N * wl.L)
-                  + 4 * wl.K * wl.D * (args.front_kw + 1 + M + args.front_r))
+    # written once; the fp32 weights read once.  With dt_proj folded into the scan, the
+    # front end writes the R dt rows (B, K, R, L) in place of dt_raw and reads no dt_proj_w.
+    BKL = wl.B * wl.K * wl.L
+    proj_bytes = (e * (wl.B * wl.D * wl.L + BKL * wl.D + 2 * BKL * wl.N)
+                  + 4 * wl.K * wl.D * (args.front_kw + 1 + M))
+    proj_bytes += e * BKL * R if args.front_lowrank else e * BKL * wl.D + 4 * wl.K * wl.D * R
     if args.front:  # the scan then reads u (B, K, D, L) in place of x (B, D, L)
         alg_bytes += proj_bytes + e * (wl.K - 1) * wl.B * wl.D * wl.L
+    if args.front_lowrank:  # ... and dt_lr (B, K, R, L) and dt_w (K, D, R) for dt_raw
+        alg_bytes += e * BKL * R + 4 * wl.K * wl.D * R - e * BKL * wl.D
     gbps = alg_bytes / (ms_step / 1e3) / 1e9
     for name, (ms, n) in kernels.items():
         if n:
@@ -365,14 +395,18 @@ def main() -> int:
                           "kernel": "k_project",
                           "kernel_avg_us": round(p_avg_s * 1e6, 1),
                           "algorithmic_bytes_per_launch": proj_bytes,
-                          "R": args.front_r, "KW": args.front_kw}
+                          "R": args.front_r, "KW": args.front_kw,
+                          "dt_proj_in_scan": bool(args.front_lowrank)}
+        if args.front_lowrank:  # the committed counters cover the unfolded front end
+            roofline_front["traffic"] = None
 
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         if args.front:
             cpu = cpu_baseline_front(wl, inp, front_w, args.cpu_seconds,
-                                     z=gate["z"] if gate else None, zoh=args.zoh)
+                                     z=gate["z"] if gate else None, zoh=args.zoh,
+                                     lowrank=args.front_lowrank)
         elif args.backward:
             cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds)
         else:
@@ -398,6 +432,7 @@ def main() -> int:
                    "state_dtype": "f32", "A_log": args.a_log, "gate": bool(args.gate),
                    "zoh": bool(args.zoh),
                    "pass": ("backward" if args.backward else
+                            "front(dt_proj in scan)+forward" if args.front_lowrank else
                             "front+forward" if args.front else "forward")},
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 4
+#define SS2D_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -215,6 +215,47 @@ int ss1d_bidir_forward_routes(const void *u, const void *dt_raw, const float *A_
                               const float *dt_bias, const void *z, void *y, int64_t B,
                               int64_t D, int64_t L, int64_t N, int dtype, int flags,
                               void *stream);
+
+/* ---- the front end and the operator with dt_proj folded into the scan ---------------------
+ * dt_proj is linear and has no bias of its own (its bias is dt_bias, added inside the
+ * softplus), and the explainer's SelectiveSSM applies it to the R-row dt slice of x_proj's
+ * output (dt_rank = ceil(d_model / 16), a low rank): step t's dt_raw[d] is
+ * sum_{r<R} dt_proj_w[k,d,r] * xd[r,t].  Forming that sum inside the scan, from the R rows
+ * instead of the D rows, leaves the operator unchanged and removes dt_raw (B, K, D, L) from
+ * memory: the front end stores the R dt rows and the scan reads them back.
+ *
+ * ss2d_project_lr / ss1d_bidir_project_lr are ss2d_project / ss1d_bidir_project without
+ * dt_proj: in place of dt_raw they write dt_lr[b,k,r,t] = xd[r,t] (B, K, R, L) in dtype, and
+ * take no dt_proj_w.  Every other output, argument and error is as there.
+ *
+ * ss2d_forward_routes_lr / ss1d_bidir_forward_routes_lr are ss2d_forward_routes /
+ * ss1d_bidir_forward_routes with dt_raw given as the product
+ *   dt_raw[b,k,d,t] = sum_{r<R} dt_w[k,d,r] * dt_lr[b,k,r,t]
+ * formed in fp32 at every step (dt_lr (B, K, R, L) in dtype, dt_w (K, D, R) fp32, both read
+ * only).  Supported: 1 <= R <= 4 (else SS2D_ERR_UNSUPPORTED); y must overlap neither dt_lr
+ * nor dt_w (SS2D_ERR_ALIAS); NULL dt_lr or dt_w gives SS2D_ERR_NULL.  Every other argument,
+ * error and convention is that of ss2d_forward_routes. */
+int ss2d_project_lr(const void *x, const float *conv_w, const float *conv_b,
+                    const float *x_proj_w, void *u, void *dt_lr, void *Bs, void *Cs, int64_t B,
+                    int64_t D, int64_t H, int64_t W, int64_t N, int64_t R, int64_t KW,
+                    int dtype, void *stream);
+
+int ss1d_bidir_project_lr(const void *x, const float *conv_w, const float *conv_b,
+                          const float *x_proj_w, void *u, void *dt_lr, void *Bs, void *Cs,
+                          int64_t B, int64_t D, int64_t L, int64_t N, int64_t R, int64_t KW,
+                          int dtype, void *stream);
+
+int ss2d_forward_routes_lr(const void *u, const void *dt_lr, const float *dt_w,
+                           const float *A_log, const void *Bs, const void *Cs, const float *Ds,
+                           const float *dt_bias, const void *z, void *y, int64_t B, int64_t D,
+                           int64_t H, int64_t W, int64_t N, int64_t R, int dtype, int flags,
+                           void *stream);
+
+int ss1d_bidir_forward_routes_lr(const void *u, const void *dt_lr, const float *dt_w,
+                                 const float *A_log, const void *Bs, const void *Cs,
+                                 const float *Ds, const float *dt_bias, const void *z, void *y,
+                                 int64_t B, int64_t D, int64_t L, int64_t N, int64_t R,
+                                 int dtype, int flags, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ss2d_status_string(int status);

@@ -40,6 +40,12 @@ SIGNATURES = {
     "ss2d_forward_routes": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_forward_routes": (ctypes.c_int,
                                   [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_project_lr": (ctypes.c_int, [_P] * 8 + [_I64] * 7 + [ctypes.c_int, _P]),
+    "ss1d_bidir_project_lr": (ctypes.c_int, [_P] * 8 + [_I64] * 6 + [ctypes.c_int, _P]),
+    "ss2d_forward_routes_lr": (ctypes.c_int,
+                               [_P] * 10 + [_I64] * 6 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_forward_routes_lr": (ctypes.c_int,
+                                     [_P] * 10 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -246,7 +252,10 @@ def ss1d_bidir_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=Fal
     return y
 
 
-def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream, xshape):
+def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream, xshape,
+                    dt_w=None):
+    """dt_w given: dt_raw is the low-rank dt_lr (B, K, R, L), multiplied by dt_w (K, D, R)
+    inside the scan."""
     torch = _torch()
     lib = load_library()
     if u.device.type != "cuda":
@@ -256,7 +265,14 @@ def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
     dt, dev = u.dtype, u.device
     _dtype_code(u)
     _expect("u", u, (B, K, D, L), dt, dev)
-    _expect("dt_raw", dt_raw, (B, K, D, L), dt, dev)
+    if dt_w is None:
+        _expect("dt_raw", dt_raw, (B, K, D, L), dt, dev)
+    else:
+        if dt_w.dim() != 3:
+            raise ValueError("dt_w must be (K, D, R)")
+        R = dt_w.shape[-1]
+        _expect("dt_w", dt_w, (K, D, R), torch.float32, dev)
+        _expect("dt_lr", dt_raw, (B, K, R, L), dt, dev)
     _expect("A_log", A_log, (K, D, N), torch.float32, dev)
     _expect("Bs", Bs, (B, K, N, L), dt, dev)
     _expect("Cs", Cs, (B, K, N, L), dt, dev)
@@ -267,11 +283,16 @@ def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
     else:
         _expect("y", y, xshape, dt, dev)
     zp = _gate_ptr(z, xshape, u)
-    fn = lib.ss2d_forward_routes if K == 4 else lib.ss1d_bidir_forward_routes
-    status = fn(u.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(), Bs.data_ptr(),
-                Cs.data_ptr(), Ds.data_ptr(), dt_bias.data_ptr(), zp, y.data_ptr(),
-                *xshape[:2], *xshape[2:], N, _dtype_code(u), SS2D_FLAG_ZOH if zoh else 0,
-                _stream_handle(dev, stream))
+    common = (A_log.data_ptr(), Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
+              dt_bias.data_ptr(), zp, y.data_ptr(), *xshape[:2], *xshape[2:], N)
+    tail = (_dtype_code(u), SS2D_FLAG_ZOH if zoh else 0, _stream_handle(dev, stream))
+    if dt_w is None:
+        fn = lib.ss2d_forward_routes if K == 4 else lib.ss1d_bidir_forward_routes
+        status = fn(u.data_ptr(), dt_raw.data_ptr(), *common, *tail)
+    else:
+        fn = lib.ss2d_forward_routes_lr if K == 4 else lib.ss1d_bidir_forward_routes_lr
+        status = fn(u.data_ptr(), dt_raw.data_ptr(), dt_w.data_ptr(), *common, dt_w.shape[-1],
+                    *tail)
     _check(status)
     return y
 
@@ -297,7 +318,30 @@ def ss1d_bidir_forward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh
                            (u.shape[0], u.shape[2], u.shape[3]))
 
 
-def _project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, xshape):
+def ss2d_forward_routes_lr(u, dt_lr, dt_w, A_log, Bs, Cs, Ds, dt_bias, H, W, z=None,
+                           zoh=False, y=None, stream=None):
+    """ss2d_forward_routes with dt_proj folded into the scan: each step's dt_raw is
+    dt_w (4, D, R) fp32 times the step's column of dt_lr (B, 4, R, L).  Returns y (B, D, H, W)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 4, D, L)")
+    if u.shape[-1] != H * W:
+        raise ValueError(f"u has {u.shape[-1]} steps, expected H * W = {H * W}")
+    return _routes_forward(4, u, dt_lr, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (u.shape[0], u.shape[2], H, W), dt_w=dt_w)
+
+
+def ss1d_bidir_forward_routes_lr(u, dt_lr, dt_w, A_log, Bs, Cs, Ds, dt_bias, z=None,
+                                 zoh=False, y=None, stream=None):
+    """ss1d_bidir_forward_routes with dt_proj folded into the scan (dt_lr (B, 2, R, L),
+    dt_w (2, D, R)).  Returns y (B, D, L)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 2, D, L)")
+    return _routes_forward(2, u, dt_lr, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (u.shape[0], u.shape[2], u.shape[3]), dt_w=dt_w)
+
+
+def _project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, xshape, R=None):
+    """dt_proj_w None: the low-rank variant with R dt rows, returning dt_lr for dt_raw."""
     torch = _torch()
     lib = load_library()
     if x.device.type != "cuda":
@@ -308,9 +352,12 @@ def _project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, xshape):
         L *= v
     dt, dev = x.dtype, x.device
     _dtype_code(x)
-    if conv_w.dim() != 3 or dt_proj_w.dim() != 3 or x_proj_w.dim() != 3:
+    lr = dt_proj_w is None
+    if conv_w.dim() != 3 or x_proj_w.dim() != 3 or (not lr and dt_proj_w.dim() != 3):
         raise ValueError("conv_w, x_proj_w and dt_proj_w must be 3-D")
-    KW, R, M = conv_w.shape[-1], dt_proj_w.shape[-1], x_proj_w.shape[1]
+    if not lr:
+        R = dt_proj_w.shape[-1]
+    KW, M = conv_w.shape[-1], x_proj_w.shape[1]
     N = (M - R) // 2
     if N < 1 or M != R + 2 * N:
         raise ValueError(f"x_proj_w has {M} rows, expected R + 2N with R = {R}")
@@ -318,15 +365,23 @@ def _project(K, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, xshape):
     _expect("conv_w", conv_w, (K, D, KW), torch.float32, dev)
     _expect("conv_b", conv_b, (K, D), torch.float32, dev)
     _expect("x_proj_w", x_proj_w, (K, M, D), torch.float32, dev)
-    _expect("dt_proj_w", dt_proj_w, (K, D, R), torch.float32, dev)
-    out = dict(u=torch.empty((B, K, D, L), dtype=dt, device=dev),
-               dt_raw=torch.empty((B, K, D, L), dtype=dt, device=dev),
-               Bs=torch.empty((B, K, N, L), dtype=dt, device=dev),
-               Cs=torch.empty((B, K, N, L), dtype=dt, device=dev))
-    fn = lib.ss2d_project if K == 4 else lib.ss1d_bidir_project
-    status = fn(x.data_ptr(), conv_w.data_ptr(), conv_b.data_ptr(), x_proj_w.data_ptr(),
-                dt_proj_w.data_ptr(), *[out[k].data_ptr() for k in ("u", "dt_raw", "Bs", "Cs")],
-                *xshape, N, R, KW, _dtype_code(x), _stream_handle(dev, stream))
+    if not lr:
+        _expect("dt_proj_w", dt_proj_w, (K, D, R), torch.float32, dev)
+    dt_name = "dt_lr" if lr else "dt_raw"
+    out = {"u": torch.empty((B, K, D, L), dtype=dt, device=dev),
+           dt_name: torch.empty((B, K, R if lr else D, L), dtype=dt, device=dev),
+           "Bs": torch.empty((B, K, N, L), dtype=dt, device=dev),
+           "Cs": torch.empty((B, K, N, L), dtype=dt, device=dev)}
+    outs = [out[k].data_ptr() for k in ("u", dt_name, "Bs", "Cs")]
+    tail = (*xshape, N, R, KW, _dtype_code(x), _stream_handle(dev, stream))
+    if lr:
+        fn = lib.ss2d_project_lr if K == 4 else lib.ss1d_bidir_project_lr
+        status = fn(x.data_ptr(), conv_w.data_ptr(), conv_b.data_ptr(), x_proj_w.data_ptr(),
+                    *outs, *tail)
+    else:
+        fn = lib.ss2d_project if K == 4 else lib.ss1d_bidir_project
+        status = fn(x.data_ptr(), conv_w.data_ptr(), conv_b.data_ptr(), x_proj_w.data_ptr(),
+                    dt_proj_w.data_ptr(), *outs, *tail)
     _check(status)
     return out
 
@@ -346,6 +401,21 @@ def ss1d_bidir_project(x, conv_w, conv_b, x_proj_w, dt_proj_w, stream=None):
     if x.dim() != 3:
         raise ValueError("x must be (B, D, L)")
     return _project(2, x, conv_w, conv_b, x_proj_w, dt_proj_w, stream, tuple(x.shape))
+
+
+def ss2d_project_lr(x, conv_w, conv_b, x_proj_w, R, stream=None):
+    """ss2d_project without dt_proj: returns u, Bs, Cs as there and dt_lr (B, 4, R, L), the
+    R dt rows of x_proj's output, for ss2d_forward_routes_lr."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    return _project(4, x, conv_w, conv_b, x_proj_w, None, stream, tuple(x.shape), R=int(R))
+
+
+def ss1d_bidir_project_lr(x, conv_w, conv_b, x_proj_w, R, stream=None):
+    """ss1d_bidir_project without dt_proj (dt_lr (B, 2, R, L) in place of dt_raw)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    return _project(2, x, conv_w, conv_b, x_proj_w, None, stream, tuple(x.shape), R=int(R))
 
 
 GRAD_NAMES = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")

@@ -173,6 +173,13 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
 
 int run_scan(const ss2d::ScanArgs& a, int dtype, int split, bool vec, int mode,
              hipStream_t st) {
+  if (a.dt_lr) {
+    if (a.zoh)
+      return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh_lr(a, split, vec, mode, st)
+                               : ss2d::launch_scan_bf16_zoh_lr(a, split, vec, mode, st);
+    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_lr(a, split, vec, mode, st)
+                             : ss2d::launch_scan_bf16_lr(a, split, vec, mode, st);
+  }
   if (a.zoh)
     return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh(a, split, vec, mode, st)
                              : ss2d::launch_scan_bf16_zoh(a, split, vec, mode, st);
@@ -194,7 +201,8 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
     const int64_t x_per_b = (a.x_routes ? K : 1) * D * L * e;  // per-route inputs: (B, K, D, L)
     s.x_row = static_cast<const char*>(a.x_row) + b0 * x_per_b;
     s.x_col = static_cast<const char*>(a.x_col) + b0 * x_per_b;
-    s.dt_raw = static_cast<const char*>(a.dt_raw) + b0 * K * D * L * e;
+    if (a.dt_raw) s.dt_raw = static_cast<const char*>(a.dt_raw) + b0 * K * D * L * e;
+    if (a.dt_lr) s.dt_lr = static_cast<const char*>(a.dt_lr) + b0 * K * a.R * L * e;
     s.Bs = static_cast<const char*>(a.Bs) + b0 * K * N * L * e;
     s.Cs = static_cast<const char*>(a.Cs) + b0 * K * N * L * e;
     s.y_route = a.y_route ? a.y_route + b0 * K * D * L : nullptr;
@@ -211,10 +219,14 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
 }
 
 // routes: x is every route's own input u (B, K, D, L) in scan order instead of the image x.
+// dt_lr (not NULL): dt_proj folded in; dt_raw is then ignored and each step's dt_raw is
+// dt_w (K, D, R) times the step's column of dt_lr (B, K, R, L).
 int forward(int K, bool routes, const void* x, const void* dt_raw, const float* A_log,
             const void* Bs, const void* Cs, const float* Ds, const float* dt_bias, const void* z,
             void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
-            int flags, void* stream) {
+            int flags, void* stream, const void* dt_lr = nullptr, const float* dt_w = nullptr,
+            int64_t R = 0) {
+  const bool lr = dt_lr != nullptr || dt_w != nullptr || R != 0;
   // ---- validation (nothing is enqueued before all of it passes) -------------------------
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
@@ -227,18 +239,23 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   if (!mul_ok(B, D, &tmp) || !mul_ok(tmp, L, &n_x)) return SS2D_ERR_SHAPE;
   if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
   if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
+  if (lr && (R < 1 || R > ss2d::kMaxLowRank)) return SS2D_ERR_UNSUPPORTED;
   if (B == 0 || D == 0) return SS2D_OK;
-  if (!x || !dt_raw || !A_log || !Bs || !Cs || !Ds || !dt_bias || !y) return SS2D_ERR_NULL;
+  if (!x || !A_log || !Bs || !Cs || !Ds || !dt_bias || !y) return SS2D_ERR_NULL;
+  if (lr ? (!dt_lr || !dt_w) : !dt_raw) return SS2D_ERR_NULL;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
-  for (const void* ptr : {x, dt_raw, Bs, Cs, z, static_cast<const void*>(y)})
+  for (const void* ptr : {x, lr ? dt_lr : dt_raw, Bs, Cs, z, static_cast<const void*>(y)})
     if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
+  if (lr && (reinterpret_cast<uintptr_t>(dt_w) & 3u)) return SS2D_ERR_ALIGN;
   for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
                           static_cast<const void*>(dt_bias)})
     if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
   const int64_t y_bytes = n_x * e;
   if (overlaps(y, y_bytes, x, (routes ? n_dt : n_x) * e) ||
-      overlaps(y, y_bytes, dt_raw, n_dt * e) ||
+      (lr ? overlaps(y, y_bytes, dt_lr, B * K * R * H * W * e) ||
+                overlaps(y, y_bytes, dt_w, int64_t(K) * D * R * 4)
+          : overlaps(y, y_bytes, dt_raw, n_dt * e)) ||
       overlaps(y, y_bytes, Bs, n_bc * e) || overlaps(y, y_bytes, Cs, n_bc * e) ||
       overlaps(y, y_bytes, A_log, int64_t(K) * D * N * 4) ||
       overlaps(y, y_bytes, Ds, int64_t(K) * D * 4) ||
@@ -253,7 +270,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   if (he != hipSuccess) return hip_fail(he);
   int rc = prepare_pool(device);
   if (rc != SS2D_OK) return rc;
-  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, dt_raw, routes);
+  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, lr ? dt_lr : dt_raw, routes);
   char* ws = nullptr;
   he = hipMallocAsync(reinterpret_cast<void**>(&ws), p.bytes, st);
   if (he != hipSuccess) return hip_fail(he);
@@ -277,6 +294,12 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   a.chunk_len = p.chunk_len;
   a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
   a.x_routes = routes ? 1 : 0;
+  if (lr) {
+    a.dt_raw = nullptr;
+    a.dt_lr = dt_lr;
+    a.dt_w = dt_w;
+    a.R = static_cast<int>(R);
+  }
 
   int err = 0;
   if (p.need_xt)
@@ -498,10 +521,13 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
 }
 
 // ---- per-route front end -----------------------------------------------------------------
+// dt_lr (not NULL): store x_proj's R dt rows there instead of applying dt_proj (dt_proj_w
+// and dt_raw are then unused).
 int project(int K, const void* x, const float* conv_w, const float* conv_b,
             const float* x_proj_w, const float* dt_proj_w, void* u, void* dt_raw, void* Bs,
             void* Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
-            int64_t KW, int dtype, void* stream) {
+            int64_t KW, int dtype, void* stream, void* dt_lr = nullptr) {
+  const bool lr = dt_lr != nullptr;
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1 || R < 1 || KW < 1) return SS2D_ERR_SHAPE;
   if (KW > ss2d::kProjMaxKW || R + 2 * N > ss2d::kProjMaxM) return SS2D_ERR_UNSUPPORTED;
@@ -517,24 +543,25 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
   if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
   if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
   if (B == 0 || D == 0) return SS2D_OK;
-  const void* ins[] = {x, conv_w, conv_b, x_proj_w, dt_proj_w};
-  const void* outs[] = {u, dt_raw, Bs, Cs};
+  // with dt_lr, its place among the outputs is dt_lr's and dt_proj_w's among the inputs
+  // is taken by conv_b again (checked twice, harmlessly)
+  const void* ins[] = {x, conv_w, conv_b, x_proj_w, lr ? conv_b : dt_proj_w};
+  const void* outs[] = {u, lr ? dt_lr : dt_raw, Bs, Cs};
   for (const void* ptr : ins)
     if (!ptr) return SS2D_ERR_NULL;
   for (const void* ptr : outs)
     if (!ptr) return SS2D_ERR_NULL;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
-  for (const void* ptr : {x, static_cast<const void*>(u), static_cast<const void*>(dt_raw),
-                          static_cast<const void*>(Bs), static_cast<const void*>(Cs)})
+  for (const void* ptr : {x, outs[0], outs[1], outs[2], outs[3]})
     if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
-  for (const void* ptr : {static_cast<const void*>(conv_w), static_cast<const void*>(conv_b),
-                          static_cast<const void*>(x_proj_w),
-                          static_cast<const void*>(dt_proj_w)})
+  for (const void* ptr : {ins[1], ins[2], ins[3], ins[4]})
     if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
   const int64_t in_bytes[] = {n_x * e, int64_t(K) * D * KW * 4, int64_t(K) * D * 4,
-                              int64_t(K) * (R + 2 * N) * D * 4, int64_t(K) * D * R * 4};
-  const int64_t out_bytes[] = {n_dt * e, n_dt * e, n_bc * e, n_bc * e};
+                              int64_t(K) * (R + 2 * N) * D * 4,
+                              lr ? int64_t(K) * D * 4 : int64_t(K) * D * R * 4};
+  const int64_t n_lr = B * K * R * L;
+  const int64_t out_bytes[] = {n_dt * e, (lr ? n_lr : n_dt) * e, n_bc * e, n_bc * e};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 5; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SS2D_ERR_ALIAS;
@@ -574,7 +601,10 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
     a.x_proj_w = x_proj_w;
     a.dt_proj_w = dt_proj_w;
     a.u = static_cast<char*>(u) + b0 * K * D * L * e;
-    a.dt_raw = static_cast<char*>(dt_raw) + b0 * K * D * L * e;
+    if (lr)
+      a.dt_lr = static_cast<char*>(dt_lr) + b0 * K * R * L * e;
+    else
+      a.dt_raw = static_cast<char*>(dt_raw) + b0 * K * D * L * e;
     a.Bs = static_cast<char*>(Bs) + b0 * K * N * L * e;
     a.Cs = static_cast<char*>(Cs) + b0 * K * N * L * e;
     a.wprep = ws + off_prep;
@@ -661,12 +691,46 @@ int ss1d_bidir_project(const void* x, const float* conv_w, const float* conv_b,
                  R, KW, dtype, stream);
 }
 
+int ss2d_project_lr(const void* x, const float* conv_w, const float* conv_b,
+                    const float* x_proj_w, void* u, void* dt_lr, void* Bs, void* Cs, int64_t B,
+                    int64_t D, int64_t H, int64_t W, int64_t N, int64_t R, int64_t KW,
+                    int dtype, void* stream) {
+  return project(4, x, conv_w, conv_b, x_proj_w, nullptr, u, nullptr, Bs, Cs, B, D, H, W, N,
+                 R, KW, dtype, stream, dt_lr);
+}
+
+int ss1d_bidir_project_lr(const void* x, const float* conv_w, const float* conv_b,
+                          const float* x_proj_w, void* u, void* dt_lr, void* Bs, void* Cs,
+                          int64_t B, int64_t D, int64_t L, int64_t N, int64_t R, int64_t KW,
+                          int dtype, void* stream) {
+  return project(2, x, conv_w, conv_b, x_proj_w, nullptr, u, nullptr, Bs, Cs, B, D, 1, L, N,
+                 R, KW, dtype, stream, dt_lr);
+}
+
 int ss2d_forward_routes(const void* u, const void* dt_raw, const float* A_log, const void* Bs,
                         const void* Cs, const float* Ds, const float* dt_bias, const void* z,
                         void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                         int dtype, int flags, void* stream) {
   return forward(4, true, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype,
                  flags, stream);
+}
+
+int ss2d_forward_routes_lr(const void* u, const void* dt_lr, const float* dt_w,
+                           const float* A_log, const void* Bs, const void* Cs, const float* Ds,
+                           const float* dt_bias, const void* z, void* y, int64_t B, int64_t D,
+                           int64_t H, int64_t W, int64_t N, int64_t R, int dtype, int flags,
+                           void* stream) {
+  return forward(4, true, u, nullptr, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype,
+                 flags, stream, dt_lr, dt_w, R);
+}
+
+int ss1d_bidir_forward_routes_lr(const void* u, const void* dt_lr, const float* dt_w,
+                                 const float* A_log, const void* Bs, const void* Cs,
+                                 const float* Ds, const float* dt_bias, const void* z, void* y,
+                                 int64_t B, int64_t D, int64_t L, int64_t N, int64_t R,
+                                 int dtype, int flags, void* stream) {
+  return forward(2, true, u, nullptr, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype,
+                 flags, stream, dt_lr, dt_w, R);
 }
 
 int ss1d_bidir_forward_routes(const void* u, const void* dt_raw, const float* A_log,

@@ -136,7 +136,11 @@ struct ScanArgs {
   int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
   int ck_tiles;           // kModeCkpt: 32-step tiles per sequence; h_in receives the states
   int x_routes;           // nonzero: x_row holds each route's own input sequence
+  const void* dt_lr;      // dt_proj folded in (else NULL): x_proj's dt rows (B, K, R, L) ...
+  const float* dt_w;      // ... and the dt_proj weight (K, D, R): dt_raw = dt_w @ dt_lr
+  int R;                  // rows of dt_lr, 1 .. kMaxLowRank
 };
+constexpr int kMaxLowRank = 4;  // dt rows a tile row of the scan's B/C LDS tile can hold
 
 enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2 };
 
@@ -176,6 +180,8 @@ struct ProjArgs {
   void* dt_raw;             // (B, K, D, L)
   void* Bs;                 // (B, K, N, L)
   void* Cs;                 // (B, K, N, L)
+  void* dt_lr;              // not NULL: x_proj's R dt rows (B, K, R, L) are stored here and
+                            // dt_proj is not applied (dt_raw and dt_proj_w are unused)
   const void* wprep;        // per (k, 64-channel chunk): x_proj weights and conv taps laid
                             // out as the kernel's LDS image, img_bytes each
   int B, K, D, L, N, R, KW;
@@ -191,6 +197,11 @@ int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_
 int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
 int launch_scan_f32_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
 int launch_scan_bf16_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+// dt_proj folded in (a.dt_lr set): forward modes only
+int launch_scan_f32_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_bf16_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_f32_zoh_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_bf16_zoh_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st);
 int launch_carry(const ScanArgs& a, hipStream_t st);

@@ -421,11 +421,18 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
   __syncthreads();
 
   // ---- 5. dt_proj (wave w: channels 16 w .. 16 w + 15 of each chunk of 64), then B, C ---
-  T* dt_out = static_cast<T*>(a.dt_raw) + bk * D * L;
-  const __amdgpu_buffer_rsrc_t dt_r = make_rsrc(dt_out, uint32_t(D) * row_bytes);
-  cfloat* wdt = (cfloat*)(a.dt_proj_w + int64_t(k) * D * R);
+  if (a.dt_lr) {  // dt_proj folded into the scan: store x_proj's dt rows instead
+    const __amdgpu_buffer_rsrc_t lr_r =
+        make_rsrc(static_cast<T*>(a.dt_lr) + bk * R * L, uint32_t(R) * row_bytes);
+    for (int row = wave; row < R; row += 4)
+      buf_store_at(lr_r, so_t, uint32_t(row) * row_bytes, out_elem<T>(sXd[row][lane]));
+  }
+  T* dt_out = a.dt_lr ? nullptr : static_cast<T*>(a.dt_raw) + bk * D * L;
+  const __amdgpu_buffer_rsrc_t dt_r =
+      make_rsrc(dt_out, a.dt_lr ? 0u : uint32_t(D) * row_bytes);
+  cfloat* wdt = (cfloat*)(a.dt_lr ? nullptr : a.dt_proj_w + int64_t(k) * D * R);
 #pragma unroll 1
-  for (int d0 = wave * 16; d0 < D; d0 += kDC) {
+  for (int d0 = wave * 16; a.dt_lr == nullptr && d0 < D; d0 += kDC) {
     float dv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) dv[i] = 0.0f;
@@ -616,11 +623,22 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
 
   // ---- 5. dt_proj: wave w covers channels 16 w .. 16 w + 15 of each chunk of 64, four
   //         per lane group; then the B and C rows, four rows per wave instruction --------
+  if (a.dt_lr) {  // dt_proj folded into the scan: store x_proj's dt rows instead
+    const __amdgpu_buffer_rsrc_t lr_r =
+        make_rsrc(static_cast<T*>(a.dt_lr) + bk * R * L, uint32_t(R) * row_bytes);
+    for (int rg = wave; 4 * rg < R; rg += 4) {
+      const int row = 4 * rg + sr;
+      const float4 x4 = *reinterpret_cast<const float4*>(&sXd[min(row, R - 1)][4 * q4]);
+      const float v[4] = {x4.x, x4.y, x4.z, x4.w};
+      Quad<T>::store(lr_r, (row < R && ok4) ? uint32_t(row) * row_bytes + st4 : kDrop, 0, v);
+    }
+  }
   const __amdgpu_buffer_rsrc_t dt_r =
-      make_rsrc(static_cast<T*>(a.dt_raw) + bk * D * L, uint32_t(D) * row_bytes);
-  const float* wdt = a.dt_proj_w + int64_t(k) * D * R;
+      make_rsrc(a.dt_lr ? nullptr : static_cast<T*>(a.dt_raw) + bk * D * L,
+                a.dt_lr ? 0u : uint32_t(D) * row_bytes);
+  const float* wdt = a.dt_lr ? nullptr : a.dt_proj_w + int64_t(k) * D * R;
 #pragma unroll 1
-  for (int dc = wave * 16; dc < D; dc += kDC) {
+  for (int dc = wave * 16; a.dt_lr == nullptr && dc < D; dc += kDC) {
     float dv[4][4];
 #pragma unroll
     for (int G = 0; G < 4; ++G)

@@ -3,6 +3,6 @@
 
 namespace ss2d {
 int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
-  return launch_scan_t<uint16_t, false>(a, split, vec, mode, st);
+  return launch_scan_t<uint16_t, false, false>(a, split, vec, mode, st);
 }
 }  // namespace ss2d

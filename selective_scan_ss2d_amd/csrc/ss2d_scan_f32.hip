@@ -3,6 +3,6 @@
 
 namespace ss2d {
 int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
-  return launch_scan_t<float, false>(a, split, vec, mode, st);
+  return launch_scan_t<float, false, false>(a, split, vec, mode, st);
 }
 }  // namespace ss2d

@@ -1,0 +1,8 @@
+// fp32 instantiations of the selective-scan kernel, delta * B discretisation, dt_proj folded into the scan.
+#include "ss2d_scan.inc"
+
+namespace ss2d {
+int launch_scan_f32_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
+  return launch_scan_t<float, false, true>(a, split, vec, mode, st);
+}
+}  // namespace ss2d

@@ -3,6 +3,6 @@
 
 namespace ss2d {
 int launch_scan_f32_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
-  return launch_scan_t<float, true>(a, split, vec, mode, st);
+  return launch_scan_t<float, true, false>(a, split, vec, mode, st);
 }
 }  // namespace ss2d

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 4
+    assert lib.ss2d_abi_version() == 5
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -263,6 +263,80 @@ def test_forward_routes_argument_errors(lib):
     import torch
     if not torch.cuda.is_available():
         assert call_routes(lib, fake_ptrs(), None) == bnd.SS2D_ERR_HIP
+
+
+def call_proj_lr(lib, ptrs, B=1, D=8, H=8, W=8, N=4, R=2, KW=4, dtype=0, K=4):
+    if K == 4:
+        return lib.ss2d_project_lr(*ptrs, B, D, H, W, N, R, KW, dtype, None)
+    return lib.ss1d_bidir_project_lr(*ptrs, B, D, H * W, N, R, KW, dtype, None)
+
+
+def test_project_lr_argument_errors(lib):
+    # x, conv_w, conv_b, x_proj_w, then the outputs u, dt_lr, Bs, Cs
+    ptrs = fake_ptrs(8)
+    for K in (4, 2):
+        for i in range(8):
+            p = list(ptrs)
+            p[i] = None
+            assert call_proj_lr(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        assert call_proj_lr(lib, ptrs, KW=9, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_proj_lr(lib, ptrs, R=65, N=16, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        for bad in (dict(KW=0), dict(R=0), dict(N=0), dict(B=-1), dict(H=0)):
+            assert call_proj_lr(lib, ptrs, K=K, **bad) == bnd.SS2D_ERR_SHAPE, bad
+        assert call_proj_lr(lib, [None] * 8, B=0, K=K) == bnd.SS2D_OK
+        for i in range(8):
+            p = list(ptrs)
+            p[i] += 1
+            assert call_proj_lr(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
+        for i in range(4, 8):
+            for j in range(0, i):
+                p = list(ptrs)
+                p[i] = p[j] + 4
+                assert call_proj_lr(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i, j)
+        # dt_lr holds B * K * R * L elements: an output placed just past that is disjoint,
+        # one placed inside it is not
+        p = list(ptrs)
+        p[6] = p[5] + 1 * K * 2 * 64 * 4 - 4
+        assert call_proj_lr(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
+    import torch
+    if not torch.cuda.is_available():
+        assert call_proj_lr(lib, ptrs) == bnd.SS2D_ERR_HIP
+        p = list(ptrs)
+        p[6] = p[5] + 1 * 4 * 2 * 64 * 4
+        assert call_proj_lr(lib, p) == bnd.SS2D_ERR_HIP
+
+
+def call_routes_lr(lib, ptrs, z=None, flags=0, B=1, D=8, H=8, W=8, N=4, R=2, dtype=0, K=4):
+    # ptrs: u, dt_lr, dt_w, A_log, Bs, Cs, Ds, dt_bias, y
+    if K == 4:
+        return lib.ss2d_forward_routes_lr(*ptrs[:8], z, ptrs[8], B, D, H, W, N, R, dtype,
+                                          flags, None)
+    return lib.ss1d_bidir_forward_routes_lr(*ptrs[:8], z, ptrs[8], B, D, H * W, N, R, dtype,
+                                            flags, None)
+
+
+def test_forward_routes_lr_argument_errors(lib):
+    z = (1 << 40) + 10 * (1 << 32)
+    for K in (4, 2):
+        for i in range(9):
+            p = fake_ptrs(9)
+            p[i] = None
+            assert call_routes_lr(lib, p, z, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        for R in (0, 5, -1):
+            assert call_routes_lr(lib, fake_ptrs(9), z, R=R, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_routes_lr(lib, fake_ptrs(9), z, N=3, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        p = fake_ptrs(9)
+        p[2] += 2  # dt_w is fp32
+        assert call_routes_lr(lib, p, z, K=K) == bnd.SS2D_ERR_ALIGN
+        for j in (1, 2):  # y inside dt_lr or dt_w
+            p = fake_ptrs(9)
+            p[8] = p[j] + 4
+            assert call_routes_lr(lib, p, z, K=K) == bnd.SS2D_ERR_ALIAS, (K, j)
+        assert call_routes_lr(lib, [None] * 9, None, B=0, K=K) == bnd.SS2D_OK
+    import torch
+    if not torch.cuda.is_available():
+        for R in (1, 4):
+            assert call_routes_lr(lib, fake_ptrs(9), None, R=R) == bnd.SS2D_ERR_HIP
 
 
 def test_valid_call_without_gpu_reports_hip_error(lib):

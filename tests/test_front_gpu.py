@@ -213,3 +213,190 @@ def test_full_size_sampled_images(orc, name, R):
                                   sl["Cs"], inp["Ds"], inp["dt_bias"], wl.H, wl.W)
         assert_parity(to_numpy_f64(y[b:b + 1]), refy.reshape(y[b:b + 1].shape), wl.dtype,
                       f"full {name} b={b} routes")
+
+
+# ---- dt_proj folded into the scan: the front end's R dt rows and the operator over them ----
+def check_project_lr(orc, wl, R, KW, seed=0):
+    import torch
+    import selective_scan_ss2d_amd as ss
+    what = f"project_lr B{wl.B} D{wl.D} {wl.H}x{wl.W} N{wl.N} K{wl.K} R{R} KW{KW} {wl.dtype}"
+    log(f"case {what}")
+    inp = workloads.make_inputs(wl, seed=seed)
+    w = workloads.make_front_weights(wl, seed, R=R, KW=KW)
+    ref = orc.project_lr(wl.K, inp["x"], w["conv_w"], w["conv_b"], w["x_proj_w"], R)
+    wd = _weights_dev(w)
+    fn = ss.ss2d_project_lr if wl.K == 4 else ss.ss1d_bidir_project_lr
+    got = fn(to_device(inp, wl)["x"], wd["conv_w"], wd["conv_b"], wd["x_proj_w"], R)
+    torch.cuda.synchronize()
+    assert set(got) == {"u", "dt_lr", "Bs", "Cs"}
+    for k in ("u", "dt_lr", "Bs", "Cs"):
+        assert tuple(got[k].shape) == ref[k].shape, k
+        assert_parity(to_numpy_f64(got[k]), ref[k], wl.dtype, f"{what} {k}", tol=TOL_FRONT)
+
+
+PROJ_LR_SHAPES = [  # B, D, H, W, N, K, dtype, R, KW
+    (2, 70, 5, 27, 4, 4, "f32", 3, 4),         # one step per lane
+    (2, 70, 5, 27, 4, 4, "bf16", 3, 4),
+    (2, 130, 6, 10, 16, 4, "bf16", 1, 4),      # four steps per lane, ragged tile
+    (2, 70, 6, 10, 4, 4, "f32", 4, 4),
+    (1, 40, 12, 20, 16, 4, "f32", 64, 4),      # 96 x_proj rows, 64 dt rows
+    (1, 40, 6, 13, 8, 4, "bf16", 2, 8),
+    (2, 48, 1, 197, 16, 2, "bf16", 1, 4),      # Vim paths
+    (2, 48, 1, 196, 16, 2, "f32", 2, 4),
+]
+
+
+@pytest.mark.parametrize("case", PROJ_LR_SHAPES,
+                         ids=lambda c: "B{}D{}_{}x{}_N{}_K{}_{}_R{}_KW{}".format(*c))
+def test_project_lr_small(orc, case):
+    B, D, H, W, N, K, dt, R, KW = case
+    check_project_lr(orc, workloads.custom(B, D, H, W, N, K, dt), R, KW, seed=36)
+
+
+def run_routes_lr(u_dev, lr_dev, dtw_dev, dev, wl, z=None, zoh=False):
+    import selective_scan_ss2d_amd as ss
+    rest = [dev[k] for k in ARGS[1:]]
+    if wl.K == 4:
+        return ss.ss2d_forward_routes_lr(u_dev, lr_dev, dtw_dev, *rest, wl.H, wl.W, z=z,
+                                         zoh=zoh)
+    return ss.ss1d_bidir_forward_routes_lr(u_dev, lr_dev, dtw_dev, *rest, z=z, zoh=zoh)
+
+
+def check_routes_lr(orc, wl, R, gate, zoh, seed=0, **overrides):
+    import torch
+    what = (f"routes_lr B{wl.B} D{wl.D} {wl.H}x{wl.W} N{wl.N} K{wl.K} R{R} {wl.dtype} "
+            f"gate={gate} zoh={zoh} {overrides}")
+    log(f"case {what}")
+    inp = workloads.make_inputs(wl, seed=seed, a_log="random")
+    ri = workloads.make_route_inputs(wl, seed)
+    lr = workloads.make_lowrank_dt(wl, seed, R=R)
+    g = workloads.make_gate(wl, seed) if gate else None
+    ref = orc.forward_routes_lr(wl.K, ri["u"], lr["dt_lr"], lr["dt_w"],
+                                *[inp[k] for k in ARGS[1:]], wl.H, wl.W,
+                                z=g["z"] if gate else None, zoh=zoh)
+    dev = to_device(inp, wl)
+    z = _dev(g["z"], wl.dtype) if gate else None
+    dtw = torch.from_numpy(lr["dt_w"]).to("cuda:0")
+    with env_override(**overrides):
+        y = run_routes_lr(route_inputs_to_device(ri, wl), _dev(lr["dt_lr"], wl.dtype), dtw,
+                          dev, wl, z=z, zoh=zoh)
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(y), ref.reshape(y.shape), wl.dtype, what)
+
+
+ROUTE_LR_SHAPES = [  # B, D, H, W, N, K, dtype, R
+    (1, 8, 8, 8, 4, 4, "f32", 1),
+    (2, 70, 5, 7, 16, 4, "f32", 2),
+    (2, 70, 5, 7, 16, 4, "bf16", 4),
+    (2, 130, 24, 24, 16, 4, "bf16", 1),
+    (1, 40, 9, 11, 32, 4, "f32", 4),           # the largest state with the most dt rows
+    (1, 40, 9, 11, 1, 4, "bf16", 3),
+    (3, 100, 1, 197, 16, 2, "bf16", 1),
+    (2, 64, 1, 320, 16, 2, "f32", 3),
+]
+
+
+@pytest.mark.parametrize("gate,zoh", [(False, False), (True, True)], ids=["plain", "gate_zoh"])
+@pytest.mark.parametrize("case", ROUTE_LR_SHAPES,
+                         ids=lambda c: "B{}D{}_{}x{}_N{}_K{}_{}_R{}".format(*c))
+def test_routes_lr_small(orc, case, gate, zoh):
+    B, D, H, W, N, K, dt, R = case
+    check_routes_lr(orc, workloads.custom(B, D, H, W, N, K, dt), R, gate, zoh, seed=37)
+
+
+@pytest.mark.parametrize("var", [dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
+                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96),
+                                 dict(SS2D_SPLIT=2, SS2D_CHUNK_LEN=0)],
+                         ids=["S1_C64", "S4_C96", "S2_C0"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_routes_lr_launch_variants(orc, var, dt):
+    """Chunked passes and the lane splits with dt_proj folded into the scan."""
+    check_routes_lr(orc, workloads.custom(2, 72, 13, 11, 16, 4, dt), 2, True, False, seed=38,
+                    **var)
+
+
+@pytest.mark.parametrize("K,H,W,dt", [(4, 9, 14, "f32"), (2, 1, 130, "f32"),
+                                      (4, 12, 12, "bf16")])
+def test_chain_lr(orc, K, H, W, dt):
+    """project_lr then forward_routes_lr on the GPU against the same chain in the oracle (its
+    front-end outputs, rounded to the data type, fed to its folded operator).  The GPU's
+    bf16 outputs and the oracle's rounding of its own can differ by one bf16 step where a
+    value falls near a rounding boundary, so the bf16 chain is held to the bf16 bar."""
+    import torch
+    import selective_scan_ss2d_amd as ss
+    wl = workloads.custom(2, 80, H, W, 16, K, dt)
+    R = 2
+    log(f"case chain_lr K={K} {H}x{W} {dt}")
+    inp = workloads.make_inputs(wl, seed=39, a_log="random")
+    w = workloads.make_front_weights(wl, 39, R=R, KW=4)
+    g = workloads.make_gate(wl, 39)
+    pr = orc.project_lr(K, inp["x"], w["conv_w"], w["conv_b"], w["x_proj_w"], R)
+    rnd = (lambda a: workloads.round_bf16(a.astype(np.float32))) if dt == "bf16" else \
+        (lambda a: a.astype(np.float32))
+    dt_w = w["dt_proj_w"]
+    ref = orc.forward_routes_lr(K, rnd(pr["u"]), rnd(pr["dt_lr"]), dt_w, inp["A_log"],
+                                rnd(pr["Bs"]), rnd(pr["Cs"]), inp["Ds"], inp["dt_bias"], H, W,
+                                z=g["z"] if dt == "f32" else workloads.round_bf16(g["z"]))
+    dev = to_device(inp, wl)
+    wd = _weights_dev(w)
+    fn = ss.ss2d_project_lr if K == 4 else ss.ss1d_bidir_project_lr
+    out = fn(dev["x"], wd["conv_w"], wd["conv_b"], wd["x_proj_w"], R)
+    dev2 = dict(dev, Bs=out["Bs"], Cs=out["Cs"])
+    y = run_routes_lr(out["u"], out["dt_lr"], wd["dt_proj_w"], dev2, wl,
+                      z=_dev(g["z"], dt))
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(y), ref.reshape(y.shape), dt, f"chain_lr K={K} {dt}",
+                  tol=TOL_FRONT)
+
+
+def test_lr_matches_unfolded_operator(orc):
+    """With dt_raw = dt_w @ dt_lr formed beforehand, the unfolded operator on the GPU and the
+    folded one agree to fp32 rounding (the sum of R products taken in another order)."""
+    import torch
+    wl = workloads.custom(2, 96, 10, 12, 16, 4, "f32")
+    log("case lr vs unfolded")
+    inp = workloads.make_inputs(wl, seed=40, a_log="random")
+    ri = workloads.make_route_inputs(wl, 40)
+    lr = workloads.make_lowrank_dt(wl, 40, R=4)
+    dt_raw = np.einsum("kdr,bkrl->bkdl", lr["dt_w"].astype(np.float64),
+                       lr["dt_lr"].astype(np.float64)).astype(np.float32)
+    dev = to_device(inp, wl)
+    u = route_inputs_to_device(ri, wl)
+    y_lr = run_routes_lr(u, _dev(lr["dt_lr"], "f32"), torch.from_numpy(lr["dt_w"]).cuda(), dev,
+                         wl)
+    y = run_routes(u, dict(dev, dt_raw=_dev(dt_raw, "f32")), wl)
+    torch.cuda.synchronize()
+    assert_parity(to_numpy_f64(y_lr), to_numpy_f64(y), "f32", "lr vs unfolded")
+
+
+@pytest.mark.parametrize("name", ["vmamba_t_stage1_bf16", "vim_bidir_bf16"])
+def test_full_size_lr_sampled_images(orc, name):
+    """Both folded entry points at the full benchmark shapes (R = 1, the explainer's rank),
+    checked on two images against the oracle run on those images alone."""
+    import torch
+    import selective_scan_ss2d_amd as ss
+    wl = workloads.workload(name)
+    R = 1
+    log(f"case full size lr {name}")
+    inp = workloads.make_inputs(wl, seed=41)
+    w = workloads.make_front_weights(wl, 41, R=R, KW=4)
+    dev = to_device(inp, wl)
+    wd = _weights_dev(w)
+    fp = ss.ss2d_project_lr if wl.K == 4 else ss.ss1d_bidir_project_lr
+    out = fp(dev["x"], wd["conv_w"], wd["conv_b"], wd["x_proj_w"], R)
+    ri = workloads.make_route_inputs(wl, 41)
+    lr = workloads.make_lowrank_dt(wl, 41, R=R)
+    y = run_routes_lr(route_inputs_to_device(ri, wl), _dev(lr["dt_lr"], wl.dtype),
+                      torch.from_numpy(lr["dt_w"]).cuda(), dev, wl)
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        ref = orc.project_lr(wl.K, inp["x"][b:b + 1], w["conv_w"], w["conv_b"], w["x_proj_w"],
+                             R)
+        for k in ("u", "dt_lr", "Bs", "Cs"):
+            assert_parity(to_numpy_f64(out[k][b:b + 1]), ref[k], wl.dtype,
+                          f"full {name} b={b} project_lr {k}", tol=TOL_FRONT)
+        refy = orc.forward_routes_lr(wl.K, ri["u"][b:b + 1], lr["dt_lr"][b:b + 1], lr["dt_w"],
+                                     inp["A_log"], inp["Bs"][b:b + 1], inp["Cs"][b:b + 1],
+                                     inp["Ds"], inp["dt_bias"], wl.H, wl.W)
+        assert_parity(to_numpy_f64(y[b:b + 1]), refy.reshape(y[b:b + 1].shape), wl.dtype,
+                      f"full {name} b={b} routes_lr")

@@ -233,3 +233,24 @@ def make_route_inputs(wl: Workload, seed: int = 0) -> dict:
         out["u_bf16"] = bits
         out["u"] = bf16_bits_to_f32(bits)
     return out
+
+
+def make_lowrank_dt(wl: Workload, seed: int = 0, R: int = 1) -> dict:
+    """Seeded low-rank dt inputs for the operator with dt_proj folded in, from a generator of
+    their own: dt_w (K, D, R) uniform in (-1/sqrt(R), 1/sqrt(R)) (dt_proj's default
+    initialisation, fan_in = R) and dt_lr (B, K, R, L) ~ N(0, 3/4), so that the product
+    dt_raw = dt_w @ dt_lr has variance 1/4, the standard deviation 0.5 of the dt_raw the
+    other inputs use.  dt_w is fp32; dt_lr is bf16-exact for bf16 workloads, with its bit
+    patterns under dt_lr_bf16."""
+    rng = np.random.default_rng([seed, 0x1d])
+    K, D, L = wl.K, wl.D, wl.L
+    bound = 1.0 / np.sqrt(R)
+    dt_w = rng.uniform(-bound, bound, size=(K, D, R)).astype(np.float32)
+    dt_lr = rng.standard_normal((wl.B, K, R, L), dtype=np.float32)
+    dt_lr *= np.float32(np.sqrt(0.75))
+    out = dict(dt_w=dt_w, dt_lr=dt_lr)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(dt_lr)
+        out["dt_lr_bf16"] = bits
+        out["dt_lr"] = bf16_bits_to_f32(bits)
+    return out
