@@ -85,12 +85,14 @@ def source_hash(names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4):
+def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4,
+                     lowrank: bool = False):
     """HBM bytes per launch of the scan kernel (or, with front, of k_project for the given
-    R and KW) from the committed counter summary, if it was taken on the current kernel
-    sources; else None."""
-    f = ROOT / "profiles" / (f"traffic_front_{workload}.json" if front
-                             else f"traffic_{workload}.json")
+    R and KW, with lowrank in its variant that stores the R dt rows) from the committed
+    counter summary, if it was taken on the current kernel sources; else None."""
+    name = (f"traffic_front_lr_{workload}.json" if front and lowrank else
+            f"traffic_front_{workload}.json" if front else f"traffic_{workload}.json")
+    f = ROOT / "profiles" / name
     if not f.exists():
         return None
     try:
@@ -391,14 +393,13 @@ def main() -> int:
         roofline_front = {"bound": "hbm", "achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(p_gbps / HBM_PEAK_GBPS, 4),
                           "traffic": measured_traffic(wl.name, front=True, R=args.front_r,
-                                                      KW=args.front_kw),
+                                                      KW=args.front_kw,
+                                                      lowrank=args.front_lowrank),
                           "kernel": "k_project",
                           "kernel_avg_us": round(p_avg_s * 1e6, 1),
                           "algorithmic_bytes_per_launch": proj_bytes,
                           "R": args.front_r, "KW": args.front_kw,
                           "dt_proj_in_scan": bool(args.front_lowrank)}
-        if args.front_lowrank:  # the committed counters cover the unfolded front end
-            roofline_front["traffic"] = None
 
     cpu = None
     if not args.no_cpu_baseline:
