@@ -102,7 +102,6 @@ struct Plan {
   int split = 1;        // lanes per channel
   int num_chunks = 1;
   int chunk_len = 0;
-  bool vec = false;
   bool need_xt = false;
   size_t off_xt = 0, off_yr = 0, off_hend = 0, off_dsum = 0, off_hin = 0, bytes = 0;
 };
@@ -115,7 +114,7 @@ struct Plan {
 // chains them, and a second pass rescans each chunk from its true start state, so chunking
 // roughly doubles the work and is used only for short, long-sequence batches.
 Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
-               const void* x, const void* dt_raw, bool routes) {
+               bool routes) {
   Plan p;
   const int64_t L = H * W;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
@@ -147,9 +146,6 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
     p.chunk_len = static_cast<int>(((L + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) *
                                    ss2d::kChunkAlign);
   }
-  const int vec_elems = dtype == SS2D_F32 ? 4 : 8;
-  p.vec = (L % vec_elems == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
-          (reinterpret_cast<uintptr_t>(dt_raw) % 16 == 0);
   p.need_xt = !routes && (K == 4) && H > 1 && W > 1;
   size_t off = 0;
   if (p.need_xt) {
@@ -171,20 +167,19 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
   return p;
 }
 
-int run_scan(const ss2d::ScanArgs& a, int dtype, int split, bool vec, int mode,
-             hipStream_t st) {
+int run_scan(const ss2d::ScanArgs& a, int dtype, int split, int mode, hipStream_t st) {
   if (a.dt_lr) {
     if (a.zoh)
-      return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh_lr(a, split, vec, mode, st)
-                               : ss2d::launch_scan_bf16_zoh_lr(a, split, vec, mode, st);
-    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_lr(a, split, vec, mode, st)
-                             : ss2d::launch_scan_bf16_lr(a, split, vec, mode, st);
+      return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh_lr(a, split, mode, st)
+                               : ss2d::launch_scan_bf16_zoh_lr(a, split, mode, st);
+    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_lr(a, split, mode, st)
+                             : ss2d::launch_scan_bf16_lr(a, split, mode, st);
   }
   if (a.zoh)
-    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh(a, split, vec, mode, st)
-                             : ss2d::launch_scan_bf16_zoh(a, split, vec, mode, st);
-  return dtype == SS2D_F32 ? ss2d::launch_scan_f32(a, split, vec, mode, st)
-                           : ss2d::launch_scan_bf16(a, split, vec, mode, st);
+    return dtype == SS2D_F32 ? ss2d::launch_scan_f32_zoh(a, split, mode, st)
+                             : ss2d::launch_scan_bf16_zoh(a, split, mode, st);
+  return dtype == SS2D_F32 ? ss2d::launch_scan_f32(a, split, mode, st)
+                           : ss2d::launch_scan_bf16(a, split, mode, st);
 }
 
 // Launch one scan pass over all images, in batches that keep gridDim.z within range.
@@ -212,7 +207,7 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
     const int kind = mode == ss2d::kModeAgg    ? SS2D_KERNEL_CHUNK_AGG
                      : mode == ss2d::kModeCkpt ? SS2D_KERNEL_CHECKPOINT
                                                : SS2D_KERNEL_SCAN;
-    const int rc = timed(kind, st, [&] { return run_scan(s, dtype, p.split, p.vec, mode, st); });
+    const int rc = timed(kind, st, [&] { return run_scan(s, dtype, p.split, mode, st); });
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc));
   }
   return SS2D_OK;
@@ -270,7 +265,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   if (he != hipSuccess) return hip_fail(he);
   int rc = prepare_pool(device);
   if (rc != SS2D_OK) return rc;
-  const Plan p = make_plan(K, B, D, H, W, N, dtype, x, lr ? dt_lr : dt_raw, routes);
+  const Plan p = make_plan(K, B, D, H, W, N, dtype, routes);
   char* ws = nullptr;
   he = hipMallocAsync(reinterpret_cast<void**>(&ws), p.bytes, st);
   if (he != hipSuccess) return hip_fail(he);
@@ -456,9 +451,6 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     a.ck_tiles = int(tiles);
     Plan p;
     p.split = 4;
-    p.vec = ((L % (dtype == SS2D_F32 ? 4 : 8)) == 0) &&
-            (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
-            (reinterpret_cast<uintptr_t>(dt_raw) % 16 == 0);
     rc = scan_pass(a, dtype, p, ss2d::kModeCkpt, e, st);
   }
   // Adjoint scan, in batches of images that keep gridDim.z in range.

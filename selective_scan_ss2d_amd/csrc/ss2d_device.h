@@ -193,15 +193,15 @@ constexpr int kProjMaxM = 96;   // most x_proj rows (R + 2N) supported
 
 // Host-side launchers (defined in the .hip files).  The _zoh scan launchers run the
 // zero-order-hold discretisation of B (a.zoh set), the others delta * B.
-int launch_scan_f32(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_bf16(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_f32_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_bf16_zoh(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_f32(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_bf16(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_f32_zoh(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_bf16_zoh(const ScanArgs& a, int split, int mode, hipStream_t st);
 // dt_proj folded in (a.dt_lr set): forward modes only
-int launch_scan_f32_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_bf16_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_f32_zoh_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
-int launch_scan_bf16_zoh_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st);
+int launch_scan_f32_lr(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_bf16_lr(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_f32_zoh_lr(const ScanArgs& a, int split, int mode, hipStream_t st);
+int launch_scan_bf16_zoh_lr(const ScanArgs& a, int split, int mode, hipStream_t st);
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st);
 int launch_carry(const ScanArgs& a, hipStream_t st);

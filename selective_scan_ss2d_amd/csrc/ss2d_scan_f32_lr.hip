@@ -2,7 +2,7 @@
 #include "ss2d_scan.inc"
 
 namespace ss2d {
-int launch_scan_f32_lr(const ScanArgs& a, int split, bool vec, int mode, hipStream_t st) {
-  return launch_scan_t<float, false, true>(a, split, vec, mode, st);
+int launch_scan_f32_lr(const ScanArgs& a, int split, int mode, hipStream_t st) {
+  return launch_scan_t<float, false, true>(a, split, mode, st);
 }
 }  // namespace ss2d
