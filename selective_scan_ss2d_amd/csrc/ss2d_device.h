@@ -25,11 +25,10 @@ template <> struct Elem<uint16_t> {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
   }
   static __device__ __forceinline__ float load(const uint16_t* p) { return to_f32(*p); }
-  // fp32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+  // fp32 -> bfloat16 by the hardware conversion (v_cvt_pk_bf16_f32): round to nearest
+  // even; NaN stays a NaN.
   static __device__ __forceinline__ uint16_t from_f32(float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
   }
 };
 
