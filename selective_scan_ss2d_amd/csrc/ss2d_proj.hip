@@ -23,6 +23,8 @@
 // dt_proj (R fused multiply-adds per output, weights from scalar registers) writes dt_raw.
 // The kernel is bound by HBM traffic: per step and route it reads D inputs (x, once per
 // route) and writes 2D + 2N outputs.
+#include <type_traits>
+
 #include "ss2d_device.h"
 
 namespace ss2d {
@@ -95,27 +97,39 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 template <typename T> struct Quad;
 template <> struct Quad<uint16_t> {
+  // Byte selectors of v_perm_b32 that widen element k of the loaded 8 bytes to fp32 (its
+  // two bytes on top, zero bytes below), for x[j] = element j, or 3 - j with rev.
+  struct Sel {
+    uint32_t s[4];
+    __device__ __forceinline__ explicit Sel(bool rev) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k = rev ? 3 - j : j;
+        s[j] = ((2 * k + 1) << 24) | ((2 * k) << 16) | 0x0c0cu;
+      }
+    }
+  };
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                              uint32_t soff, bool rev, float (&x)[4]) {
+                                              uint32_t soff, const Sel& sel, float (&x)[4]) {
     const v2u p = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    const float a0 = __uint_as_float(p.x << 16), a1 = __uint_as_float(p.x & 0xffff0000u);
-    const float a2 = __uint_as_float(p.y << 16), a3 = __uint_as_float(p.y & 0xffff0000u);
-    x[0] = rev ? a3 : a0;
-    x[1] = rev ? a2 : a1;
-    x[2] = rev ? a1 : a2;
-    x[3] = rev ? a0 : a3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(__builtin_amdgcn_perm(p.y, p.x, sel.s[j]));
   }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff, const float (&u)[4]);
 };
 template <> struct Quad<float> {
+  struct Sel {
+    bool rev;
+    __device__ __forceinline__ explicit Sel(bool r) : rev(r) {}
+  };
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                              uint32_t soff, bool rev, float (&x)[4]) {
+                                              uint32_t soff, const Sel& sel, float (&x)[4]) {
     const v4u p = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     const float a[4] = {__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z),
                         __uint_as_float(p.w)};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = rev ? a[3 - j] : a[j];
+    for (int j = 0; j < 4; ++j) x[j] = sel.rev ? a[3 - j] : a[j];
   }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff, const float (&u)[4]) {
@@ -477,7 +491,9 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
 // row takes the halo), then 16 FMAs for the four outputs.
 constexpr int kRowShr1 = 0x111;  // DPP row_shr:1
 
-template <typename T>
+// MTC: 16-row tiles of x_proj outputs (R + 2N rounded up to 16, over 16), fixed at compile
+// time so that the accumulators stay in place.
+template <typename T, int MTC>
 __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   using Ops = ProjOps<T>;
   using E = typename Ops::E;
@@ -490,7 +506,9 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   const int k = blockIdx.y, b = blockIdx.z;
   const int L = a.L, D = a.D, N = a.N, R = a.R;
   const int M = R + 2 * N;
-  const int MT = (M + 15) / 16, MP = 16 * MT;
+  constexpr int MT = MTC;
+  const int MP = 16 * MT;
+  (void)M;
   E* sU = reinterpret_cast<E*>(smem);
   E* sW = sU + Ops::elems(kTT);
   float (*sCW)[kCW] = reinterpret_cast<float (*)[kCW]>(sW + Ops::elems(MP));
@@ -519,31 +537,41 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   const __amdgpu_buffer_rsrc_t u_r =
       make_rsrc(static_cast<T*>(a.u) + bk * D * L, uint32_t(D) * row_bytes);
 
-  v4f acc[kMT];
+  v4f acc[MT];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < MT; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   // four steps of the wave's 16 channels of a chunk (lane group G: channels 4 G .. 4 G + 3),
-  // and the three steps before the tile
-  float xv[4][4], hv[4][3];
-  auto load_rows = [&](int d0) {
+  // and the three steps before the tile (zero before the first step: t0 is a multiple of
+  // 64, so either all three exist or none)
+  // Two register sets, used in turn: a chunk is processed from one while the next chunk's
+  // rows load into the other.
+  float xA[4][4], hA[4][3], xB[4][4], hB[4][3];
+  const typename Quad<T>::Sel qsel(rev);
+  auto load_rows = [&](int d0, float (&xv)[4][4], float (&hv)[4][3]) {
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
       const int rb = min(d0 + wave * 16 + 4 * G, D - 1);
       const uint32_t rel = uint32_t(min(d0 + wave * 16 + 4 * G + sr, D - 1) - rb) * row_bytes;
       const uint32_t so = uint32_t(rb) * row_bytes;
-      Quad<T>::load(x_r, rel + xo4, so, rev, xv[G]);
+      Quad<T>::load(x_r, rel + xo4, so, qsel, xv[G]);
 #pragma unroll
       for (int sh = 1; sh < 4; ++sh) {
         const int s = max(t0 - sh, 0);
-        const float h = buf_load_at<T>(x_r, rel + uint32_t(rev ? L - 1 - s : s) * sizeof(T), so);
-        hv[G][sh - 1] = t0 - sh >= 0 ? h : 0.0f;
+        hv[G][sh - 1] = buf_load_at<T>(x_r, rel + uint32_t(rev ? L - 1 - s : s) * sizeof(T), so);
       }
     }
+    if (t0 == 0) {
+#pragma unroll
+      for (int G = 0; G < 4; ++G)
+#pragma unroll
+        for (int sh = 0; sh < 3; ++sh) hv[G][sh] = 0.0f;
+    }
   };
-  load_rows(0);
+  load_rows(0, xA, hA);
 
-  for (int d0 = 0; d0 < D; d0 += kDC) {
+  auto chunk = [&](int d0, const float (&xc)[4][4], const float (&hc)[4][3],
+                   float (&xn)[4][4], float (&hn)[4][3]) {
     // ---- 1. this chunk's weight image to LDS (its rows were loaded a chunk ahead) --------
     __syncthreads();  // the previous chunk's products have read sW
     {
@@ -557,15 +585,7 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
       __builtin_amdgcn_s_waitcnt(0);  // the image and this chunk's rows have arrived
     }
     __syncthreads();
-    float xc[4][4], hc[4][3];
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xc[G][j] = xv[G][j];
-#pragma unroll
-      for (int j = 0; j < 3; ++j) hc[G][j] = hv[G][j];
-    }
-    if (d0 + kDC < D) load_rows(d0 + kDC);  // before this chunk's stores
+    if (d0 + kDC < D) load_rows(d0 + kDC, xn, hn);  // before this chunk's stores
 
     // ---- 2. conv + SiLU, four outputs per lane and group ---------------------------------
 #pragma unroll
@@ -588,7 +608,11 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
           fmaf(w.w, x[0], fmaf(w.z, x[1], fmaf(w.y, x[2], fmaf(w.x, x[3], bias))))};
       float u[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = d < D ? silu_f32(cv[j]) : 0.0f;
+      for (int j = 0; j < 4; ++j) u[j] = silu_f32(cv[j]);
+      if (d0 + kDC > D) {  // a ragged last chunk: channels past D enter x_proj as zeros
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = d < D ? u[j] : 0.0f;
+      }
       const int rb = min(d0 + wave * 16 + 4 * G, D - 1);
       Quad<T>::store(u_r, (d < D && ok4) ? uint32_t(sr) * row_bytes + st4 : kDrop,
                      uint32_t(rb) * row_bytes, u);
@@ -602,22 +626,23 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
 #pragma unroll 1
     for (int kk = 0; kk < kDC / KS; ++kk) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        if (mt < MT)
-          acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP, urow + kk * KS,
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP, urow + kk * KS,
                                  kTT, acc[mt]);
       }
     }
+  };
+  for (int d0 = 0; d0 < D; d0 += 2 * kDC) {
+    chunk(d0, xA, hA, xB, hB);
+    if (d0 + kDC < D) chunk(d0 + kDC, xB, hB, xA, hA);
   }
   __syncthreads();  // the last products have read sU and sW
 
   // ---- 4. x_proj outputs to LDS: lane holds rows 4 (l / 16) + j of column l % 16 -------
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    if (mt < MT) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sXd[mt * 16 + 4 * g + j][wave * 16 + n16] = acc[mt][j];
-    }
+    for (int j = 0; j < 4; ++j) sXd[mt * 16 + 4 * g + j][wave * 16 + n16] = acc[mt][j];
   }
   __syncthreads();
 
@@ -703,10 +728,22 @@ int launch_project(const ProjArgs& a0, int dtype, hipStream_t st) {
   const dim3 grid((a.L + kTT - 1) / kTT, a.K, a.B);
   const bool kw4 = a.KW == 4;
   if (kw4 && a.L % 4 == 0) {
-    if (dtype == 0)
-      k_project4<float><<<grid, 256, proj_lds_bytes<float>(MP), st>>>(a);
-    else
-      k_project4<uint16_t><<<grid, 256, proj_lds_bytes<uint16_t>(MP), st>>>(a);
+    const size_t lds = dtype == 0 ? proj_lds_bytes<float>(MP) : proj_lds_bytes<uint16_t>(MP);
+    auto launch4 = [&](auto mt_tag) {
+      constexpr int MTC = decltype(mt_tag)::value;
+      if (dtype == 0)
+        k_project4<float, MTC><<<grid, 256, lds, st>>>(a);
+      else
+        k_project4<uint16_t, MTC><<<grid, 256, lds, st>>>(a);
+    };
+    switch (MP / 16) {
+      case 1: launch4(std::integral_constant<int, 1>{}); break;
+      case 2: launch4(std::integral_constant<int, 2>{}); break;
+      case 3: launch4(std::integral_constant<int, 3>{}); break;
+      case 4: launch4(std::integral_constant<int, 4>{}); break;
+      case 5: launch4(std::integral_constant<int, 5>{}); break;
+      default: launch4(std::integral_constant<int, kMT>{}); break;
+    }
   } else if (dtype == 0) {
     if (kw4)
       k_project<float, 4><<<grid, 256, proj_lds_bytes<float>(MP), st>>>(a);
