@@ -275,6 +275,14 @@ __device__ __forceinline__ float4 load4_stream(const float* p) {
   const v4f_stream v = __builtin_nontemporal_load(reinterpret_cast<const v4f_stream*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
 }
+// The same for a 4-byte aligned address (served at any alignment in the chip's unaligned
+// access mode).
+typedef float v4f_stream_any __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ float4 load4_stream_any(const float* p) {
+  const v4f_stream_any v =
+      __builtin_nontemporal_load(reinterpret_cast<const v4f_stream_any*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 template <typename T, bool GATE>
 __global__ void __launch_bounds__(256)
@@ -376,15 +384,30 @@ k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restric
   const int64_t run = static_cast<int64_t>(D) * L;
   const int64_t e = 4 * (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
   if (e >= run) return;
+  // route 1's values of positions e .. e + 3 (reversed within each row): one 16-byte load
+  // of any alignment, reversed, when the four lie in one row; else one by one
+  const int64_t d0 = e / L;
+  const int l0 = static_cast<int>(e - d0 * L);
+  const bool one_row = l0 + 3 < L;
+  int64_t src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool wrap = l0 + i >= L;
+    const int64_t d = wrap ? d0 + 1 : d0;
+    const int l = wrap ? l0 + i - L : l0 + i;
+    src[i] = d * L + (L - 1 - l);
+  }
   for (int64_t b = blockIdx.y; b < images; b += gridDim.y) {
     const float* y0 = yr + b * 2 * run;
     const float* y1 = y0 + run;
     const float4 a = load4_stream(y0 + e);
     float r[4];
+    if (one_row) {
+      const float4 v = load4_stream_any(y1 + src[3]);
+      r[0] = v.w; r[1] = v.z; r[2] = v.y; r[3] = v.x;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t d = (e + i) / L, l = (e + i) - d * L;
-      r[i] = __builtin_nontemporal_load(y1 + d * L + (L - 1 - l));
+      for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load(y1 + src[i]);
     }
     float v0 = a.x + r[0], v1 = a.y + r[1], v2 = a.z + r[2], v3 = a.w + r[3];
     if constexpr (GATE) {
