@@ -284,40 +284,80 @@ __device__ __forceinline__ float4 load4_stream_any(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resources over one plane (L elements): 32-bit per-lane offsets instead of 64-bit
+// addresses keep the kernel's registers low; loads use the nontemporal policy (the route
+// outputs are read exactly once).
+constexpr uint32_t kMergeRsrc = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kNt = 2;                       // cache policy: nontemporal
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kMergeRsrc);
+}
+__device__ __forceinline__ float4 rsrc_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+// four gate values (the data type) at element offset e of a plane
+template <typename T> struct Gate4;
+template <> struct Gate4<float> {
+  float4 r;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t e) {
+    r = rsrc_load4(rs, e * 4);
+  }
+  __device__ __forceinline__ float4 get() const { return r; }
+};
+template <> struct Gate4<uint16_t> {
+  uint2 r;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t e) {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, e * 2, 0, kNt);
+    r = make_uint2(v.x, v.y);
+  }
+  __device__ __forceinline__ float4 get() const {
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+};
+
 template <typename T, bool GATE>
 __global__ void __launch_bounds__(256)
 k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D,
              int H, int W, int64_t planes) {
-  // A block covers a 64 x 64 tile (h x w) of one plane; every thread keeps four float4
-  // loads of each route in flight (the row-route loads are issued before the barrier).
+  // A block covers a 64 x 64 tile (h x w) of one plane; every thread keeps four 16-byte
+  // loads of each route (and, with the gate, its four gate loads) in flight before the
+  // barrier.
   constexpr int TS = 64;
   __shared__ float t2[TS][TS + 1];
   __shared__ float t3[TS][TS + 1];
   const int tid = threadIdx.x;
   const int w0 = blockIdx.x * TS, h0 = blockIdx.y * TS;
   const int64_t L = static_cast<int64_t>(H) * W;
+  const uint32_t pbytes = static_cast<uint32_t>(L * 4);  // L < 2^30
   const int lh = 4 * (tid % 16), lw = tid / 16;     // load phase: (w0 + lw + 16 j, h0 + lh)
   const int ow = 4 * (tid % 16), oh = tid / 16;     // output phase: (h0 + oh + 16 j, w0 + ow)
   for (int64_t p = blockIdx.z; p < planes; p += gridDim.z) {
     const int64_t b = p / D, d = p % D;
-    const float* y0 = yr + ((b * 4 + 0) * D + d) * L;
-    const float* y1 = yr + ((b * 4 + 1) * D + d) * L;
-    const float* y2 = yr + ((b * 4 + 2) * D + d) * L;
-    const float* y3 = yr + ((b * 4 + 3) * D + d) * L;
+    const __amdgpu_buffer_rsrc_t y0 = plane_rsrc(yr + ((b * 4 + 0) * D + d) * L, pbytes);
+    const __amdgpu_buffer_rsrc_t y1 = plane_rsrc(yr + ((b * 4 + 1) * D + d) * L, pbytes);
+    const __amdgpu_buffer_rsrc_t y2 = plane_rsrc(yr + ((b * 4 + 2) * D + d) * L, pbytes);
+    const __amdgpu_buffer_rsrc_t y3 = plane_rsrc(yr + ((b * 4 + 3) * D + d) * L, pbytes);
     float4 c2[4], c3[4], r0[4], r1[4];
+    Gate4<T> g[GATE ? 4 : 1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int w = w0 + lw + 16 * j, h = h0 + lh;
       if (w < W && h < H) {
-        const int64_t st = static_cast<int64_t>(w) * H + h;  // steps st .. st+3
-        c2[j] = load4_stream(y2 + st);
-        c3[j] = load4_stream(y3 + (L - 4 - st));
+        const uint32_t st = static_cast<uint32_t>(w * H + h);  // steps st .. st+3
+        c2[j] = rsrc_load4(y2, st * 4);
+        c3[j] = rsrc_load4(y3, static_cast<uint32_t>(L - 4 - st) * 4);
       }
       const int hh = h0 + oh + 16 * j, ww = w0 + ow;
       if (hh < H && ww < W) {
-        const int64_t l = static_cast<int64_t>(hh) * W + ww;  // positions l .. l+3
-        r0[j] = load4_stream(y0 + l);
-        r1[j] = load4_stream(y1 + (L - 4 - l));
+        const uint32_t l = static_cast<uint32_t>(hh * W + ww);  // positions l .. l+3
+        r0[j] = rsrc_load4(y0, l * 4);
+        r1[j] = rsrc_load4(y1, static_cast<uint32_t>(L - 4 - l) * 4);
+        if constexpr (GATE) g[j].load(plane_rsrc(z + p * L, pbytes / 4 * sizeof(T)), l);
       }
     }
 #pragma unroll
@@ -342,9 +382,7 @@ k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restric
         v0 += t2[ow + 0][ht]; v1 += t2[ow + 1][ht]; v2 += t2[ow + 2][ht]; v3 += t2[ow + 3][ht];
         v0 += t3[ow + 0][ht]; v1 += t3[ow + 1][ht]; v2 += t3[ow + 2][ht]; v3 += t3[ow + 3][ht];
         if constexpr (GATE) {
-          In4<T> g;
-          g.load(z + p * L + l);
-          const float4 gz = g.get();
+          const float4 gz = g[j].get();
           v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
         }
         Out4<T>::store(y + p * L + l, v0, v1, v2, v3);
