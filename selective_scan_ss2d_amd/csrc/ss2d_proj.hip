@@ -169,13 +169,24 @@ template <> struct ProjOps<uint16_t> {
   static constexpr int kK = 32;          // channels per product
   static constexpr int kRowE = kDC + 8;  // 144-byte rows
   static constexpr int elems(int rows) { return 2 * rows * kRowE; }
+  // Position of channel col in row `row` of the u operand: its 8-channel (16-byte) group is
+  // XORed with bits 2..4 of the row.  The column writes of the four-steps-per-lane kernel
+  // touch rows 4 apart, which would otherwise fall on two LDS bank groups (8-way
+  // conflicts); the product's 16-byte reads stay whole.
+  static __device__ __forceinline__ int ucol(int row, int col) {
+    return (((col >> 3) ^ ((row >> 2) & 7)) << 3) | (col & 7);
+  }
+  static __device__ __forceinline__ const E* u_at(const E* base, int row, int col) {
+    return base + row * kRowE + ucol(row, col);
+  }
   static __device__ __forceinline__ void put4(E* base, int rows, int row, int col,
                                               const float (&v)[4]) {
     uint32_t hi[2], lo[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) hi[j] = split2(v[2 * j], v[2 * j + 1], lo[j]);
-    *reinterpret_cast<uint2*>(&base[row * kRowE + col]) = make_uint2(hi[0], hi[1]);
-    *reinterpret_cast<uint2*>(&base[(rows + row) * kRowE + col]) = make_uint2(lo[0], lo[1]);
+    const int c = ucol(row, col);
+    *reinterpret_cast<uint2*>(&base[row * kRowE + c]) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2*>(&base[(rows + row) * kRowE + c]) = make_uint2(lo[0], lo[1]);
   }
   // v[j] to column col of rows row0 + j (four steps of one channel)
   static __device__ __forceinline__ void put_col4(E* base, int rows, int row0, int col,
@@ -186,8 +197,9 @@ template <> struct ProjOps<uint16_t> {
     const uint32_t ls[4] = {lo01 & 0xffffu, lo01 >> 16, lo23 & 0xffffu, lo23 >> 16};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      base[(row0 + j) * kRowE + col] = static_cast<E>(hs[j]);
-      base[(rows + row0 + j) * kRowE + col] = static_cast<E>(ls[j]);
+      const int c = ucol(row0 + j, col);
+      base[(row0 + j) * kRowE + c] = static_cast<E>(hs[j]);
+      base[(rows + row0 + j) * kRowE + c] = static_cast<E>(ls[j]);
     }
   }
   static __device__ __forceinline__ v4f product(const E* w, int wrows, const E* u, int urows,
@@ -208,14 +220,23 @@ template <> struct ProjOps<float> {
   static constexpr int kK = 4;
   static constexpr int kRowE = kDC + 4;  // 272-byte rows
   static constexpr int elems(int rows) { return rows * kRowE; }
+  // Position of channel col in row `row` of the u operand: bits 2..4 of the column XORed
+  // with bits 2..4 of the row (the same bank spreading as for bfloat16 operands).
+  static __device__ __forceinline__ int ucol(int row, int col) {
+    return col ^ (((row >> 2) & 7) << 2);
+  }
+  static __device__ __forceinline__ const E* u_at(const E* base, int row, int col) {
+    return base + row * kRowE + ucol(row, col);
+  }
   static __device__ __forceinline__ void put4(E* base, int, int row, int col,
                                               const float (&v)[4]) {
-    *reinterpret_cast<float4*>(&base[row * kRowE + col]) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(&base[row * kRowE + ucol(row, col)]) =
+        make_float4(v[0], v[1], v[2], v[3]);
   }
   static __device__ __forceinline__ void put_col4(E* base, int, int row0, int col,
                                                   const float (&v)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) base[(row0 + j) * kRowE + col] = v[j];
+    for (int j = 0; j < 4; ++j) base[(row0 + j) * kRowE + ucol(row0 + j, col)] = v[j];
   }
   static __device__ __forceinline__ v4f product(const E* w, int, const E* u, int, v4f acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(w[0], u[0], acc, 0, 0, 0);
@@ -410,15 +431,15 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
     __syncthreads();
 
     // ---- 3. x_proj on the matrix cores: wave w owns steps 16 w .. 16 w + 15 --------------
-    const E* urow = sU + (wave * 16 + n16) * Ops::kRowE + CJ * g;
+    const int urow = wave * 16 + n16;  // this lane's step in the u operand
     const E* wrow = sW + n16 * Ops::kRowE + CJ * g;
 #pragma unroll 1
     for (int kk = 0; kk < kDC / KS; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         if (mt < MT)
-          acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP, urow + kk * KS,
-                                 kTT, acc[mt]);
+          acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP,
+                                 Ops::u_at(sU, urow, kk * KS + CJ * g), kTT, acc[mt]);
       }
     }
   }
@@ -621,14 +642,14 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
     __syncthreads();
 
     // ---- 3. x_proj on the matrix cores: wave w owns steps 16 w .. 16 w + 15 --------------
-    const E* urow = sU + (wave * 16 + n16) * Ops::kRowE + CJ * g;
+    const int urow = wave * 16 + n16;  // this lane's step in the u operand
     const E* wrow = sW + n16 * Ops::kRowE + CJ * g;
 #pragma unroll 1
     for (int kk = 0; kk < kDC / KS; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP, urow + kk * KS,
-                                 kTT, acc[mt]);
+        acc[mt] = Ops::product(wrow + mt * 16 * Ops::kRowE + kk * KS, MP,
+                               Ops::u_at(sU, urow, kk * KS + CJ * g), kTT, acc[mt]);
       }
     }
   };
