@@ -659,12 +659,28 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   }
   __syncthreads();  // the last products have read sU and sW
 
+  // dt_proj's weights of this route (D x R fp32) go memory -> LDS behind the x_proj outputs
+  // when they fit there (no registers held, one wave instruction per 64 floats); otherwise
+  // they are read from memory in the loop below.
+  const int DR = D * R;
+  float* sWdt = &sXd[0][0] + MP * kTT;
+  const bool w_lds = a.dt_lr == nullptr &&
+                     DR <= (int(Ops::elems(kTT) * sizeof(E)) + img_bytes) / 4 - MP * kTT;
+  const float* wdt = a.dt_lr ? nullptr : a.dt_proj_w + int64_t(k) * D * R;
+  if (w_lds) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    for (int e0 = wave * kWave; e0 < DR; e0 += 4 * kWave)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(wdt + min(e0 + lane, DR - 1)),
+                                       (lds_void*)(sWdt + e0), 4, 0, 0);
+  }
+
   // ---- 4. x_proj outputs to LDS: lane holds rows 4 (l / 16) + j of column l % 16 -------
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) sXd[mt * 16 + 4 * g + j][wave * 16 + n16] = acc[mt][j];
   }
+  if (w_lds) __builtin_amdgcn_s_waitcnt(0);  // this wave's weight copies have landed
   __syncthreads();
 
   // ---- 5. dt_proj: wave w covers channels 16 w .. 16 w + 15 of each chunk of 64, four
@@ -682,32 +698,41 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   const __amdgpu_buffer_rsrc_t dt_r =
       make_rsrc(a.dt_lr ? nullptr : static_cast<T*>(a.dt_raw) + bk * D * L,
                 a.dt_lr ? 0u : uint32_t(D) * row_bytes);
-  const float* wdt = a.dt_lr ? nullptr : a.dt_proj_w + int64_t(k) * D * R;
+  // the weights from LDS or from memory: one copy of the loop for each (w_lds is the same
+  // for the whole block), so every load has a known address space
+  auto dt_proj = [&](auto wsrc) {
 #pragma unroll 1
-  for (int dc = wave * 16; a.dt_lr == nullptr && dc < D; dc += kDC) {
-    float dv[4][4];
+    for (int dc = wave * 16; dc < D; dc += kDC) {
+      float dv[4][4];
 #pragma unroll
-    for (int G = 0; G < 4; ++G)
+      for (int G = 0; G < 4; ++G)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dv[G][j] = 0.0f;
-    for (int r = 0; r < R; ++r) {
-      const float4 x4 = *reinterpret_cast<const float4*>(&sXd[r][4 * q4]);
+        for (int j = 0; j < 4; ++j) dv[G][j] = 0.0f;
+      for (int r = 0; r < R; ++r) {
+        const float4 x4 = *reinterpret_cast<const float4*>(&sXd[r][4 * q4]);
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+          const int d = dc + 4 * G + sr;
+          const float w = wsrc[min(d, D - 1) * R + r];
+          dv[G][0] = fmaf(w, x4.x, dv[G][0]);
+          dv[G][1] = fmaf(w, x4.y, dv[G][1]);
+          dv[G][2] = fmaf(w, x4.z, dv[G][2]);
+          dv[G][3] = fmaf(w, x4.w, dv[G][3]);
+        }
+      }
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         const int d = dc + 4 * G + sr;
-        const float w = wdt[int64_t(min(d, D - 1)) * R + r];
-        dv[G][0] = fmaf(w, x4.x, dv[G][0]);
-        dv[G][1] = fmaf(w, x4.y, dv[G][1]);
-        dv[G][2] = fmaf(w, x4.z, dv[G][2]);
-        dv[G][3] = fmaf(w, x4.w, dv[G][3]);
+        const uint32_t off = (d < D && ok4) ? uint32_t(d) * row_bytes + st4 : kDrop;
+        Quad<T>::store(dt_r, off, 0, dv[G]);
       }
     }
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      const int d = dc + 4 * G + sr;
-      const uint32_t off = (d < D && ok4) ? uint32_t(d) * row_bytes + st4 : kDrop;
-      Quad<T>::store(dt_r, off, 0, dv[G]);
-    }
+  };
+  if (w_lds) {
+    typedef const __attribute__((address_space(3))) float lds_float;
+    dt_proj((lds_float*)sWdt);
+  } else if (a.dt_lr == nullptr) {
+    dt_proj(wdt);
   }
   const __amdgpu_buffer_rsrc_t b_r =
       make_rsrc(static_cast<T*>(a.Bs) + bk * N * L, uint32_t(N) * row_bytes);

@@ -75,6 +75,7 @@ PROJ_SHAPES = [  # B, D, H, W, N, K, dtype, R, KW
     (2, 70, 6, 10, 4, 4, "bf16", 3, 4),
     (1, 130, 12, 20, 16, 4, "bf16", 1, 4),     # four tiles, the last one ragged
     (1, 40, 12, 20, 16, 4, "f32", 64, 4),      # 96 x_proj rows
+    (1, 130, 12, 20, 16, 4, "bf16", 64, 4),    # dt_proj weights too large for LDS
     (2, 48, 1, 196, 16, 2, "bf16", 1, 4),      # Vim paths without the class token
     (1, 24, 4, 1, 4, 4, "f32", 2, 4),          # four steps in all
 ]
