@@ -97,8 +97,9 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 template <typename T> struct Quad;
 template <> struct Quad<uint16_t> {
-  // Byte selectors of v_perm_b32 that widen element k of the loaded 8 bytes to fp32 (its
-  // two bytes on top, zero bytes below), for x[j] = element j, or 3 - j with rev.
+  // Byte selectors of v_perm_b32 that widen element k[j] of the loaded 8 bytes to fp32 (its
+  // two bytes on top, zero bytes below) as x[j]: k[j] = j, or 3 - j with rev, for a whole
+  // quad; any 0..3 per lane at the end of a row whose length is not a multiple of 4.
   struct Sel {
     uint32_t s[4];
     __device__ __forceinline__ explicit Sel(bool rev) {
@@ -107,6 +108,11 @@ template <> struct Quad<uint16_t> {
         const uint32_t k = rev ? 3 - j : j;
         s[j] = ((2 * k + 1) << 24) | ((2 * k) << 16) | 0x0c0cu;
       }
+    }
+    __device__ __forceinline__ explicit Sel(const int (&k)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s[j] = ((2u * k[j] + 1) << 24) | ((2u * k[j]) << 16) | 0x0c0cu;
     }
   };
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
@@ -119,9 +125,13 @@ template <> struct Quad<uint16_t> {
                                                uint32_t soff, const float (&u)[4]);
 };
 template <> struct Quad<float> {
+  // x[j] = element j, or 3 - j with rev (whole quads); element k[j] per lane otherwise
   struct Sel {
-    bool rev;
-    __device__ __forceinline__ explicit Sel(bool r) : rev(r) {}
+    bool rev, any;
+    int k[4];
+    __device__ __forceinline__ explicit Sel(bool r) : rev(r), any(false), k{0, 1, 2, 3} {}
+    __device__ __forceinline__ explicit Sel(const int (&kk)[4])
+        : rev(false), any(true), k{kk[0], kk[1], kk[2], kk[3]} {}
   };
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff, const Sel& sel, float (&x)[4]) {
@@ -129,7 +139,14 @@ template <> struct Quad<float> {
     const float a[4] = {__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z),
                         __uint_as_float(p.w)};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = sel.rev ? a[3 - j] : a[j];
+    for (int j = 0; j < 4; ++j) {
+      if (sel.any) {
+        const int k = sel.k[j];
+        x[j] = k == 0 ? a[0] : k == 1 ? a[1] : k == 2 ? a[2] : a[3];
+      } else {
+        x[j] = sel.rev ? a[3 - j] : a[j];
+      }
+    }
   }
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff, const float (&u)[4]) {
@@ -513,8 +530,11 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
 constexpr int kRowShr1 = 0x111;  // DPP row_shr:1
 
 // MTC: 16-row tiles of x_proj outputs (R + 2N rounded up to 16, over 16), fixed at compile
-// time so that the accumulators stay in place.
-template <typename T, int MTC>
+// time so that the accumulators stay in place.  ANYL: L is not a multiple of 4 (L >= 4),
+// so the lane holding a row's last steps has one to three of its four: it loads the last
+// four elements of the row (an in-range quad) and picks its own from them per lane, and
+// stores element by element.
+template <typename T, int MTC, bool ANYL>
 __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   using Ops = ProjOps<T>;
   using E = typename Ops::E;
@@ -544,14 +564,16 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   const int n16 = lane & 15, g = lane >> 4;
   const int sr = lane >> 4, q4 = lane & 15;  // this lane's channel of the four, step group
   const int ts = t0 + 4 * q4;                // first of this lane's four steps
-  const bool ok4 = ts < L;                   // L % 4 == 0: all four steps exist, or none
+  const bool ok4 = ts < L;                   // at least one of them exists
+  const int nv = ANYL ? min(max(L - ts, 0), 4) : (ok4 ? 4 : 0);  // how many exist
 
   // Offsets in bytes (the host keeps each plane set below 2^31 bytes).  Loads read clamped,
-  // in-range addresses; stores of absent steps or channels get an offset past the
-  // resource, which the hardware drops.
+  // in-range addresses (a quad that would run past the row's end, or start before it on a
+  // backward route, is moved inside it and the lane picks its elements out of it); stores
+  // of absent steps or channels get an offset past the resource, which the hardware drops.
   const uint32_t row_bytes = uint32_t(L) * sizeof(T);
-  const int tsc = ok4 ? ts : L - 4;
-  const uint32_t xo4 = uint32_t(rev ? L - 4 - tsc : tsc) * sizeof(T);
+  const int qs = rev ? max(L - 4 - ts, 0) : min(ts, L - 4);  // first element loaded
+  const uint32_t xo4 = uint32_t(qs) * sizeof(T);
   const uint32_t st4 = uint32_t(ts) * sizeof(T);
   constexpr uint32_t kDrop = 0x80000000u;
   const __amdgpu_buffer_rsrc_t x_r = make_rsrc(xplanes, uint32_t(D) * row_bytes);
@@ -568,7 +590,30 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   // Two register sets, used in turn: a chunk is processed from one while the next chunk's
   // rows load into the other.
   float xA[4][4], hA[4][3], xB[4][4], hB[4][3];
-  const typename Quad<T>::Sel qsel(rev);
+  auto make_sel = [&]() {
+    if constexpr (ANYL) {
+      int kq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)  // element of step ts + j in the loaded quad
+        kq[j] = min(max(rev ? L - 1 - ts - j - qs : ts + j - qs, 0), 3);
+      return typename Quad<T>::Sel(kq);
+    } else {
+      return typename Quad<T>::Sel(rev);
+    }
+  };
+  const typename Quad<T>::Sel qsel = make_sel();
+  // four values to steps ts .. ts + 3 of a row (voff: the row's byte offset, or kDrop)
+  auto store_quad = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                        const float (&v)[4]) {
+    if (!ANYL || nv == 4 || voff == kDrop) {  // kDrop + st4 is past the resource too
+      Quad<T>::store(r, voff + st4, soff, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        buf_store_at(r, j < nv ? voff + st4 + uint32_t(j) * sizeof(T) : kDrop, soff,
+                     out_elem<T>(v[j]));
+    }
+  };
   auto load_rows = [&](int d0, float (&xv)[4][4], float (&hv)[4][3]) {
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
@@ -635,8 +680,8 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
         for (int j = 0; j < 4; ++j) u[j] = d < D ? u[j] : 0.0f;
       }
       const int rb = min(d0 + wave * 16 + 4 * G, D - 1);
-      Quad<T>::store(u_r, (d < D && ok4) ? uint32_t(sr) * row_bytes + st4 : kDrop,
-                     uint32_t(rb) * row_bytes, u);
+      store_quad(u_r, (d < D && ok4) ? uint32_t(sr) * row_bytes : kDrop,
+                 uint32_t(rb) * row_bytes, u);
       Ops::put_col4(sU, kTT, 4 * q4, c, u);
     }
     __syncthreads();
@@ -692,7 +737,7 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
       const int row = 4 * rg + sr;
       const float4 x4 = *reinterpret_cast<const float4*>(&sXd[min(row, R - 1)][4 * q4]);
       const float v[4] = {x4.x, x4.y, x4.z, x4.w};
-      Quad<T>::store(lr_r, (row < R && ok4) ? uint32_t(row) * row_bytes + st4 : kDrop, 0, v);
+      store_quad(lr_r, (row < R && ok4) ? uint32_t(row) * row_bytes : kDrop, 0, v);
     }
   }
   const __amdgpu_buffer_rsrc_t dt_r =
@@ -723,8 +768,7 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         const int d = dc + 4 * G + sr;
-        const uint32_t off = (d < D && ok4) ? uint32_t(d) * row_bytes + st4 : kDrop;
-        Quad<T>::store(dt_r, off, 0, dv[G]);
+        store_quad(dt_r, (d < D && ok4) ? uint32_t(d) * row_bytes : kDrop, 0, dv[G]);
       }
     }
   };
@@ -743,10 +787,10 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
     const float4 x4 = *reinterpret_cast<const float4*>(&sXd[R + min(row, 2 * N - 1)][4 * q4]);
     const float v[4] = {x4.x, x4.y, x4.z, x4.w};
     if (4 * rg < N)
-      Quad<T>::store(b_r, (row < N && ok4) ? uint32_t(row) * row_bytes + st4 : kDrop, 0, v);
+      store_quad(b_r, (row < N && ok4) ? uint32_t(row) * row_bytes : kDrop, 0, v);
     if (4 * rg + 3 >= N)
-      Quad<T>::store(c_r, (row >= N && row < 2 * N && ok4)
-                              ? uint32_t(row - N) * row_bytes + st4 : kDrop, 0, v);
+      store_quad(c_r, (row >= N && row < 2 * N && ok4) ? uint32_t(row - N) * row_bytes : kDrop,
+                 0, v);
   }
 }
 
@@ -773,14 +817,18 @@ int launch_project(const ProjArgs& a0, int dtype, hipStream_t st) {
   if (e != hipSuccess) return static_cast<int>(e);
   const dim3 grid((a.L + kTT - 1) / kTT, a.K, a.B);
   const bool kw4 = a.KW == 4;
-  if (kw4 && a.L % 4 == 0) {
+  if (kw4 && a.L >= 4) {
     const size_t lds = dtype == 0 ? proj_lds_bytes<float>(MP) : proj_lds_bytes<uint16_t>(MP);
+    const bool anyl = a.L % 4 != 0;
     auto launch4 = [&](auto mt_tag) {
       constexpr int MTC = decltype(mt_tag)::value;
-      if (dtype == 0)
-        k_project4<float, MTC><<<grid, 256, lds, st>>>(a);
-      else
-        k_project4<uint16_t, MTC><<<grid, 256, lds, st>>>(a);
+      if (dtype == 0) {
+        if (anyl) k_project4<float, MTC, true><<<grid, 256, lds, st>>>(a);
+        else k_project4<float, MTC, false><<<grid, 256, lds, st>>>(a);
+      } else {
+        if (anyl) k_project4<uint16_t, MTC, true><<<grid, 256, lds, st>>>(a);
+        else k_project4<uint16_t, MTC, false><<<grid, 256, lds, st>>>(a);
+      }
     };
     switch (MP / 16) {
       case 1: launch4(std::integral_constant<int, 1>{}); break;
