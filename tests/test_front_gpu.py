@@ -78,6 +78,9 @@ PROJ_SHAPES = [  # B, D, H, W, N, K, dtype, R, KW
     (1, 130, 12, 20, 16, 4, "bf16", 64, 4),    # dt_proj weights too large for LDS
     (2, 48, 1, 196, 16, 2, "bf16", 1, 4),      # Vim paths without the class token
     (1, 24, 4, 1, 4, 4, "f32", 2, 4),          # four steps in all
+    (1, 24, 1, 5, 4, 4, "bf16", 2, 4),         # five steps: one lane holds the fifth alone
+    (1, 24, 7, 1, 4, 4, "f32", 2, 4),          # seven steps (the last lane holds three)
+    (2, 20, 1, 6, 4, 2, "bf16", 1, 4),         # six steps, both paths
 ]
 
 
