@@ -415,30 +415,45 @@ int oracle_project_lr(int K, const float *x, const float *conv_w, const float *c
  * dx accumulates du_t at the visited position over the routes; dBs, dCs sum over the
  * channels d (Bs and Cs are shared by all channels of a (b, k)).  Everything in double.
  * Work is split over images b (each thread owns whole images, so no sum is shared between
- * threads); the per-image contributions to dA_log, dDs and ddt_bias are added in b order. */
+ * threads); the per-image contributions to dA_log, dDs and ddt_bias are added in b order.
+ *
+ * Gated operator (the Vim block's gate, Vim summary section 4.3: out = y * SiLU(z) with y the
+ * route sum above): by the product rule every route sees g = dy SiLU(z) in place of dy, and
+ *   dz = dy y SiLU'(z),   SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))),
+ * with y the ungated route sum, accumulated here from the same recomputed states. */
 
 static double sigmoid(double z) {
     return 1.0 / (1.0 + exp(-z));
 }
 
+/* d/dz of z sigmoid(z) */
+static double silu_grad(double z) {
+    const double s = sigmoid(z);
+    return s * (1.0 + z * (1.0 - s));
+}
+
 /* One image b, all routes and channels.  Accumulates into dx_b (D, L), ddt_b (K, D, L),
  * dB_b, dC_b (K, N, L) and the parameter partials pA (K, D, N), pD (K, D), pbias (K, D);
- * ws holds 2 L N + 2 L + N doubles. */
+ * with the gate z (else NULL), writes dz_b (D, L).  ws holds 2 L N + 3 L + 2 N doubles. */
 static void image_backward(int K, const float *x, const float *dt_raw, const float *A_log,
                            const float *Bs, const float *Cs, const float *Ds,
-                           const float *dt_bias, const float *dy, int64_t D, int64_t H,
-                           int64_t W, int64_t N, int64_t b, double *dx_b, double *ddt_b,
-                           double *dB_b, double *dC_b, double *pA, double *pD, double *pbias,
-                           double *ws) {
+                           const float *dt_bias, const float *z, const float *dy, int64_t D,
+                           int64_t H, int64_t W, int64_t N, int64_t b, double *dx_b,
+                           double *ddt_b, double *dB_b, double *dC_b, double *pA, double *pD,
+                           double *pbias, double *dz_b, double *ws) {
     const int64_t L = H * W;
     double *hs = ws;               /* h_t,n, t-major */
     double *as = hs + L * N;       /* a_t,n */
     double *delta = as + L * N;    /* delta_t */
     double *lam = delta + L;       /* lambda_n */
     double *A = lam + N;           /* A_n */
+    double *ysum = A + N;          /* ungated route sum y_l (gate only) */
     for (int64_t d = 0; d < D; ++d) {
         const float *xc = x + (b * D + d) * L;
         const float *gc = dy + (b * D + d) * L;
+        const float *zc = z ? z + (b * D + d) * L : NULL;
+        for (int64_t l = 0; l < L; ++l)
+            ysum[l] = 0.0;
         for (int k = 0; k < K; ++k) {
             const double bias = dt_bias[k * D + d];
             const double Dk = Ds[k * D + d];
@@ -449,14 +464,18 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                 A[n] = -exp((double)A_log[(k * D + d) * N + n]);
             /* forward, keeping every state */
             for (int64_t t = 0; t < L; ++t) {
-                const double u = xc[route_position(K, k, t, H, W)];
+                const int64_t l = route_position(K, k, t, H, W);
+                const double u = xc[l];
                 delta[t] = softplus((double)dt[t] + bias);
+                double yroute = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
                     const double a = exp(delta[t] * A[n]);
                     const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;
                     as[t * N + n] = a;
                     hs[t * N + n] = a * hprev + delta[t] * (double)Bk[n * L + t] * u;
+                    yroute += (double)Ck[n * L + t] * hs[t * N + n];
                 }
+                ysum[l] += yroute + Dk * u;
             }
             /* reverse */
             for (int64_t n = 0; n < N; ++n)
@@ -464,7 +483,7 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
             for (int64_t t = L - 1; t >= 0; --t) {
                 const int64_t l = route_position(K, k, t, H, W);
                 const double u = xc[l];
-                const double g = gc[l];
+                const double g = zc ? (double)gc[l] * silu((double)zc[l]) : (double)gc[l];
                 double ddelta = 0.0, du = g * Dk;
                 pD[k * D + d] += g * u;
                 for (int64_t n = 0; n < N; ++n) {
@@ -479,27 +498,34 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                     pA[(k * D + d) * N + n] += da * a * delta[t] * A[n];
                     du += lam[n] * delta[t] * (double)Bk[n * L + t];
                 }
-                const double dz = ddelta * sigmoid((double)dt[t] + bias);
-                ddt_b[(k * D + d) * L + t] = dz;
-                pbias[k * D + d] += dz;
+                const double dr = ddelta * sigmoid((double)dt[t] + bias);
+                ddt_b[(k * D + d) * L + t] = dr;
+                pbias[k * D + d] += dr;
                 dx_b[d * L + l] += du;
             }
         }
+        if (zc)
+            for (int64_t l = 0; l < L; ++l)
+                dz_b[d * L + l] = (double)gc[l] * ysum[l] * silu_grad((double)zc[l]);
     }
 }
 
 /* Gradients of sum(dy * y) with respect to every input (outputs in double, caller-owned):
  *   dx (B, D, H, W), ddt_raw (B, K, D, L), dA_log (K, D, N), dBs, dCs (B, K, N, L),
- *   dDs, ddt_bias (K, D).
+ *   dDs, ddt_bias (K, D); with the gate z (B, D, H, W) (else NULL), y is the gated output
+ *   and dz (B, D, H, W) receives its gradient with respect to z.
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
-int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_log,
-                    const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
-                    const float *dy, double *dx, double *ddt_raw, double *dA_log, double *dBs,
-                    double *dCs, double *dDs, double *ddt_bias, int64_t B, int64_t D,
-                    int64_t H, int64_t W, int64_t N, int nthreads) {
+int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
+                       const float *Bs, const float *Cs, const float *Ds,
+                       const float *dt_bias, const float *z, const float *dy, double *dx,
+                       double *ddt_raw, double *dA_log, double *dBs, double *dCs,
+                       double *dDs, double *ddt_bias, double *dz, int64_t B, int64_t D,
+                       int64_t H, int64_t W, int64_t N, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
         return -1;
     if (K == 2 && H != 1)
+        return -1;
+    if (z && !dz)
         return -1;
     const int threads = pick_threads(nthreads);
     const int64_t L = H * W;
@@ -518,7 +544,7 @@ int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_l
 #pragma omp parallel num_threads(threads) reduction(| : failed)
 #endif
     {
-        double *ws = (double *)malloc(sizeof(double) * (size_t)(2 * L * N + 2 * L + 2 * N));
+        double *ws = (double *)malloc(sizeof(double) * (size_t)(2 * L * N + 3 * L + 2 * N));
         if (!ws) {
             failed = 1;
         } else {
@@ -527,10 +553,10 @@ int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_l
 #endif
             for (int64_t b = 0; b < B; ++b) {
                 double *p = part + b * np;
-                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, D, H, W, N, b,
-                               dx + b * D * L, ddt_raw + b * K * D * L, dBs + b * K * N * L,
-                               dCs + b * K * N * L, p, p + K * D * N, p + K * D * N + K * D,
-                               ws);
+                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy, D, H, W, N,
+                               b, dx + b * D * L, ddt_raw + b * K * D * L,
+                               dBs + b * K * N * L, dCs + b * K * N * L, p, p + K * D * N,
+                               p + K * D * N + K * D, z ? dz + b * D * L : NULL, ws);
             }
             free(ws);
         }
@@ -554,3 +580,12 @@ int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_l
     return failed ? -1 : threads;
 }
 
+/* The plain operator's gradients (no gate). */
+int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_log,
+                    const float *Bs, const float *Cs, const float *Ds, const float *dt_bias,
+                    const float *dy, double *dx, double *ddt_raw, double *dA_log, double *dBs,
+                    double *dCs, double *dDs, double *ddt_bias, int64_t B, int64_t D,
+                    int64_t H, int64_t W, int64_t N, int nthreads) {
+    return oracle_backward_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, dy, dx, ddt_raw,
+                              dA_log, dBs, dCs, dDs, ddt_bias, NULL, B, D, H, W, N, nthreads);
+}

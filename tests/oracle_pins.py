@@ -28,6 +28,8 @@ What pins what:
                     held constant (Vim summary, sec. 4.1, defines the ZOH discretisation)
   backward fd       every gradient against central finite differences of the forward
   backward adjoint  <dy, y(v) - y(0)> = <grad, v> for the inputs y is affine in; dDs closed form
+  backward gate     the gated output's gradients (z's included) against finite differences;
+                    z = 0 and z = 40 reduce them to closed forms of the plain operator's
   project impulse   a unit impulse through the per-route causal conv gives the reversed taps
                     on the KW steps from the one that visits it, the bias elsewhere
   project brute     numpy.convolve, scipy.special.expit and matrix products on tiny inputs
@@ -505,6 +507,60 @@ def pin_backward_adjoint(orc):
         _close(got["Ds"], np.broadcast_to(want, (K, D)), 1e-12, 1e-13, f"dDs closed form, K={K}")
 
 
+def pin_backward_gate(orc):
+    """Gradients of the gated output sum(dy * y * SiLU(z)): every input's, z's included,
+    element by element against central finite differences of the gated forward oracle; and
+    two closed forms against the plain operator's own (separately pinned) forward and
+    backward: at z = 0 (SiLU = 0, SiLU' = 1/2) every input's gradient is exactly zero and
+    dz = dy y / 2; at z = 40 (SiLU(z) = 40 and SiLU'(z) = 1 in double) the gradients are 40
+    times the plain ones and dz = dy y."""
+    rng = _rng(18)
+    for K, xshape in ((4, (1, 2, 3, 4)), (2, (2, 2, 7))):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 2
+        args = list(_random_inputs(rng, B, K, D, N, L, xshape))
+        dy = rng.standard_normal(xshape).astype(np.float32)
+        z = (1.5 * rng.standard_normal(xshape)).astype(np.float32)
+        got = orc.backward(K, *args, dy, z=z)
+        dyd = dy.astype(np.float64)
+
+        def loss(a, zz):
+            return float(np.sum(orc.forward(K, *a, z=zz) * dyd))
+
+        names = BWD_NAMES + ("z",)
+        for i, name in enumerate(names):
+            base_arr = z if name == "z" else args[i]
+            flat = base_arr.reshape(-1)
+            fd = np.empty(flat.size)
+            for j in range(flat.size):
+                base = float(flat[j])
+                step = 1e-3 * max(1.0, abs(base))
+                hi, lo = np.float32(base + step), np.float32(base - step)
+                vals = []
+                for v in (hi, lo):
+                    pert = [a.copy() for a in args]
+                    zz = z.copy()
+                    (zz if name == "z" else pert[i]).reshape(-1)[j] = v
+                    vals.append(loss(pert, zz))
+                fd[j] = (vals[0] - vals[1]) / (float(hi) - float(lo))
+            g = got[name].reshape(-1)
+            scale = max(float(np.max(np.abs(fd))), 1e-12)
+            err = float(np.max(np.abs(g - fd))) / scale
+            assert err < 2e-5, f"gated d/d{name} (K={K}) differs from finite differences: {err:.2e}"
+
+        y = orc.forward(K, *args)
+        plain = orc.backward(K, *args, dy)
+        at0 = orc.backward(K, *args, dy, z=np.zeros(xshape, np.float32))
+        for name in BWD_NAMES:
+            assert np.all(at0[name] == 0.0), f"gate at z = 0: d/d{name} (K={K}) not zero"
+        _close(at0["z"], dyd * y / 2.0, 1e-13, 1e-15, f"gate at z = 0: dz, K={K}")
+        at40 = orc.backward(K, *args, dy, z=np.full(xshape, 40.0, np.float32))
+        for name in BWD_NAMES:
+            _close(at40[name], 40.0 * plain[name], 1e-13, 1e-15, f"gate at z = 40: d/d{name}")
+        _close(at40["z"], dyd * y, 1e-13, 1e-15, f"gate at z = 40: dz, K={K}")
+
+
 # ---- per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj) -----------------
 def _front_weights(rng, K, D, N, R, KW):
     conv_w = rng.standard_normal((K, D, KW)).astype(np.float32)
@@ -681,5 +737,5 @@ def pin_routes_lowrank(orc):
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
             pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
-            pin_backward_adjoint, pin_project_impulse, pin_project_brute, pin_project_select,
-            pin_routes_variant, pin_routes_lowrank]
+            pin_backward_adjoint, pin_backward_gate, pin_project_impulse, pin_project_brute,
+            pin_project_select, pin_routes_variant, pin_routes_lowrank]

@@ -54,6 +54,13 @@ MUTATIONS = [
     ("B layout (L, N)", "bbar * (double)Bk[n * L + t] * u", "bbar * (double)Bk[t * N + n] * u"),
     ("delta read at image position", "                dtv = dt[t];", "                dtv = dt[l];"),
     ("backward 1D route not reversed", "return k == 0 ? t : L - 1 - t;", "return t;"),
+    ("bwd gate: SiLU' without the z term", "return s * (1.0 + z * (1.0 - s));",
+     "return s;"),
+    ("bwd gate: routes see dy times sigmoid(z)",
+     "(double)gc[l] * silu((double)zc[l]) : (double)gc[l];",
+     "(double)gc[l] * sigmoid((double)zc[l]) : (double)gc[l];"),
+    ("bwd gate: dz without the skip term", "ysum[l] += yroute + Dk * u;",
+     "ysum[l] += yroute;"),
     ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;",
      "A_log[(k * N + n) * D + d]);\n            h[n] = 0.0;"),
     ("Ds indexed (D, K)", "\n        const double Dk = Ds[k * D + d];",
@@ -68,7 +75,7 @@ MUTATIONS = [
     ("gate is the sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     ("gate misses the skip term", "out[l] += (yk + Dk * u) * gate;",
      "out[l] += yk * gate + Dk * u;"),
-    ("gate read at the scan step", "silu((double)zc[l])", "silu((double)zc[t])"),
+    ("gate read at the scan step", "gate = zc ? silu((double)zc[l])", "gate = zc ? silu((double)zc[t])"),
     ("ZOH without the minus one", "bbar = expm1(delta * A[n]) / A[n];",
      "bbar = exp(delta * A[n]) / A[n];"),
     ("ZOH divided by delta", "bbar = expm1(delta * A[n]) / A[n];",
