@@ -107,9 +107,10 @@ def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
-    """The float64 oracle's backward, as it is, on all host cores, over a bounded sample of
-    whole images (its unit of work: dBs and dCs sum over every channel of an image)."""
+def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None) -> dict:
+    """The float64 oracle's backward (gated with z), as it is, on all host cores, over a
+    bounded sample of whole images (its unit of work: dBs and dCs sum over every channel of
+    an image)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     orc = oracle.Oracle()
@@ -117,7 +118,7 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
     def run(n):
         sl = [inp[k][:n] if k in ("x", "dt_raw", "Bs", "Cs") else inp[k] for k in ARGS]
         t0 = time.perf_counter()
-        orc.backward(wl.K, *sl, dy[:n], threads=cores)
+        orc.backward(wl.K, *sl, dy[:n], threads=cores, z=None if z is None else z[:n])
         return time.perf_counter() - t0
 
     n = min(wl.B, max(1, cores))
@@ -128,8 +129,9 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float) -> dict:
     upd = n * wl.K * wl.D * wl.L * wl.N
     return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
             "kind": "oracle",
-            "sample": f"backward of {n} of {wl.B} images of {wl.name} (all {wl.K} routes and "
-                      f"{wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
+            "sample": f"{'gated ' if z is not None else ''}backward of {n} of {wl.B} images "
+                      f"of {wl.name} (all {wl.K} routes and {wl.D} channels), {upd:.3e} state "
+                      f"updates in {dt:.2f} s"}
 
 
 def cpu_baseline_front(wl, inp, w, target_s: float, z=None, zoh=False,
@@ -219,7 +221,8 @@ def main() -> int:
     ap.add_argument("--zoh", action="store_true",
                     help="zero-order-hold discretisation of B")
     ap.add_argument("--backward", action="store_true",
-                    help="time the backward entry point (gradients of sum(dy * y))")
+                    help="time the backward entry point (gradients of sum(dy * y); with "
+                         "--gate, of the gated output, z included)")
     ap.add_argument("--front", action="store_true",
                     help="per-route front end: time ss2d_project (causal conv + SiLU, x_proj, "
                          "dt_proj) followed by ss2d_forward_routes on its outputs")
@@ -277,8 +280,8 @@ def main() -> int:
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    if args.backward and (args.gate or args.zoh or args.front):
-        log("the backward entry point covers the plain operator only")
+    if args.backward and (args.zoh or args.front):
+        log("the backward entry points cover the plain and the gated operator only")
         return 2
     z = None
     if gate is not None:
@@ -313,8 +316,12 @@ def main() -> int:
         g = workloads.make_output_grad(wl, 0)
         dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
               if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
-        fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
-        call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
+        if z is None:
+            fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
+            call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
+        else:
+            fn = ss.ss2d_backward_gated if wl.K == 4 else ss.ss1d_bidir_backward_gated
+            call = lambda: fn(*[dev[k] for k in ARGS], z, dy)  # noqa: E731
     elif args.gate or args.zoh:
         fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
         call = lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)  # noqa: E731
@@ -409,7 +416,8 @@ def main() -> int:
                                      z=gate["z"] if gate else None, zoh=args.zoh,
                                      lowrank=args.front_lowrank)
         elif args.backward:
-            cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds)
+            cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds,
+                                        z=gate["z"] if gate else None)
         else:
             cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
                                zoh=args.zoh)

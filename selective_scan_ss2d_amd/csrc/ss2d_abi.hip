@@ -188,7 +188,8 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
   const int64_t per = a.chunks_in_launch > 0 ? a.chunks_in_launch : 1;
   const int64_t max_b = kMaxGridZ / per > 0 ? kMaxGridZ / per : 1;
   const int64_t L = a.L, D = a.D, K = a.K, N = a.N;
-  const int64_t C = mode == ss2d::kModeCkpt ? a.ck_tiles : a.num_chunks;
+  const bool ckpt = mode == ss2d::kModeCkpt || mode == ss2d::kModeCkptOut;
+  const int64_t C = ckpt ? a.ck_tiles : a.num_chunks;
   for (int64_t b0 = 0; b0 < B; b0 += max_b) {
     const int64_t nb = (B - b0 < max_b) ? (B - b0) : max_b;
     ss2d::ScanArgs s = a;
@@ -204,9 +205,9 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
     if (a.h_end) s.h_end = a.h_end + b0 * K * D * C * N;
     if (a.delta_sum) s.delta_sum = a.delta_sum + b0 * K * D * C;
     if (a.h_in) s.h_in = a.h_in + b0 * K * D * C * N;
-    const int kind = mode == ss2d::kModeAgg    ? SS2D_KERNEL_CHUNK_AGG
-                     : mode == ss2d::kModeCkpt ? SS2D_KERNEL_CHECKPOINT
-                                               : SS2D_KERNEL_SCAN;
+    const int kind = mode == ss2d::kModeAgg ? SS2D_KERNEL_CHUNK_AGG
+                     : ckpt                 ? SS2D_KERNEL_CHECKPOINT
+                                            : SS2D_KERNEL_SCAN;
     const int rc = timed(kind, st, [&] { return run_scan(s, dtype, p.split, mode, st); });
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc));
   }
@@ -339,10 +340,12 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
 }
 
 // ---- backward ----------------------------------------------------------------------------
+// z (not NULL): gradients of the gated output y SiLU(z); dz receives z's gradient.
 int backward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
              const void* Cs, const float* Ds, const float* dt_bias, const void* dy, void* dx,
              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
-             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream,
+             const void* z = nullptr, void* dz = nullptr, bool gated = false) {
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
   if (N != 4 && N != 8 && N != 16) return SS2D_ERR_UNSUPPORTED;
@@ -354,28 +357,30 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
   if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
   if (B == 0 || D == 0) return SS2D_OK;
-  const void* ins[] = {x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy};
-  const void* outs[] = {dx, ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias};
-  for (const void* ptr : ins)
-    if (!ptr) return SS2D_ERR_NULL;
-  for (const void* ptr : outs)
-    if (!ptr) return SS2D_ERR_NULL;
+  // z and dz are the last input and output of the gated entry points
+  const void* ins[] = {x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z};
+  const void* outs[] = {dx, ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias, dz};
+  const int n_in = gated ? 9 : 8, n_out = gated ? 8 : 7;
+  for (int i = 0; i < n_in; ++i)
+    if (!ins[i]) return SS2D_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i]) return SS2D_ERR_NULL;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
-  for (const void* ptr : {x, dt_raw, Bs, Cs, dy, static_cast<const void*>(dx),
+  for (const void* ptr : {x, dt_raw, Bs, Cs, dy, z, static_cast<const void*>(dx),
                           static_cast<const void*>(ddt_raw), static_cast<const void*>(dBs),
-                          static_cast<const void*>(dCs)})
+                          static_cast<const void*>(dCs), static_cast<const void*>(dz)})
     if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
   for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
                           static_cast<const void*>(dt_bias), static_cast<const void*>(dA_log),
                           static_cast<const void*>(dDs), static_cast<const void*>(ddt_bias)})
     if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
   const int64_t in_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
-                              int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e};
+                              int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e, n_x * e};
   const int64_t out_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
-                               int64_t(K) * D * 4, int64_t(K) * D * 4};
-  for (int i = 0; i < 7; ++i) {
-    for (int j = 0; j < 8; ++j)
+                               int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e};
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SS2D_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SS2D_ERR_ALIAS;
@@ -388,16 +393,21 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   int rc = prepare_pool(device);
   if (rc != SS2D_OK) return rc;
 
-  // Scratch: transposes of x and dy, checkpoints, per-route du, dB/dC block partials and the
-  // per-image parameter partials.
+  // Scratch: transposes of x and of the route gradient g, checkpoints, per-route du, dB/dC
+  // block partials and the per-image parameter partials; with the gate, g = dy SiLU(z) in
+  // fp32 (the gradient every route receives, not rounded to the data type) and, until the
+  // adjoint overwrites them with du, the per-route outputs.
   const int64_t tiles = (L + 31) / 32;
   const int64_t n_cb = (D + 63) / 64;
   const bool need_t = (K == 4) && H > 1 && W > 1;
+  const int64_t ge = gated ? 4 : e;  // bytes per element of g
   size_t off = 0;
   const size_t off_xt = off;
   if (need_t) off = align256(off + size_t(n_x * e));
   const size_t off_gt = off;
-  if (need_t) off = align256(off + size_t(n_x * e));
+  if (need_t) off = align256(off + size_t(n_x * ge));
+  const size_t off_g = off;
+  if (gated) off = align256(off + size_t(n_x * 4));
   const size_t off_ck = off;
   off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
   const size_t off_du = off;
@@ -415,19 +425,16 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   if (he != hipSuccess) return hip_fail(he);
 
   int err = 0;
+  // g: the gradient every route's output receives (dy, or dy SiLU(z) with the gate)
+  const void* g_img = gated ? static_cast<const void*>(ws + off_g) : dy;
   const void* xt = need_t ? static_cast<const void*>(ws + off_xt) : x;
-  const void* gt = need_t ? static_cast<const void*>(ws + off_gt) : dy;
-  if (need_t) {
+  const void* gt = need_t ? static_cast<const void*>(ws + off_gt) : g_img;
+  if (need_t)
     err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
       return ss2d::launch_transpose(x, ws + off_xt, int(B), int(D), int(H), int(W), dtype, st);
     });
-    if (!err)
-      err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
-        return ss2d::launch_transpose(dy, ws + off_gt, int(B), int(D), int(H), int(W), dtype,
-                                      st);
-      });
-  }
-  // Checkpoints: the forward scan storing the state before every 32-step tile.
+  // Checkpoints: the forward scan storing the state before every 32-step tile (and, with the
+  // gate, the per-route outputs, which the merge kernel turns into g and dz).
   if (!err) {
     ss2d::ScanArgs a{};
     a.x_row = x;
@@ -449,18 +456,33 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     a.chunk_base = 0;
     a.chunks_in_launch = 1;
     a.ck_tiles = int(tiles);
+    if (gated) a.y_route = reinterpret_cast<float*>(ws + off_du);
     Plan p;
     p.split = 4;
-    rc = scan_pass(a, dtype, p, ss2d::kModeCkpt, e, st);
+    rc = scan_pass(a, dtype, p, gated ? ss2d::kModeCkptOut : ss2d::kModeCkpt, e, st);
   }
+  if (gated && !err && rc == SS2D_OK)
+    err = timed(SS2D_KERNEL_MERGE, st, [&] {
+      const float* yr = reinterpret_cast<const float*>(ws + off_du);
+      return (K == 4) ? ss2d::launch_merge4_gate_bwd(yr, z, dy, ws + off_g, dz, int(B), int(D),
+                                                     int(H), int(W), dtype, st)
+                      : ss2d::launch_merge2_gate_bwd(yr, z, dy, ws + off_g, dz, int(B), int(D),
+                                                     int(L), dtype, st);
+    });
+  if (need_t && !err && rc == SS2D_OK)
+    err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
+      return ss2d::launch_transpose(g_img, ws + off_gt, int(B), int(D), int(H), int(W),
+                                    gated ? SS2D_F32 : dtype, st);
+    });
   // Adjoint scan, in batches of images that keep gridDim.z in range.
   for (int64_t b0 = 0; !err && rc == SS2D_OK && b0 < B; b0 += kMaxGridZ) {
     const int64_t nb = (B - b0 < kMaxGridZ) ? (B - b0) : kMaxGridZ;
     ss2d::BwdArgs g{};
     g.x_row = static_cast<const char*>(x) + b0 * D * L * e;
     g.x_col = static_cast<const char*>(xt) + b0 * D * L * e;
-    g.g_row = static_cast<const char*>(dy) + b0 * D * L * e;
-    g.g_col = static_cast<const char*>(gt) + b0 * D * L * e;
+    g.g_row = static_cast<const char*>(g_img) + b0 * D * L * ge;
+    g.g_col = static_cast<const char*>(gt) + b0 * D * L * ge;
+    g.g_f32 = gated ? 1 : 0;
     g.dt_raw = static_cast<const char*>(dt_raw) + b0 * K * D * L * e;
     g.Bs = static_cast<const char*>(Bs) + b0 * K * N * L * e;
     g.Cs = static_cast<const char*>(Cs) + b0 * K * N * L * e;
@@ -665,6 +687,25 @@ int ss1d_bidir_backward(const void* x, const void* dt_raw, const float* A_log,
                         int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream) {
   return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream);
+}
+
+int ss2d_backward_gated(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                        const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                        const void* dy, void* dx, void* ddt_raw, float* dA_log, void* dBs,
+                        void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B, int64_t D,
+                        int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+  return backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, true);
+}
+
+int ss1d_bidir_backward_gated(const void* x, const void* dt_raw, const float* A_log,
+                              const void* Bs, const void* Cs, const float* Ds,
+                              const float* dt_bias, const void* z, const void* dy, void* dx,
+                              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs,
+                              float* ddt_bias, void* dz, int64_t B, int64_t D, int64_t L,
+                              int64_t N, int dtype, void* stream) {
+  return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, true);
 }
 
 int ss2d_project(const void* x, const float* conv_w, const float* conv_b,

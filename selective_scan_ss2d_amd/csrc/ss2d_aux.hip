@@ -1,10 +1,30 @@
 // Support kernels of the SS2D forward operator (gfx950): the per-plane transpose that turns
 // the column routes into contiguous walks, the chunk-carry pass of the chunked scan, and the
 // cross-merge that undoes each route's permutation and sums the routes in a fixed order.
+#include <type_traits>
+
 #include "ss2d_device.h"
 
 namespace ss2d {
 namespace {
+
+// What the merge does with the route sum v at a position (GM, a template parameter):
+constexpr int kGateNone = 0;  // y = v
+constexpr int kGateFwd = 1;   // y = v SiLU(z)
+constexpr int kGateBwd = 2;   // gated backward: y = dy SiLU(z) in fp32, dz = dy v SiLU'(z)
+
+// Element type of the merge's output y: the data type, or fp32 for the gated backward's g
+// (the gradient every route receives is kept in fp32 for the adjoint scan).
+template <typename T, int GM> using MergeOut = std::conditional_t<GM == kGateBwd, float, T>;
+
+// The gate's backward at one position, for out = v SiLU(z): g = dy SiLU(z) is the gradient
+// that reaches every route's output, and dz = dy v SiLU'(z), with
+// SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))).
+__device__ __forceinline__ void gate_bwd(float v, float z, float dy, float& g, float& dz) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e));
+  g = dy * (z * sg);
+  dz = dy * v * (sg * fmaf(z, 1.0f - sg, 1.0f));
+}
 
 constexpr int kTr = 32;        // transpose / merge tile edge
 constexpr int kTrRows = 8;     // thread rows per tile (block = 32 x 8)
@@ -187,14 +207,16 @@ __global__ void __launch_bounds__(256) k_carry(const ScanArgs a) {
 
 // Four-route merge.  For image position (h, w), l = h * W + w and s = w * H + h (its step
 // on the column-major route):
-//   y[l] = ((y0[l] + y1[L-1-l]) + y2[s]) + y3[L-1-s]          (times SiLU(z[l]) with GATE)
-// with y_k the per-route outputs in scan order.  Column-route values go through an LDS tile
-// so that every global access is a contiguous run.  The gate is shared by the routes, so
-// gating the sum once equals summing the gated route outputs.
-template <typename T, bool GATE>
+//   v[l] = ((y0[l] + y1[L-1-l]) + y2[s]) + y3[L-1-s]
+// with y_k the per-route outputs in scan order, and y = v, v SiLU(z) or the gate's backward
+// (GM).  Column-route values go through an LDS tile so that every global access is a
+// contiguous run.  The gate is shared by the routes, so gating the sum once equals summing
+// the gated route outputs.
+template <typename T, int GM>
 __global__ void __launch_bounds__(kTr * kTrRows)
-k_merge4(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D, int H,
-         int W, int64_t planes) {
+k_merge4(const float* __restrict__ yr, const T* __restrict__ z, const T* __restrict__ dy,
+         MergeOut<T, GM>* __restrict__ y, T* __restrict__ dz, int D, int H, int W,
+         int64_t planes) {
   __shared__ float t2[kTr][kTr + 1];
   __shared__ float t3[kTr][kTr + 1];
   const int tx = threadIdx.x, ty = threadIdx.y;
@@ -224,8 +246,15 @@ k_merge4(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ 
         float v = y0[l] + y1[L - 1 - l];
         v += t2[tx][r];
         v += t3[tx][r];
-        if (GATE) v *= silu_f32(Elem<T>::load(z + p * L + l));
-        y[p * L + l] = Elem<T>::from_f32(v);
+        if constexpr (GM == kGateBwd) {
+          float g, dzv;
+          gate_bwd(v, Elem<T>::load(z + p * L + l), Elem<T>::load(dy + p * L + l), g, dzv);
+          y[p * L + l] = g;
+          dz[p * L + l] = Elem<T>::from_f32(dzv);
+        } else {
+          if (GM == kGateFwd) v *= silu_f32(Elem<T>::load(z + p * L + l));
+          y[p * L + l] = Elem<T>::from_f32(v);
+        }
       }
     }
     __syncthreads();
@@ -320,10 +349,12 @@ template <> struct Gate4<uint16_t> {
   }
 };
 
-template <typename T, bool GATE>
+template <typename T, int GM>
 __global__ void __launch_bounds__(256)
-k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D,
-             int H, int W, int64_t planes) {
+k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, const T* __restrict__ dy,
+             MergeOut<T, GM>* __restrict__ y, T* __restrict__ dz, int D, int H, int W,
+             int64_t planes) {
+  constexpr bool GATE = GM != kGateNone;
   // A block covers a 64 x 64 tile (h x w) of one plane; every thread keeps four 16-byte
   // loads of each route (and, with the gate, its four gate loads) in flight before the
   // barrier.
@@ -381,23 +412,39 @@ k_merge4_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restric
         float v2 = r0[j].z + r1[j].y, v3 = r0[j].w + r1[j].x;
         v0 += t2[ow + 0][ht]; v1 += t2[ow + 1][ht]; v2 += t2[ow + 2][ht]; v3 += t2[ow + 3][ht];
         v0 += t3[ow + 0][ht]; v1 += t3[ow + 1][ht]; v2 += t3[ow + 2][ht]; v3 += t3[ow + 3][ht];
-        if constexpr (GATE) {
-          const float4 gz = g[j].get();
-          v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
+        if constexpr (GM == kGateBwd) {
+          // dy is read here, after the barrier, to keep the registers of the loads in flight
+          // before it at the gated forward's count
+          Gate4<T> gd;
+          gd.load(plane_rsrc(dy + p * L, pbytes / 4 * sizeof(T)), static_cast<uint32_t>(l));
+          const float4 gz = g[j].get(), gy = gd.get();
+          float g0, g1, g2, g3, z0, z1, z2, z3;
+          gate_bwd(v0, gz.x, gy.x, g0, z0);
+          gate_bwd(v1, gz.y, gy.y, g1, z1);
+          gate_bwd(v2, gz.z, gy.z, g2, z2);
+          gate_bwd(v3, gz.w, gy.w, g3, z3);
+          Out4<float>::store(y + p * L + l, g0, g1, g2, g3);
+          Out4<T>::store(dz + p * L + l, z0, z1, z2, z3);
+        } else {
+          if constexpr (GM == kGateFwd) {
+            const float4 gz = g[j].get();
+            v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z);
+            v3 *= silu_f32(gz.w);
+          }
+          Out4<T>::store(y + p * L + l, v0, v1, v2, v3);
         }
-        Out4<T>::store(y + p * L + l, v0, v1, v2, v3);
       }
     }
     __syncthreads();
   }
 }
 
-// Two-route merge (forward + reversed 1D sequence): y[l] = y0[l] + y1[L-1-l], times
-// SiLU(z[l]) with GATE.
-template <typename T, bool GATE>
+// Two-route merge (forward + reversed 1D sequence): v[l] = y0[l] + y1[L-1-l], and y = v,
+// v SiLU(z[l]) or the gate's backward (GM).
+template <typename T, int GM>
 __global__ void __launch_bounds__(256)
-k_merge2(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D, int L,
-         int64_t planes) {
+k_merge2(const float* __restrict__ yr, const T* __restrict__ z, const T* __restrict__ dy,
+         MergeOut<T, GM>* __restrict__ y, T* __restrict__ dz, int D, int L, int64_t planes) {
   const int l = blockIdx.x * blockDim.x + threadIdx.x;
   if (l >= L) return;
   for (int64_t p = blockIdx.y; p < planes; p += gridDim.y) {
@@ -405,8 +452,15 @@ k_merge2(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ 
     const float* y0 = yr + ((b * 2 + 0) * D + d) * L;
     const float* y1 = yr + ((b * 2 + 1) * D + d) * L;
     float v = y0[l] + y1[L - 1 - l];
-    if (GATE) v *= silu_f32(Elem<T>::load(z + p * L + l));
-    y[p * L + l] = Elem<T>::from_f32(v);
+    if constexpr (GM == kGateBwd) {
+      float g, dzv;
+      gate_bwd(v, Elem<T>::load(z + p * L + l), Elem<T>::load(dy + p * L + l), g, dzv);
+      y[p * L + l] = g;
+      dz[p * L + l] = Elem<T>::from_f32(dzv);
+    } else {
+      if (GM == kGateFwd) v *= silu_f32(Elem<T>::load(z + p * L + l));
+      y[p * L + l] = Elem<T>::from_f32(v);
+    }
   }
 }
 
@@ -415,10 +469,11 @@ k_merge2(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ 
 // are the outer dimension of the per-route buffer).  Each thread takes 4 consecutive
 // elements e .. e+3 of the run: route 0 with one 16-byte load, route 1 (reversed within each
 // plane of length L) with four 4-byte loads that may straddle a plane boundary.
-template <typename T, bool GATE>
+template <typename T, int GM>
 __global__ void __launch_bounds__(256)
-k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restrict__ y, int D,
-             int L, int64_t images) {
+k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, const T* __restrict__ dy,
+             MergeOut<T, GM>* __restrict__ y, T* __restrict__ dz, int D, int L,
+             int64_t images) {
   const int64_t run = static_cast<int64_t>(D) * L;
   const int64_t e = 4 * (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
   if (e >= run) return;
@@ -448,13 +503,27 @@ k_merge2_vec(const float* __restrict__ yr, const T* __restrict__ z, T* __restric
       for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load(y1 + src[i]);
     }
     float v0 = a.x + r[0], v1 = a.y + r[1], v2 = a.z + r[2], v3 = a.w + r[3];
-    if constexpr (GATE) {
-      In4<T> g;
+    if constexpr (GM == kGateBwd) {
+      In4<T> g, gd;
       g.load(z + b * run + e);
-      const float4 gz = g.get();
-      v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
+      gd.load(dy + b * run + e);
+      const float4 gz = g.get(), gy = gd.get();
+      float g0, g1, g2, g3, z0, z1, z2, z3;
+      gate_bwd(v0, gz.x, gy.x, g0, z0);
+      gate_bwd(v1, gz.y, gy.y, g1, z1);
+      gate_bwd(v2, gz.z, gy.z, g2, z2);
+      gate_bwd(v3, gz.w, gy.w, g3, z3);
+      Out4<float>::store(y + b * run + e, g0, g1, g2, g3);
+      Out4<T>::store(dz + b * run + e, z0, z1, z2, z3);
+    } else {
+      if constexpr (GM == kGateFwd) {
+        In4<T> g;
+        g.load(z + b * run + e);
+        const float4 gz = g.get();
+        v0 *= silu_f32(gz.x); v1 *= silu_f32(gz.y); v2 *= silu_f32(gz.z); v3 *= silu_f32(gz.w);
+      }
+      Out4<T>::store(y + b * run + e, v0, v1, v2, v3);
     }
-    Out4<T>::store(y + b * run + e, v0, v1, v2, v3);
   }
 }
 
@@ -501,7 +570,9 @@ k_bwd_reduce_bc4(const float* __restrict__ part, T* __restrict__ dBs, T* __restr
   Out4<T>::store(dst + (bk * N + (n2 % N)) * static_cast<int64_t>(L) + t, v.x, v.y, v.z, v.w);
 }
 
-// dA_log, dDs, ddt_bias: sums over images, in image order, of the per-image partials.
+// dA_log, dDs, ddt_bias: sums over images, in image order, of the per-image partials,
+// accumulated in fp64 and rounded once (these sums cancel: over a large batch, an fp32
+// running sum would add an error of up to B roundings of the partials' size).
 __global__ void __launch_bounds__(256)
 k_bwd_reduce_params(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
                     const float* __restrict__ dbias_part, float* __restrict__ dA_log,
@@ -519,9 +590,9 @@ k_bwd_reduce_params(const float* __restrict__ dA_part, const float* __restrict__
   } else {
     src = dbias_part + (i - nA - KD); stride = KD; dst = ddt_bias + (i - nA - KD);
   }
-  float v = 0.0f;
-  for (int b = 0; b < B; ++b) v += src[b * stride];
-  *dst = v;
+  double v = 0.0;
+  for (int b = 0; b < B; ++b) v += static_cast<double>(src[b * stride]);
+  *dst = static_cast<float>(v);
 }
 
 }  // namespace
@@ -613,87 +684,119 @@ int launch_carry(const ScanArgs& a, hipStream_t st) {
 
 namespace {
 
-// Launches one merge kernel instantiation for the element type and gate of the call.
-template <template <typename, bool> class Launch, typename... Args>
-int merge_dispatch(int dtype, const void* z, Args... args) {
-  if (dtype == 0)
-    return z ? Launch<float, true>::run(static_cast<const float*>(z), args...)
-             : Launch<float, false>::run(nullptr, args...);
-  return z ? Launch<uint16_t, true>::run(static_cast<const uint16_t*>(z), args...)
-           : Launch<uint16_t, false>::run(nullptr, args...);
+// Launches one merge kernel instantiation for the element type and gate mode of the call.
+template <template <typename, int> class Launch, typename... Args>
+int merge_dispatch(int dtype, int gm, const void* z, const void* dy, void* dz, Args... args) {
+  auto run = [&](auto tag) {
+    using T = decltype(tag);
+    const T* zt = static_cast<const T*>(z);
+    const T* dyt = static_cast<const T*>(dy);
+    T* dzt = static_cast<T*>(dz);
+    if (gm == kGateBwd) return Launch<T, kGateBwd>::run(zt, dyt, dzt, args...);
+    if (gm == kGateFwd) return Launch<T, kGateFwd>::run(zt, dyt, dzt, args...);
+    return Launch<T, kGateNone>::run(zt, dyt, dzt, args...);
+  };
+  return dtype == 0 ? run(float{}) : run(uint16_t{});
 }
 
-template <typename T, bool GATE>
+template <typename T, int GM>
 struct Merge4Vec {
-  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int H,
-                 int W, int64_t planes) {
-    hipLaunchKernelGGL((k_merge4_vec<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y),
-                       D, H, W, planes);
+  static int run(const T* z, const T* dy, T* dz, dim3 g, hipStream_t st, const float* yr,
+                 void* y, int D, int H, int W, int64_t planes) {
+    hipLaunchKernelGGL((k_merge4_vec<T, GM>), g, dim3(256), 0, st, yr, z, dy,
+                       static_cast<MergeOut<T, GM>*>(y), dz, D, H, W, planes);
     return static_cast<int>(hipGetLastError());
   }
 };
-template <typename T, bool GATE>
+template <typename T, int GM>
 struct Merge4 {
-  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int H,
-                 int W, int64_t planes) {
-    hipLaunchKernelGGL((k_merge4<T, GATE>), g, dim3(kTr, kTrRows), 0, st, yr, z,
-                       static_cast<T*>(y), D, H, W, planes);
+  static int run(const T* z, const T* dy, T* dz, dim3 g, hipStream_t st, const float* yr,
+                 void* y, int D, int H, int W, int64_t planes) {
+    hipLaunchKernelGGL((k_merge4<T, GM>), g, dim3(kTr, kTrRows), 0, st, yr, z, dy,
+                       static_cast<MergeOut<T, GM>*>(y), dz, D, H, W, planes);
     return static_cast<int>(hipGetLastError());
   }
 };
-template <typename T, bool GATE>
+template <typename T, int GM>
 struct Merge2Vec {
-  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int L,
-                 int64_t images) {
-    hipLaunchKernelGGL((k_merge2_vec<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y),
-                       D, L, images);
+  static int run(const T* z, const T* dy, T* dz, dim3 g, hipStream_t st, const float* yr,
+                 void* y, int D, int L, int64_t images) {
+    hipLaunchKernelGGL((k_merge2_vec<T, GM>), g, dim3(256), 0, st, yr, z, dy,
+                       static_cast<MergeOut<T, GM>*>(y), dz, D, L, images);
     return static_cast<int>(hipGetLastError());
   }
 };
-template <typename T, bool GATE>
+template <typename T, int GM>
 struct Merge2 {
-  static int run(const T* z, dim3 g, hipStream_t st, const float* yr, void* y, int D, int L,
-                 int64_t planes) {
-    hipLaunchKernelGGL((k_merge2<T, GATE>), g, dim3(256), 0, st, yr, z, static_cast<T*>(y), D,
-                       L, planes);
+  static int run(const T* z, const T* dy, T* dz, dim3 g, hipStream_t st, const float* yr,
+                 void* y, int D, int L, int64_t planes) {
+    hipLaunchKernelGGL((k_merge2<T, GM>), g, dim3(256), 0, st, yr, z, dy,
+                       static_cast<MergeOut<T, GM>*>(y), dz, D, L, planes);
     return static_cast<int>(hipGetLastError());
   }
 };
+
+bool aligned_to(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+int merge4(const float* y_route, int gm, const void* z, const void* dy, void* y, void* dz,
+           int B, int D, int H, int W, int dtype, hipStream_t st) {
+  const int64_t planes = static_cast<int64_t>(B) * D;
+  const unsigned gz = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
+  const uintptr_t out_align = dtype == 0 ? 16 : 8;
+  const bool aligned = aligned_to(y_route, 16) &&
+                       aligned_to(y, gm == kGateBwd ? 16 : out_align) &&
+                       aligned_to(z, out_align) && aligned_to(dy, out_align) &&
+                       aligned_to(dz, out_align);
+  if (aligned && H % 4 == 0 && W % 4 == 0)
+    return merge_dispatch<Merge4Vec>(dtype, gm, z, dy, dz,
+                                     dim3((W + 63) / 64, (H + 63) / 64, gz), st, y_route, y, D,
+                                     H, W, planes);
+  return merge_dispatch<Merge4>(dtype, gm, z, dy, dz,
+                                dim3((W + kTr - 1) / kTr, (H + kTr - 1) / kTr, gz), st, y_route,
+                                y, D, H, W, planes);
+}
+
+int merge2(const float* y_route, int gm, const void* z, const void* dy, void* y, void* dz,
+           int B, int D, int L, int dtype, hipStream_t st) {
+  const int64_t planes = static_cast<int64_t>(B) * D;
+  const unsigned gy = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
+  const uintptr_t out_align = dtype == 0 ? 16 : 8;
+  const bool aligned = aligned_to(y_route, 16) &&
+                       aligned_to(y, gm == kGateBwd ? 16 : out_align) &&
+                       aligned_to(z, out_align) && aligned_to(dy, out_align) &&
+                       aligned_to(dz, out_align);
+  const int64_t run = static_cast<int64_t>(D) * L;
+  if (aligned && run % 4 == 0) {
+    const unsigned gb = static_cast<unsigned>(B < kMaxGridZ ? B : kMaxGridZ);
+    return merge_dispatch<Merge2Vec>(dtype, gm, z, dy, dz,
+                                     dim3(static_cast<unsigned>((run / 4 + 255) / 256), gb), st,
+                                     y_route, y, D, L, static_cast<int64_t>(B));
+  }
+  return merge_dispatch<Merge2>(dtype, gm, z, dy, dz, dim3((L + 255) / 256, gy), st, y_route, y,
+                                D, L, planes);
+}
 
 }  // namespace
 
 int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, int H, int W,
                   int dtype, hipStream_t st) {
-  const int64_t planes = static_cast<int64_t>(B) * D;
-  const unsigned gz = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
-  const uintptr_t out_align = dtype == 0 ? 16 : 8;
-  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(y) % out_align == 0) &&
-                       (reinterpret_cast<uintptr_t>(z) % out_align == 0);
-  if (aligned && H % 4 == 0 && W % 4 == 0)
-    return merge_dispatch<Merge4Vec>(dtype, z, dim3((W + 63) / 64, (H + 63) / 64, gz), st,
-                                     y_route, y, D, H, W, planes);
-  return merge_dispatch<Merge4>(dtype, z, dim3((W + kTr - 1) / kTr, (H + kTr - 1) / kTr, gz), st,
-                                y_route, y, D, H, W, planes);
+  return merge4(y_route, z ? kGateFwd : kGateNone, z, nullptr, y, nullptr, B, D, H, W, dtype,
+                st);
 }
 
 int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L, int dtype,
                   hipStream_t st) {
-  const int64_t planes = static_cast<int64_t>(B) * D;
-  const unsigned gy = static_cast<unsigned>(planes < kMaxGridZ ? planes : kMaxGridZ);
-  const uintptr_t out_align = dtype == 0 ? 16 : 8;
-  const bool aligned = (reinterpret_cast<uintptr_t>(y_route) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(y) % out_align == 0) &&
-                       (reinterpret_cast<uintptr_t>(z) % out_align == 0);
-  const int64_t run = static_cast<int64_t>(D) * L;
-  if (aligned && run % 4 == 0) {
-    const unsigned gb = static_cast<unsigned>(B < kMaxGridZ ? B : kMaxGridZ);
-    return merge_dispatch<Merge2Vec>(dtype, z,
-                                     dim3(static_cast<unsigned>((run / 4 + 255) / 256), gb), st,
-                                     y_route, y, D, L, static_cast<int64_t>(B));
-  }
-  return merge_dispatch<Merge2>(dtype, z, dim3((L + 255) / 256, gy), st, y_route, y, D, L,
-                                planes);
+  return merge2(y_route, z ? kGateFwd : kGateNone, z, nullptr, y, nullptr, B, D, L, dtype, st);
+}
+
+int launch_merge4_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
+                           void* dz, int B, int D, int H, int W, int dtype, hipStream_t st) {
+  return merge4(y_route, kGateBwd, z, dy, g, dz, B, D, H, W, dtype, st);
+}
+
+int launch_merge2_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
+                           void* dz, int B, int D, int L, int dtype, hipStream_t st) {
+  return merge2(y_route, kGateBwd, z, dy, g, dz, B, D, L, dtype, st);
 }
 
 }  // namespace ss2d

@@ -1,6 +1,10 @@
-// bfloat16 instantiations of the backward scan kernel.
+// bfloat16 instantiations of the backward scan kernel (route gradient g in bfloat16, or in
+// fp32 for the gated operator).
 #include "ss2d_bwd.inc"
 
 namespace ss2d {
-int launch_scan_bwd_bf16(const BwdArgs& a, hipStream_t st) { return launch_scan_bwd_t<uint16_t>(a, st); }
+int launch_scan_bwd_bf16(const BwdArgs& a, hipStream_t st) {
+  return a.g_f32 ? launch_scan_bwd_t<uint16_t, float>(a, st)
+                 : launch_scan_bwd_t<uint16_t, uint16_t>(a, st);
+}
 }  // namespace ss2d

@@ -133,7 +133,7 @@ struct ScanArgs {
   int chunk_base;         // first chunk index covered by this launch
   int chunks_in_launch;   // chunks covered by this launch per (b, k)
   int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
-  int ck_tiles;           // kModeCkpt: 32-step tiles per sequence; h_in receives the states
+  int ck_tiles;           // kModeCkpt(Out): 32-step tiles per sequence; h_in gets the states
   int x_routes;           // nonzero: x_row holds each route's own input sequence
   const void* dt_lr;      // dt_proj folded in (else NULL): x_proj's dt rows (B, K, R, L) ...
   const float* dt_w;      // ... and the dt_proj weight (K, D, R): dt_raw = dt_w @ dt_lr
@@ -141,14 +141,14 @@ struct ScanArgs {
 };
 constexpr int kMaxLowRank = 4;  // dt rows a tile row of the scan's B/C LDS tile can hold
 
-enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2 };
+enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2, kModeCkptOut = 3 };
 
 // Arguments of the backward scan kernel (gradients of sum(dy * y), plain operator).
 struct BwdArgs {
   const void* x_row;      // x, (B, D, L)
   const void* x_col;      // x transposed per plane (routes 2 and 3)
-  const void* g_row;      // dy, (B, D, L)
-  const void* g_col;      // dy transposed per plane
+  const void* g_row;      // route gradient g (B, D, L): dy, or dy SiLU(z) for the gate
+  const void* g_col;      // g transposed per plane
   const void* dt_raw;     // (B, K, D, L)
   const void* Bs;         // (B, K, N, L)
   const void* Cs;         // (B, K, N, L)
@@ -165,6 +165,7 @@ struct BwdArgs {
   int B, K, D, L, N;
   int ck_tiles;           // ceil(L / 32)
   int n_cb;               // channel blocks per (b, k): ceil(D / 64)
+  int g_f32;              // nonzero: g is fp32 whatever the data type
 };
 
 // Arguments of the per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj).
@@ -218,6 +219,13 @@ int launch_merge4(const float* y_route, const void* z, void* y, int B, int D, in
                   int dtype, hipStream_t st);
 int launch_merge2(const float* y_route, const void* z, void* y, int B, int D, int L,
                   int dtype, hipStream_t st);
+// The gate's backward in place of the gated output: from the per-route outputs (the ungated
+// route sum v), z and dy (the element type and layout of y), g = dy SiLU(z) in fp32 and
+// dz = dy v SiLU'(z) in the element type.
+int launch_merge4_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
+                           void* dz, int B, int D, int H, int W, int dtype, hipStream_t st);
+int launch_merge2_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
+                           void* dz, int B, int D, int L, int dtype, hipStream_t st);
 // Bytes of the prepared weight images of one call (K * ceil(D / 64) images).
 size_t project_prep_bytes(int K, int D, int N, int R, int dtype);
 // Fills a.wprep (which must hold project_prep_bytes) from the weights, then runs the front

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 5
+    assert lib.ss2d_abi_version() == 6
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -198,6 +198,46 @@ def test_backward_argument_errors(lib):
     import torch
     if not torch.cuda.is_available():
         assert call_bwd(lib, ptrs) == bnd.SS2D_ERR_HIP
+
+
+def call_bwd_gated(lib, ptrs, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4):
+    if K == 4:
+        return lib.ss2d_backward_gated(*ptrs, B, D, H, W, N, dtype, None)
+    return lib.ss1d_bidir_backward_gated(*ptrs, B, D, H * W, N, dtype, None)
+
+
+def test_backward_gated_argument_errors(lib):
+    # x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy | dx, ddt_raw, dA_log, dBs, dCs, dDs,
+    # ddt_bias, dz
+    ptrs = fake_ptrs(17)
+    for K in (4, 2):
+        for i in range(17):
+            p = list(ptrs)
+            p[i] = None
+            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+        for N in (1, 2, 32, 3):
+            assert call_bwd_gated(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd_gated(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd_gated(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
+        assert call_bwd_gated(lib, [None] * 17, B=0, K=K) == bnd.SS2D_OK
+        for i in range(17):
+            p = list(ptrs)
+            p[i] += 1
+            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
+        for i in range(9, 16):  # a gradient inside its input
+            p = list(ptrs)
+            p[i] = p[i - 9] + 4
+            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i)
+        for j in (7, 8, 9, 15):  # dz inside z, dy, dx or ddt_bias
+            p = list(ptrs)
+            p[16] = p[j] + 4
+            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, j)
+        p = list(ptrs)
+        p[9] = p[7] + 8  # dx inside z
+        assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
+    import torch
+    if not torch.cuda.is_available():
+        assert call_bwd_gated(lib, ptrs) == bnd.SS2D_ERR_HIP
 
 
 # ---- per-route front end and the operator over per-route inputs ---------------------------
