@@ -79,8 +79,8 @@ class Oracle:
         lib.oracle_backward.argtypes = [ctypes.c_int] + [_f32p] * 8 + [_f64p] * 7 + \
             [ctypes.c_int64] * 5 + [ctypes.c_int]
         lib.oracle_backward_ex.restype = ctypes.c_int
-        lib.oracle_backward_ex.argtypes = [ctypes.c_int] + [_f32p] * 9 + [_f64p] * 8 + \
-            [ctypes.c_int64] * 5 + [ctypes.c_int]
+        lib.oracle_backward_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + [ctypes.c_int, _f32p] + \
+            [_f64p] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int]
         self.lib = lib
         self.last_threads = None
 
@@ -270,10 +270,12 @@ class Oracle:
         self.last_threads = rc
         return out
 
-    def backward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, threads=0, z=None):
+    def backward(self, K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, threads=0, z=None,
+                 zoh=False):
         """Gradients of sum(dy * y), float64, as a dict with keys x, dt_raw, A_log, Bs, Cs,
         Ds, dt_bias (each the shape of that input).  With the gate z (shape of x), y is the
-        gated output and the dict also holds z's gradient under "z"."""
+        gated output and the dict also holds z's gradient under "z"; zoh: y is the
+        zero-order-hold operator's output."""
         (B, D, H, W, N), keep, ptrs = self._prep(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
         dyk, dyp = self._gate(dy, x)
         if dyp is None:
@@ -285,13 +287,15 @@ class Oracle:
                    Cs=np.empty((B, K, N, L)), Ds=np.empty((K, D)), dt_bias=np.empty((K, D)))
         order = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
         outs = [out[k].ctypes.data_as(_f64p) for k in order]
-        if zp is None:
+        if zp is None and not zoh:
             rc = self.lib.oracle_backward(K, *ptrs, dyp, *outs, B, D, H, W, N, int(threads))
         else:
-            out["z"] = np.empty((B, D, L))
-            rc = self.lib.oracle_backward_ex(K, *ptrs, zp, dyp, *outs,
-                                             out["z"].ctypes.data_as(_f64p), B, D, H, W, N,
-                                             int(threads))
+            dzp = None
+            if zp is not None:
+                out["z"] = np.empty((B, D, L))
+                dzp = out["z"].ctypes.data_as(_f64p)
+            rc = self.lib.oracle_backward_ex(K, *ptrs, zp, 1 if zoh else 0, dyp, *outs, dzp,
+                                             B, D, H, W, N, int(threads))
         if rc < 0:
             raise RuntimeError("oracle_backward rejected its arguments")
         self.last_threads = rc

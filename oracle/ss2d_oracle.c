@@ -420,7 +420,14 @@ int oracle_project_lr(int K, const float *x, const float *conv_w, const float *c
  * Gated operator (the Vim block's gate, Vim summary section 4.3: out = y * SiLU(z) with y the
  * route sum above): by the product rule every route sees g = dy SiLU(z) in place of dy, and
  *   dz = dy y SiLU'(z),   SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))),
- * with y the ungated route sum, accumulated here from the same recomputed states. */
+ * with y the ungated route sum, accumulated here from the same recomputed states.
+ *
+ * Zero-order hold (ORACLE_ZOH; Vim summary section 4.1): the update is h = a h + bb B u with
+ * bb = expm1(delta A) / A, so in the sums above delta u becomes bb u and
+ *   dB_t,n = lambda bb u,    du_t = g D + sum_n lambda bb B,
+ *   ddelta_t = sum_n lambda a (h_prev A + B u)                  (d bb / d delta = a),
+ *   dA_n += lambda (h_prev a delta + B u d bb / dA),            d bb / dA = delta^2 psi(delta A),
+ *   psi(x) = (x e^x - expm1(x)) / x^2 = sum_k x^k (k + 1) / (k + 2)!   (psi(0) = 1/2). */
 
 static double sigmoid(double z) {
     return 1.0 / (1.0 + exp(-z));
@@ -432,16 +439,33 @@ static double silu_grad(double z) {
     return s * (1.0 + z * (1.0 - s));
 }
 
+/* psi(x) = (x e^x - (e^x - 1)) / x^2: its power series below |x| = 1/64 (terms to x^6,
+ * truncation below 1e-16 relative), the closed form above */
+static double zoh_psi(double x) {
+    if (fabs(x) < 1.0 / 64.0) {
+        double p = 0.0, f = 2.0; /* f = (k + 2)! */
+        double xk = 1.0;
+        for (int k = 0; k <= 6; ++k) {
+            p += xk * (double)(k + 1) / f;
+            xk *= x;
+            f *= (double)(k + 3);
+        }
+        return p;
+    }
+    return (x * exp(x) - expm1(x)) / (x * x);
+}
+
 /* One image b, all routes and channels.  Accumulates into dx_b (D, L), ddt_b (K, D, L),
  * dB_b, dC_b (K, N, L) and the parameter partials pA (K, D, N), pD (K, D), pbias (K, D);
  * with the gate z (else NULL), writes dz_b (D, L).  ws holds 2 L N + 3 L + 2 N doubles. */
 static void image_backward(int K, const float *x, const float *dt_raw, const float *A_log,
                            const float *Bs, const float *Cs, const float *Ds,
-                           const float *dt_bias, const float *z, const float *dy, int64_t D,
-                           int64_t H, int64_t W, int64_t N, int64_t b, double *dx_b,
-                           double *ddt_b, double *dB_b, double *dC_b, double *pA, double *pD,
-                           double *pbias, double *dz_b, double *ws) {
+                           const float *dt_bias, const float *z, int flags, const float *dy,
+                           int64_t D, int64_t H, int64_t W, int64_t N, int64_t b,
+                           double *dx_b, double *ddt_b, double *dB_b, double *dC_b, double *pA,
+                           double *pD, double *pbias, double *dz_b, double *ws) {
     const int64_t L = H * W;
+    const int zoh = (flags & ORACLE_ZOH) != 0;
     double *hs = ws;               /* h_t,n, t-major */
     double *as = hs + L * N;       /* a_t,n */
     double *delta = as + L * N;    /* delta_t */
@@ -471,8 +495,11 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                 for (int64_t n = 0; n < N; ++n) {
                     const double a = exp(delta[t] * A[n]);
                     const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;
+                    double bb = delta[t];
+                    if (zoh && A[n] != 0.0)
+                        bb = expm1(delta[t] * A[n]) / A[n];
                     as[t * N + n] = a;
-                    hs[t * N + n] = a * hprev + delta[t] * (double)Bk[n * L + t] * u;
+                    hs[t * N + n] = a * hprev + bb * (double)Bk[n * L + t] * u;
                     yroute += (double)Ck[n * L + t] * hs[t * N + n];
                 }
                 ysum[l] += yroute + Dk * u;
@@ -492,11 +519,21 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                     const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;
                     const double a = as[t * N + n];
                     const double da = lam[n] * hprev;
+                    const double Bv = (double)Bk[n * L + t];
+                    /* bb and its derivatives in delta and A */
+                    double bb = delta[t], bb_delta = 1.0, bb_A = 0.0;
+                    if (zoh) {
+                        bb_delta = a;
+                        bb_A = delta[t] * delta[t] * zoh_psi(delta[t] * A[n]);
+                        if (A[n] != 0.0)
+                            bb = expm1(delta[t] * A[n]) / A[n];
+                    }
                     dC_b[(k * N + n) * L + t] += g * hs[t * N + n];
-                    dB_b[(k * N + n) * L + t] += lam[n] * delta[t] * u;
-                    ddelta += da * a * A[n] + lam[n] * (double)Bk[n * L + t] * u;
-                    pA[(k * D + d) * N + n] += da * a * delta[t] * A[n];
-                    du += lam[n] * delta[t] * (double)Bk[n * L + t];
+                    dB_b[(k * N + n) * L + t] += lam[n] * bb * u;
+                    ddelta += da * a * A[n] + lam[n] * bb_delta * Bv * u;
+                    pA[(k * D + d) * N + n] +=
+                        (da * a * delta[t] + lam[n] * Bv * u * bb_A) * A[n];
+                    du += lam[n] * bb * Bv;
                 }
                 const double dr = ddelta * sigmoid((double)dt[t] + bias);
                 ddt_b[(k * D + d) * L + t] = dr;
@@ -513,15 +550,18 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
 /* Gradients of sum(dy * y) with respect to every input (outputs in double, caller-owned):
  *   dx (B, D, H, W), ddt_raw (B, K, D, L), dA_log (K, D, N), dBs, dCs (B, K, N, L),
  *   dDs, ddt_bias (K, D); with the gate z (B, D, H, W) (else NULL), y is the gated output
- *   and dz (B, D, H, W) receives its gradient with respect to z.
+ *   and dz (B, D, H, W) receives its gradient with respect to z; flags is 0 or ORACLE_ZOH
+ *   (the zero-order-hold operator).
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
 int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
                        const float *Bs, const float *Cs, const float *Ds,
-                       const float *dt_bias, const float *z, const float *dy, double *dx,
-                       double *ddt_raw, double *dA_log, double *dBs, double *dCs,
+                       const float *dt_bias, const float *z, int flags, const float *dy,
+                       double *dx, double *ddt_raw, double *dA_log, double *dBs, double *dCs,
                        double *dDs, double *ddt_bias, double *dz, int64_t B, int64_t D,
                        int64_t H, int64_t W, int64_t N, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
+        return -1;
+    if (flags & ~ORACLE_ZOH)
         return -1;
     if (K == 2 && H != 1)
         return -1;
@@ -553,8 +593,8 @@ int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *
 #endif
             for (int64_t b = 0; b < B; ++b) {
                 double *p = part + b * np;
-                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy, D, H, W, N,
-                               b, dx + b * D * L, ddt_raw + b * K * D * L,
+                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, dy, D, H,
+                               W, N, b, dx + b * D * L, ddt_raw + b * K * D * L,
                                dBs + b * K * N * L, dCs + b * K * N * L, p, p + K * D * N,
                                p + K * D * N + K * D, z ? dz + b * D * L : NULL, ws);
             }
@@ -586,6 +626,7 @@ int oracle_backward(int K, const float *x, const float *dt_raw, const float *A_l
                     const float *dy, double *dx, double *ddt_raw, double *dA_log, double *dBs,
                     double *dCs, double *dDs, double *ddt_bias, int64_t B, int64_t D,
                     int64_t H, int64_t W, int64_t N, int nthreads) {
-    return oracle_backward_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, dy, dx, ddt_raw,
-                              dA_log, dBs, dCs, dDs, ddt_bias, NULL, B, D, H, W, N, nthreads);
+    return oracle_backward_ex(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, NULL, 0, dy, dx,
+                              ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias, NULL, B, D, H, W, N,
+                              nthreads);
 }

@@ -30,6 +30,8 @@ What pins what:
   backward adjoint  <dy, y(v) - y(0)> = <grad, v> for the inputs y is affine in; dDs closed form
   backward gate     the gated output's gradients (z's included) against finite differences;
                     z = 0 and z = 40 reduce them to closed forms of the plain operator's
+  backward zoh      the zero-order hold's gradients against finite differences (both sides
+                    of the power series in delta A); A -> 0 reduces them to the plain ones
   project impulse   a unit impulse through the per-route causal conv gives the reversed taps
                     on the KW steps from the one that visits it, the bias elsewhere
   project brute     numpy.convolve, scipy.special.expit and matrix products on tiny inputs
@@ -561,6 +563,58 @@ def pin_backward_gate(orc):
         _close(at40["z"], dyd * y, 1e-13, 1e-15, f"gate at z = 40: dz, K={K}")
 
 
+def pin_backward_zoh(orc):
+    """Gradients of the zero-order-hold operator: every input's (and, gated, z's) element
+    by element against central finite differences of the ZOH forward oracle, with half of
+    the states at |delta A| ~ 1e-3 (the power-series side of d bb / dA) and half at
+    |delta A| ~ 0.1-1; and the limit A -> 0 (A_log = -30), where the hold's B term
+    expm1(delta A) / A equals delta to 1e-13: every gradient but dA_log then equals the plain
+    operator's (separately pinned) to that precision."""
+    rng = _rng(19)
+    for K, xshape, gated in ((4, (1, 2, 3, 4), True), (2, (2, 2, 7), False)):
+        B, D = xshape[:2]
+        L = int(np.prod(xshape[2:]))
+        N = 2
+        args = list(_random_inputs(rng, B, K, D, N, L, xshape))
+        args[2][..., 0] = rng.uniform(-7.0, -5.0, size=(K, D)).astype(np.float32)
+        dy = rng.standard_normal(xshape).astype(np.float32)
+        z = (1.5 * rng.standard_normal(xshape)).astype(np.float32) if gated else None
+        got = orc.backward(K, *args, dy, z=z, zoh=True)
+        dyd = dy.astype(np.float64)
+
+        def loss(a, zz):
+            return float(np.sum(orc.forward(K, *a, z=zz, zoh=True) * dyd))
+
+        names = BWD_NAMES + (("z",) if gated else ())
+        for i, name in enumerate(names):
+            base_arr = z if name == "z" else args[i]
+            flat = base_arr.reshape(-1)
+            fd = np.empty(flat.size)
+            for j in range(flat.size):
+                base = float(flat[j])
+                step = 1e-3 * max(1.0, abs(base))
+                hi, lo = np.float32(base + step), np.float32(base - step)
+                vals = []
+                for v in (hi, lo):
+                    pert = [a.copy() for a in args]
+                    zz = None if z is None else z.copy()
+                    (zz if name == "z" else pert[i]).reshape(-1)[j] = v
+                    vals.append(loss(pert, zz))
+                fd[j] = (vals[0] - vals[1]) / (float(hi) - float(lo))
+            g = got[name].reshape(-1)
+            scale = max(float(np.max(np.abs(fd))), 1e-12)
+            err = float(np.max(np.abs(g - fd))) / scale
+            assert err < 2e-5, f"ZOH d/d{name} (K={K}) differs from finite differences: {err:.2e}"
+
+        flat_a = list(args)
+        flat_a[2] = np.full_like(args[2], -30.0)
+        zoh0 = orc.backward(K, *flat_a, dy, z=z, zoh=True)
+        plain0 = orc.backward(K, *flat_a, dy, z=z)
+        for name in names:
+            if name != "A_log":
+                _close(zoh0[name], plain0[name], 1e-11, 1e-14, f"ZOH at A -> 0: d/d{name}")
+
+
 # ---- per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj) -----------------
 def _front_weights(rng, K, D, N, R, KW):
     conv_w = rng.standard_normal((K, D, KW)).astype(np.float32)
@@ -737,5 +791,6 @@ def pin_routes_lowrank(orc):
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
             pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
-            pin_backward_adjoint, pin_backward_gate, pin_project_impulse, pin_project_brute,
+            pin_backward_adjoint, pin_backward_gate, pin_backward_zoh, pin_project_impulse,
+            pin_project_brute,
             pin_project_select, pin_routes_variant, pin_routes_lowrank]

@@ -61,6 +61,16 @@ MUTATIONS = [
      "(double)gc[l] * sigmoid((double)zc[l]) : (double)gc[l];"),
     ("bwd gate: dz without the skip term", "ysum[l] += yroute + Dk * u;",
      "ysum[l] += yroute;"),
+    ("bwd zoh: d bb / d delta taken as 1", "bb_delta = a;", "bb_delta = 1.0;"),
+    ("bwd zoh: psi series coefficient", "p += xk * (double)(k + 1) / f;",
+     "p += xk * (double)(k + 2) / f;"),
+    ("bwd zoh: dA without the B u term", "(da * a * delta[t] + lam[n] * Bv * u * bb_A) * A[n];",
+     "(da * a * delta[t]) * A[n];"),
+    ("bwd zoh: psi closed form sign", "return (x * exp(x) - expm1(x)) / (x * x);",
+     "return (x * exp(x) + expm1(x)) / (x * x);"),
+    ("bwd zoh: B term of the recomputed forward left at delta",
+     "                    if (zoh && A[n] != 0.0)\n                        bb = expm1(delta[t] * A[n]) / A[n];\n                    as[t * N + n] = a;",
+     "                    as[t * N + n] = a;"),
     ("A_log indexed (K, N, D)", "A_log[(k * D + d) * N + n]);\n            h[n] = 0.0;",
      "A_log[(k * N + n) * D + d]);\n            h[n] = 0.0;"),
     ("Ds indexed (D, K)", "\n        const double Dk = Ds[k * D + d];",
@@ -80,7 +90,8 @@ MUTATIONS = [
      "bbar = exp(delta * A[n]) / A[n];"),
     ("ZOH divided by delta", "bbar = expm1(delta * A[n]) / A[n];",
      "bbar = expm1(delta * A[n]) / delta;"),
-    ("ZOH ignored", "if (zoh && A[n] != 0.0)", "if (0)"),
+    ("ZOH ignored", "if (zoh && A[n] != 0.0)\n                    bbar =",
+     "if (0)\n                    bbar ="),
     ("bwd: adjoint without decay", "lam[n] = g * (double)Ck[n * L + t] + anext * lam[n];",
      "lam[n] = g * (double)Ck[n * L + t] + lam[n];"),
     ("bwd: adjoint decays with the current step",
@@ -88,8 +99,8 @@ MUTATIONS = [
      "const double anext = as[t * N + n];"),
     ("bwd: dC from the previous state", "dC_b[(k * N + n) * L + t] += g * hs[t * N + n];",
      "dC_b[(k * N + n) * L + t] += g * hprev;"),
-    ("bwd: dB without delta", "dB_b[(k * N + n) * L + t] += lam[n] * delta[t] * u;",
-     "dB_b[(k * N + n) * L + t] += lam[n] * u;"),
+    ("bwd: B term without delta", "double bb = delta[t], bb_delta = 1.0, bb_A = 0.0;",
+     "double bb = 1.0, bb_delta = 1.0, bb_A = 0.0;"),
     ("bwd: decay derivative from the current state",
      "const double hprev = t > 0 ? hs[(t - 1) * N + n] : 0.0;\n"
      "                    const double a = as[t * N + n];",
@@ -99,8 +110,9 @@ MUTATIONS = [
      "ddelta += lam[n]"),
     ("bwd: softplus derivative without the bias", "sigmoid((double)dt[t] + bias)",
      "sigmoid((double)dt[t])"),
-    ("bwd: dA_log without the chain factor A", "pA[(k * D + d) * N + n] += da * a * delta[t] * A[n];",
-     "pA[(k * D + d) * N + n] += da * a * delta[t];"),
+    ("bwd: dA_log without the chain factor A",
+     "(da * a * delta[t] + lam[n] * Bv * u * bb_A) * A[n];",
+     "(da * a * delta[t] + lam[n] * Bv * u * bb_A);"),
     ("bwd: du without the skip term", "double ddelta = 0.0, du = g * Dk;",
      "double ddelta = 0.0, du = 0.0;"),
     ("bwd: dx at the scan step", "dx_b[d * L + l] += du;", "dx_b[d * L + t] += du;"),
