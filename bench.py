@@ -52,6 +52,15 @@ BWD_FLOPS_PER_UPDATE = 17
 BWD_ISSUE_SLOTS_PER_UPDATE = 12 + 2
 BWD_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / BWD_ISSUE_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE
                           / 1e12)
+# Backward with zero-order hold, per state update: the recompute (delta*A, (a - 1) / A as one
+# FMA, times u and B, the h update: 7 flops, one exp) and the adjoint (g*C and the lambda
+# update: 3; dC: 1; dB = lambda*(bb*u): 2; lambda*h_prev*a: 2; the sums over n for ddelta
+# (lambda h_prev a A and lambda a B) and du (lambda bb B): 8; dA with d bb / dA from a and
+# bb: 8): 31 flops in at least 22 VALU slots plus the exp.
+ZOH_BWD_FLOPS_PER_UPDATE = 31
+ZOH_BWD_ISSUE_SLOTS_PER_UPDATE = 22 + 2
+ZOH_BWD_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / ZOH_BWD_ISSUE_SLOTS_PER_UPDATE
+                              * ZOH_BWD_FLOPS_PER_UPDATE / 1e12)
 HBM_PEAK_GBPS = 8000.0
 ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
 
@@ -107,7 +116,7 @@ def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None) -> dict:
+def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None, zoh=False) -> dict:
     """The float64 oracle's backward (gated with z), as it is, on all host cores, over a
     bounded sample of whole images (its unit of work: dBs and dCs sum over every channel of
     an image)."""
@@ -118,7 +127,8 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None) -> dict:
     def run(n):
         sl = [inp[k][:n] if k in ("x", "dt_raw", "Bs", "Cs") else inp[k] for k in ARGS]
         t0 = time.perf_counter()
-        orc.backward(wl.K, *sl, dy[:n], threads=cores, z=None if z is None else z[:n])
+        orc.backward(wl.K, *sl, dy[:n], threads=cores, z=None if z is None else z[:n],
+                     zoh=zoh)
         return time.perf_counter() - t0
 
     n = min(wl.B, max(1, cores))
@@ -129,7 +139,8 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None) -> dict:
     upd = n * wl.K * wl.D * wl.L * wl.N
     return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
             "kind": "oracle",
-            "sample": f"{'gated ' if z is not None else ''}backward of {n} of {wl.B} images "
+            "sample": f"{'gated ' if z is not None else ''}{'zero-order-hold ' if zoh else ''}"
+                      f"backward of {n} of {wl.B} images "
                       f"of {wl.name} (all {wl.K} routes and {wl.D} channels), {upd:.3e} state "
                       f"updates in {dt:.2f} s"}
 
@@ -222,7 +233,7 @@ def main() -> int:
                     help="zero-order-hold discretisation of B")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward entry point (gradients of sum(dy * y); with "
-                         "--gate, of the gated output, z included)")
+                         "--gate and/or --zoh, of that operator's output, z included)")
     ap.add_argument("--front", action="store_true",
                     help="per-route front end: time ss2d_project (causal conv + SiLU, x_proj, "
                          "dt_proj) followed by ss2d_forward_routes on its outputs")
@@ -280,8 +291,8 @@ def main() -> int:
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    if args.backward and (args.zoh or args.front):
-        log("the backward entry points cover the plain and the gated operator only")
+    if args.backward and args.front:
+        log("the backward entry points cover the operator, not the front end")
         return 2
     z = None
     if gate is not None:
@@ -316,12 +327,12 @@ def main() -> int:
         g = workloads.make_output_grad(wl, 0)
         dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
               if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
-        if z is None:
+        if z is None and not args.zoh:
             fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
             call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
         else:
-            fn = ss.ss2d_backward_gated if wl.K == 4 else ss.ss1d_bidir_backward_gated
-            call = lambda: fn(*[dev[k] for k in ARGS], z, dy)  # noqa: E731
+            fn = ss.ss2d_backward_ex if wl.K == 4 else ss.ss1d_bidir_backward_ex
+            call = lambda: fn(*[dev[k] for k in ARGS], dy, z=z, zoh=args.zoh)  # noqa: E731
     elif args.gate or args.zoh:
         fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
         call = lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)  # noqa: E731
@@ -377,8 +388,10 @@ def main() -> int:
         scan_ms, scan_n = kernels["scan"]
         agg_ms, _ = kernels["chunk_agg"]
     scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
-    flops, peak = ((ZOH_FLOPS_PER_UPDATE, ZOH_UPDATE_PEAK_TFLOPS) if args.zoh
+    flops, peak = ((ZOH_BWD_FLOPS_PER_UPDATE, ZOH_BWD_UPDATE_PEAK_TFLOPS)
+                   if args.backward and args.zoh
                    else (BWD_FLOPS_PER_UPDATE, BWD_UPDATE_PEAK_TFLOPS) if args.backward
+                   else (ZOH_FLOPS_PER_UPDATE, ZOH_UPDATE_PEAK_TFLOPS) if args.zoh
                    else (FLOPS_PER_UPDATE, UPDATE_PEAK_TFLOPS))
     achieved = wl.updates * flops / scan_avg_s / 1e12
     traffic = measured_traffic(wl.name)
@@ -417,7 +430,7 @@ def main() -> int:
                                      lowrank=args.front_lowrank)
         elif args.backward:
             cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds,
-                                        z=gate["z"] if gate else None)
+                                        z=gate["z"] if gate else None, zoh=args.zoh)
         else:
             cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
                                zoh=args.zoh)

@@ -161,34 +161,44 @@ int ss1d_bidir_backward(const void *x, const void *dt_raw, const float *A_log,
                         float *dA_log, void *dBs, void *dCs, float *dDs, float *ddt_bias,
                         int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void *stream);
 
-/* ---- backward of the gated operator -------------------------------------------------------
- * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the gated
- * output of ss2d_forward_ex (ss1d_bidir_forward_ex) with gate z and flags 0:
- *   y = (sum over the routes of y_k) * SiLU(z)
- * (the gate of the Vim block, Vim summary section 4.3; the explainer's SelectiveSSM output
- * multiplied by the activated z branch).  By the product rule every route's output
- * receives g = dy * SiLU(z), and
+/* ---- backward of the gated and the zero-order-hold operator --------------------------------
+ * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output
+ * of ss2d_forward_ex (ss1d_bidir_forward_ex) with the same gate z and flags.  With z = NULL
+ * and flags = 0 this is ss2d_backward (ss1d_bidir_backward).
+ *
+ * Gate (z not NULL): y = (sum over the routes of y_k) * SiLU(z) (the gate of the Vim block,
+ * Vim summary section 4.3; the explainer's SelectiveSSM output multiplied by the activated
+ * z branch).  By the product rule every route's output receives g = dy * SiLU(z), and
  *   dz = dy * ys * SiLU'(z),   SiLU'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z))),
- * with ys the ungated route sum.  The other gradients are those of ss2d_backward with g in
- * place of dy.  z and dz (the shape and data type of x) are the only arguments beyond
- * ss2d_backward's; dz is written in full and must overlap neither an input nor another
- * output.  The checkpoint pass also writes the per-route outputs (scratch, fp32, as in the
- * forward), and the merge kernel forms g and dz from them; g stays in fp32 (scratch,
+ * with ys the ungated route sum; dz (the shape and data type of x) must then be given, is
+ * written in full and must overlap neither an input nor another output (with z = NULL, dz
+ * is not used).  The checkpoint pass also writes the per-route outputs (scratch, fp32, as
+ * in the forward), and the merge kernel forms g and dz from them; g stays in fp32 (scratch,
  * 4 B * B * D * L, twice that for the four routes' transposed copy) whatever the data type,
- * so that bfloat16 data lose nothing to a rounding of the gated gradient.  Everything else,
- * supported shapes and errors included, is as in ss2d_backward. */
-int ss2d_backward_gated(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
-                        const void *Cs, const float *Ds, const float *dt_bias, const void *z,
-                        const void *dy, void *dx, void *ddt_raw, float *dA_log, void *dBs,
-                        void *dCs, float *dDs, float *ddt_bias, void *dz, int64_t B, int64_t D,
-                        int64_t H, int64_t W, int64_t N, int dtype, void *stream);
+ * so that bfloat16 data lose nothing to a rounding of the gated gradient.
+ *
+ * SS2D_FLAG_ZOH: the zero-order-hold operator (Vim summary section 4.1), whose update is
+ * h = a h + bb B u with a = exp(delta A) and bb = (a - 1) / A.  The adjoint recurrence is
+ * unchanged; with bb in place of delta, dBs sums lambda * bb * u and dx sums
+ * lambda * bb * B; d bb / d delta = a, so ddelta takes sum_n lambda * a * B * u in place of
+ * sum_n lambda * B * u; and dA_log gains A * lambda * B * u * d bb / dA with
+ * d bb / dA = delta^2 * psi(delta A), psi(v) = (v e^v - (e^v - 1)) / v^2 (its power series
+ * for |v| < 1/4).
+ *
+ * Everything else, supported shapes and errors included, is as in ss2d_backward; flags
+ * other than SS2D_FLAG_ZOH give SS2D_ERR_UNSUPPORTED. */
+int ss2d_backward_ex(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                     const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                     const void *dy, void *dx, void *ddt_raw, float *dA_log, void *dBs,
+                     void *dCs, float *dDs, float *ddt_bias, void *dz, int64_t B, int64_t D,
+                     int64_t H, int64_t W, int64_t N, int dtype, int flags, void *stream);
 
-int ss1d_bidir_backward_gated(const void *x, const void *dt_raw, const float *A_log,
-                              const void *Bs, const void *Cs, const float *Ds,
-                              const float *dt_bias, const void *z, const void *dy, void *dx,
-                              void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
-                              float *ddt_bias, void *dz, int64_t B, int64_t D, int64_t L,
-                              int64_t N, int dtype, void *stream);
+int ss1d_bidir_backward_ex(const void *x, const void *dt_raw, const float *A_log,
+                           const void *Bs, const void *Cs, const float *Ds,
+                           const float *dt_bias, const void *z, const void *dy, void *dx,
+                           void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
+                           float *ddt_bias, void *dz, int64_t B, int64_t D, int64_t L,
+                           int64_t N, int dtype, int flags, void *stream);
 
 /* ---- per-route front end and the operator over per-route inputs ---------------------------
  * In the pages' per-direction modules every scan direction carries its own input layers: the

@@ -35,8 +35,8 @@ SIGNATURES = {
     "ss1d_bidir_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 5 + [ctypes.c_int, _P]),
     "ss1d_bidir_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 4 + [ctypes.c_int, _P]),
-    "ss2d_backward_gated": (ctypes.c_int, [_P] * 17 + [_I64] * 5 + [ctypes.c_int, _P]),
-    "ss1d_bidir_backward_gated": (ctypes.c_int, [_P] * 17 + [_I64] * 4 + [ctypes.c_int, _P]),
+    "ss2d_backward_ex": (ctypes.c_int, [_P] * 17 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_backward_ex": (ctypes.c_int, [_P] * 17 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_project": (ctypes.c_int, [_P] * 9 + [_I64] * 7 + [ctypes.c_int, _P]),
     "ss1d_bidir_project": (ctypes.c_int, [_P] * 9 + [_I64] * 6 + [ctypes.c_int, _P]),
     "ss2d_forward_routes": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
@@ -423,26 +423,29 @@ def ss1d_bidir_project_lr(x, conv_w, conv_b, x_proj_w, R, stream=None):
 GRAD_NAMES = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
 
 
-def _backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, xshape, L, z=None):
+def _backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, xshape, L, z=None,
+              zoh=False, ex=False):
     torch = _torch()
     lib = load_library()
     B, D, N, _ = _common(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, L)
     ins = (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
     grads = {name: torch.empty_like(t) for name, t in zip(GRAD_NAMES, ins)}
     dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
-    tail = (N, _dtype_code(x), _stream_handle(x.device, stream))
-    if z is None:
+    if not ex:
         args = [t.data_ptr() for t in ins] + [dy.data_ptr()] + \
             [grads[n].data_ptr() for n in GRAD_NAMES]
         fn = lib.ss2d_backward if K == 4 else lib.ss1d_bidir_backward
-        _check(fn(*args, *dims, *tail))
+        _check(fn(*args, *dims, N, _dtype_code(x), _stream_handle(x.device, stream)))
         return grads
-    _expect("z", z, xshape, x.dtype, x.device)
-    grads["z"] = torch.empty_like(z)
-    args = [t.data_ptr() for t in ins] + [z.data_ptr(), dy.data_ptr()] + \
-        [grads[n].data_ptr() for n in GRAD_NAMES] + [grads["z"].data_ptr()]
-    fn = lib.ss2d_backward_gated if K == 4 else lib.ss1d_bidir_backward_gated
-    _check(fn(*args, *dims, *tail))
+    if z is not None:
+        _expect("z", z, xshape, x.dtype, x.device)
+        grads["z"] = torch.empty_like(z)
+    args = [t.data_ptr() for t in ins] + [None if z is None else z.data_ptr(), dy.data_ptr()] + \
+        [grads[n].data_ptr() for n in GRAD_NAMES] + \
+        [None if z is None else grads["z"].data_ptr()]
+    fn = lib.ss2d_backward_ex if K == 4 else lib.ss1d_bidir_backward_ex
+    _check(fn(*args, *dims, N, _dtype_code(x), SS2D_FLAG_ZOH if zoh else 0,
+              _stream_handle(x.device, stream)))
     return grads
 
 
@@ -466,22 +469,26 @@ def ss1d_bidir_backward(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream=None):
     return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L)
 
 
-def ss2d_backward_gated(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy, stream=None):
-    """Gradients of sum(dy * y) for the gated y = ss2d_forward_ex(..., z=z): the dict of
-    ss2d_backward plus z's gradient under "z" (shape and dtype of z, which are x's)."""
+def ss2d_backward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None, zoh=False,
+                     stream=None):
+    """Gradients of sum(dy * y) for y = ss2d_forward_ex(..., z=z, zoh=zoh): the dict of
+    ss2d_backward, plus z's gradient under "z" (shape and dtype of z, which are x's) when
+    the gate is given."""
     if x.dim() != 4:
         raise ValueError("x must be (B, D, H, W)")
     B, D, H, W = x.shape
     return _backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, H, W), H * W,
-                     z=z)
+                     z=z, zoh=zoh, ex=True)
 
 
-def ss1d_bidir_backward_gated(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy, stream=None):
-    """ss2d_backward_gated for the gated y = ss1d_bidir_forward_ex(..., z=z)."""
+def ss1d_bidir_backward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None, zoh=False,
+                           stream=None):
+    """ss2d_backward_ex for y = ss1d_bidir_forward_ex(..., z=z, zoh=zoh)."""
     if x.dim() != 3:
         raise ValueError("x must be (B, D, L)")
     B, D, L = x.shape
-    return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L, z=z)
+    return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L, z=z,
+                     zoh=zoh, ex=True)
 
 
 def timing_enable(enable: bool = True) -> bool:

@@ -341,12 +341,15 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
 
 // ---- backward ----------------------------------------------------------------------------
 // z (not NULL): gradients of the gated output y SiLU(z); dz receives z's gradient.
+// flags: SS2D_FLAG_ZOH for the zero-order-hold operator.
 int backward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
              const void* Cs, const float* Ds, const float* dt_bias, const void* dy, void* dx,
              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
              int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream,
-             const void* z = nullptr, void* dz = nullptr, bool gated = false) {
+             const void* z = nullptr, void* dz = nullptr, int flags = 0) {
+  const bool gated = z != nullptr;
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
+  if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
   if (N != 4 && N != 8 && N != 16) return SS2D_ERR_UNSUPPORTED;
   if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
@@ -456,6 +459,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     a.chunk_base = 0;
     a.chunks_in_launch = 1;
     a.ck_tiles = int(tiles);
+    a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
     if (gated) a.y_route = reinterpret_cast<float*>(ws + off_du);
     Plan p;
     p.split = 4;
@@ -483,6 +487,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     g.g_row = static_cast<const char*>(g_img) + b0 * D * L * ge;
     g.g_col = static_cast<const char*>(gt) + b0 * D * L * ge;
     g.g_f32 = gated ? 1 : 0;
+    g.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
     g.dt_raw = static_cast<const char*>(dt_raw) + b0 * K * D * L * e;
     g.Bs = static_cast<const char*>(Bs) + b0 * K * N * L * e;
     g.Cs = static_cast<const char*>(Cs) + b0 * K * N * L * e;
@@ -689,23 +694,23 @@ int ss1d_bidir_backward(const void* x, const void* dt_raw, const float* A_log,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream);
 }
 
-int ss2d_backward_gated(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
-                        const void* Cs, const float* Ds, const float* dt_bias, const void* z,
-                        const void* dy, void* dx, void* ddt_raw, float* dA_log, void* dBs,
-                        void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B, int64_t D,
-                        int64_t H, int64_t W, int64_t N, int dtype, void* stream) {
+int ss2d_backward_ex(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                     const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                     const void* dy, void* dx, void* ddt_raw, float* dA_log, void* dBs,
+                     void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B, int64_t D,
+                     int64_t H, int64_t W, int64_t N, int dtype, int flags, void* stream) {
   return backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
-                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, true);
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, flags);
 }
 
-int ss1d_bidir_backward_gated(const void* x, const void* dt_raw, const float* A_log,
-                              const void* Bs, const void* Cs, const float* Ds,
-                              const float* dt_bias, const void* z, const void* dy, void* dx,
-                              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs,
-                              float* ddt_bias, void* dz, int64_t B, int64_t D, int64_t L,
-                              int64_t N, int dtype, void* stream) {
+int ss1d_bidir_backward_ex(const void* x, const void* dt_raw, const float* A_log,
+                           const void* Bs, const void* Cs, const float* Ds,
+                           const float* dt_bias, const void* z, const void* dy, void* dx,
+                           void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs,
+                           float* ddt_bias, void* dz, int64_t B, int64_t D, int64_t L,
+                           int64_t N, int dtype, int flags, void* stream) {
   return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
-                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, true);
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags);
 }
 
 int ss2d_project(const void* x, const float* conv_w, const float* conv_b,

@@ -53,6 +53,41 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return fmaxf(z, 0.0f) + l1p;
 }
 
+// Zero-order hold: B's factor (exp(delta A) - 1) / A = delta * phi(delta A) in one update,
+// with phi(v) = (e^v - 1) / v.  For |v| >= 1/16 the update's own exponential
+// a = exp(delta A) gives (a - 1) / A to within ~1e-6 relative (a - 1 is exact and a carries
+// one rounding); below that, a - 1 would lose digits to cancellation, and phi's Taylor
+// polynomial to v^3 (truncation <= v^4 / 120 < 2e-7) is used instead.  Written in
+// xa = delta A log2(e), the exponent the update already computes (v = xa ln 2); invA = 1 / A.
+constexpr float kZohSmallX = 0.0625f / 0.69314718f;      // |xa| below which the series is used
+constexpr float kZohP1 = 0.69314718f / 2.0f;             // ln2 / 2
+constexpr float kZohP2 = 0.48045301f / 6.0f;             // ln2^2 / 6
+constexpr float kZohP3 = 0.33302465f / 24.0f;            // ln2^3 / 24
+__device__ __forceinline__ float zoh_bbar(float dl, float xa, float an, float invA) {
+  const float series = dl * fmaf(xa, fmaf(xa, fmaf(xa, kZohP3, kZohP2), kZohP1), 1.0f);
+  const float direct = fmaf(an, invA, -invA);  // (a - 1) / A
+  return fabsf(xa) < kZohSmallX ? series : direct;
+}
+
+// Derivative in A of that factor: d/dA (exp(delta A) - 1) / A = (delta a - bbar) / A
+// = delta^2 psi(v), psi(v) = (v e^v - (e^v - 1)) / v^2 = sum_k v^k (k + 1) / (k + 2)!.  The
+// difference delta a - bbar ~ delta v / 2 cancels: from a and bbar (each good to about
+// 6e-8 / |v| relative) only for |v| >= 1/4 (~2e-6 relative there); below, psi's polynomial
+// to v^5 (truncation <= v^6 / 5760 relative to 1/2, < 1e-7), in xa as above.
+constexpr float kPsiSmallX = 0.25f / 0.69314718f;        // |xa| below which the series is used
+constexpr float kPsiQ1 = 0.69314718f / 3.0f;             // ln2 / 3
+constexpr float kPsiQ2 = 0.48045301f / 8.0f;             // ln2^2 / 8
+constexpr float kPsiQ3 = 0.33302465f / 30.0f;            // ln2^3 / 30
+constexpr float kPsiQ4 = 0.23083510f / 144.0f;           // ln2^4 / 144
+constexpr float kPsiQ5 = 0.16000270f / 840.0f;           // ln2^5 / 840
+__device__ __forceinline__ float zoh_bbar_dA(float dl, float xa, float an, float bbar,
+                                             float invA) {
+  const float poly = fmaf(xa, fmaf(xa, fmaf(xa, fmaf(xa, fmaf(xa, kPsiQ5, kPsiQ4), kPsiQ3),
+                                                kPsiQ2), kPsiQ1), 0.5f);
+  const float direct = fmaf(dl, an, -bbar) * invA;
+  return fabsf(xa) < kPsiSmallX ? dl * dl * poly : direct;
+}
+
 // Workgroups are handed to the 8 XCDs of the chip round-robin in linear launch order, and
 // each XCD has its own L2.  This maps the linear workgroup index to a logical one so that
 // logically consecutive workgroups (which share inputs) run on the same XCD: XCD j gets
@@ -166,6 +201,7 @@ struct BwdArgs {
   int ck_tiles;           // ceil(L / 32)
   int n_cb;               // channel blocks per (b, k): ceil(D / 64)
   int g_f32;              // nonzero: g is fp32 whatever the data type
+  int zoh;                // nonzero: the zero-order-hold operator
 };
 
 // Arguments of the per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj).
@@ -207,6 +243,8 @@ int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dt
 int launch_carry(const ScanArgs& a, hipStream_t st);
 int launch_scan_bwd_f32(const BwdArgs& a, hipStream_t st);
 int launch_scan_bwd_bf16(const BwdArgs& a, hipStream_t st);
+int launch_scan_bwd_f32_zoh(const BwdArgs& a, hipStream_t st);
+int launch_scan_bwd_bf16_zoh(const BwdArgs& a, hipStream_t st);
 // Sums of the backward partials: dBs, dCs over channel blocks; dA_log, dDs, dt_bias over
 // images (fixed order).
 int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, int N, int L,

@@ -200,44 +200,56 @@ def test_backward_argument_errors(lib):
         assert call_bwd(lib, ptrs) == bnd.SS2D_ERR_HIP
 
 
-def call_bwd_gated(lib, ptrs, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4):
+def call_bwd_ex(lib, ptrs, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4, flags=0):
     if K == 4:
-        return lib.ss2d_backward_gated(*ptrs, B, D, H, W, N, dtype, None)
-    return lib.ss1d_bidir_backward_gated(*ptrs, B, D, H * W, N, dtype, None)
+        return lib.ss2d_backward_ex(*ptrs, B, D, H, W, N, dtype, flags, None)
+    return lib.ss1d_bidir_backward_ex(*ptrs, B, D, H * W, N, dtype, flags, None)
 
 
-def test_backward_gated_argument_errors(lib):
+def test_backward_ex_argument_errors(lib):
     # x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy | dx, ddt_raw, dA_log, dBs, dCs, dDs,
     # ddt_bias, dz
     ptrs = fake_ptrs(17)
     for K in (4, 2):
         for i in range(17):
+            if i == 7:  # z = NULL: no gate
+                continue
             p = list(ptrs)
             p[i] = None
-            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
+            assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
         for N in (1, 2, 32, 3):
-            assert call_bwd_gated(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
-        assert call_bwd_gated(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
-        assert call_bwd_gated(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
-        assert call_bwd_gated(lib, [None] * 17, B=0, K=K) == bnd.SS2D_OK
+            assert call_bwd_ex(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd_ex(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call_bwd_ex(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
+        assert call_bwd_ex(lib, [None] * 17, B=0, K=K) == bnd.SS2D_OK
         for i in range(17):
             p = list(ptrs)
             p[i] += 1
-            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
+            assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_ALIGN, (K, i)
         for i in range(9, 16):  # a gradient inside its input
             p = list(ptrs)
             p[i] = p[i - 9] + 4
-            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i)
+            assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, i)
         for j in (7, 8, 9, 15):  # dz inside z, dy, dx or ddt_bias
             p = list(ptrs)
             p[16] = p[j] + 4
-            assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, j)
+            assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_ALIAS, (K, j)
         p = list(ptrs)
         p[9] = p[7] + 8  # dx inside z
-        assert call_bwd_gated(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
+        assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
+        for flags in (2, 3, -1):
+            assert call_bwd_ex(lib, ptrs, K=K, flags=flags) == bnd.SS2D_ERR_UNSUPPORTED
+        # without the gate, z and dz are not used: NULL is fine, so is a dz that would alias
+        p = list(ptrs)
+        p[7] = None
+        p[16] = p[0]
+        import torch
+        if not torch.cuda.is_available():
+            assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_HIP
+            assert call_bwd_ex(lib, p, K=K, flags=bnd.SS2D_FLAG_ZOH) == bnd.SS2D_ERR_HIP
     import torch
     if not torch.cuda.is_available():
-        assert call_bwd_gated(lib, ptrs) == bnd.SS2D_ERR_HIP
+        assert call_bwd_ex(lib, ptrs) == bnd.SS2D_ERR_HIP
 
 
 # ---- per-route front end and the operator over per-route inputs ---------------------------
