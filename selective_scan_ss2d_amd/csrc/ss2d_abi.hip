@@ -372,7 +372,8 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
   for (const void* ptr : {x, dt_raw, Bs, Cs, dy, z, static_cast<const void*>(dx),
                           static_cast<const void*>(ddt_raw), static_cast<const void*>(dBs),
-                          static_cast<const void*>(dCs), static_cast<const void*>(dz)})
+                          static_cast<const void*>(dCs),
+                          gated ? static_cast<const void*>(dz) : nullptr})
     if (reinterpret_cast<uintptr_t>(ptr) & emask) return SS2D_ERR_ALIGN;
   for (const void* ptr : {static_cast<const void*>(A_log), static_cast<const void*>(Ds),
                           static_cast<const void*>(dt_bias), static_cast<const void*>(dA_log),

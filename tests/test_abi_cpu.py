@@ -240,9 +240,10 @@ def test_backward_ex_argument_errors(lib):
         for flags in (2, 3, -1):
             assert call_bwd_ex(lib, ptrs, K=K, flags=flags) == bnd.SS2D_ERR_UNSUPPORTED
         # without the gate, z and dz are not used: NULL is fine, so is a dz that would alias
+        # or is misaligned
         p = list(ptrs)
         p[7] = None
-        p[16] = p[0]
+        p[16] = p[0] + 1
         import torch
         if not torch.cuda.is_available():
             assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_HIP
