@@ -62,6 +62,8 @@ SHAPES = [  # B, D, H, W, N, K, dtype
     (3, 100, 1, 197, 16, 2, "bf16"),
     (2, 64, 1, 320, 16, 2, "f32"),
     (1, 65, 1, 37, 4, 2, "f32"),
+    (1, 33, 1, 40, 8, 4, "f32"),      # degenerate maps: the column routes need no transpose
+    (2, 24, 17, 1, 16, 4, "bf16"),
 ]
 
 
