@@ -147,7 +147,8 @@ int ss1d_bidir_forward_ex(const void *x, const void *dt_raw, const float *A_log,
  * 32 steps (scratch, 4 B * B * K * D * ceil(L / 32) * N); sums over channels and images are
  * taken in a fixed order, so results are deterministic.
  *
- * Supported: the plain operator (no gate, delta * B) with N in {4, 8, 16}; other N give
+ * Supported: the plain operator (no gate, delta * B; ss2d_backward_ex below takes the gate
+ * and the zero-order hold) with N in {4, 8, 16}; other N give
  * SS2D_ERR_UNSUPPORTED.  Otherwise the conventions of ss2d_forward apply. */
 int ss2d_backward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
                   const void *Cs, const float *Ds, const float *dt_bias, const void *dy,
