@@ -81,6 +81,8 @@ class Oracle:
         lib.oracle_backward_ex.restype = ctypes.c_int
         lib.oracle_backward_ex.argtypes = [ctypes.c_int] + [_f32p] * 8 + [ctypes.c_int, _f32p] + \
             [_f64p] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int]
+        lib.oracle_backward_routes_ex.restype = ctypes.c_int
+        lib.oracle_backward_routes_ex.argtypes = lib.oracle_backward_ex.argtypes
         self.lib = lib
         self.last_threads = None
 
@@ -182,6 +184,43 @@ class Oracle:
             raise RuntimeError("oracle_forward_routes_ex rejected its arguments")
         self.last_threads = rc
         return y.reshape(xshape)
+
+    def backward_routes(self, K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, H, W, threads=0,
+                        z=None, zoh=False):
+        """Gradients of sum(dy * y) for y = forward_routes(...), float64, as a dict with keys
+        u (B, K, D, L: each route's own input, per step), dt_raw, A_log, Bs, Cs, Ds, dt_bias,
+        and z (with the gate)."""
+        u = np.asarray(u)
+        if u.ndim != 4 or u.shape[1] != K or u.shape[3] != H * W:
+            raise ValueError(f"u has shape {u.shape}, expected (B, {K}, D, {H * W})")
+        B, _, D, L = u.shape
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        (_, _, _, _, N), keep, ptrs = self._prep(K, None, dt_raw, A_log, Bs, Cs, Ds, dt_bias,
+                                                 xshape=xshape)
+        uk, up = self._f32(u)
+        ref = np.broadcast_to(np.float32(0), xshape)
+        dyk, dyp = self._gate(dy, ref)
+        if dyp is None:
+            raise ValueError("dy is required")
+        zk, zp = self._gate(z, ref)
+        out = dict(u=np.empty((B, K, D, L)), dt_raw=np.empty((B, K, D, L)),
+                   A_log=np.empty((K, D, N)), Bs=np.empty((B, K, N, L)),
+                   Cs=np.empty((B, K, N, L)), Ds=np.empty((K, D)), dt_bias=np.empty((K, D)))
+        order = ("u", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+        dzp = None
+        if zp is not None:
+            out["z"] = np.empty((B, D, L))
+            dzp = out["z"].ctypes.data_as(_f64p)
+        rc = self.lib.oracle_backward_routes_ex(K, up, *ptrs[1:], zp, ORACLE_ZOH if zoh else 0,
+                                                dyp, *[out[k].ctypes.data_as(_f64p)
+                                                       for k in order],
+                                                dzp, B, D, H, W, N, int(threads))
+        if rc < 0:
+            raise RuntimeError("oracle_backward_routes_ex rejected its arguments")
+        self.last_threads = rc
+        if zp is not None:
+            out["z"] = out["z"].reshape(xshape)
+        return out
 
     def forward_routes_lr(self, K, u, dt_lr, dt_w, A_log, Bs, Cs, Ds, dt_bias, H, W,
                           threads=0, z=None, zoh=False):

@@ -458,12 +458,12 @@ static double zoh_psi(double x) {
 /* One image b, all routes and channels.  Accumulates into dx_b (D, L), ddt_b (K, D, L),
  * dB_b, dC_b (K, N, L) and the parameter partials pA (K, D, N), pD (K, D), pbias (K, D);
  * with the gate z (else NULL), writes dz_b (D, L).  ws holds 2 L N + 3 L + 2 N doubles. */
-static void image_backward(int K, const float *x, const float *dt_raw, const float *A_log,
-                           const float *Bs, const float *Cs, const float *Ds,
-                           const float *dt_bias, const float *z, int flags, const float *dy,
-                           int64_t D, int64_t H, int64_t W, int64_t N, int64_t b,
-                           double *dx_b, double *ddt_b, double *dB_b, double *dC_b, double *pA,
-                           double *pD, double *pbias, double *dz_b, double *ws) {
+static void image_backward(int K, const float *x, const float *u_routes, const float *dt_raw,
+                           const float *A_log, const float *Bs, const float *Cs,
+                           const float *Ds, const float *dt_bias, const float *z, int flags,
+                           const float *dy, int64_t D, int64_t H, int64_t W, int64_t N,
+                           int64_t b, double *dx_b, double *ddt_b, double *dB_b, double *dC_b,
+                           double *pA, double *pD, double *pbias, double *dz_b, double *ws) {
     const int64_t L = H * W;
     const int zoh = (flags & ORACLE_ZOH) != 0;
     double *hs = ws;               /* h_t,n, t-major */
@@ -473,7 +473,7 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
     double *A = lam + N;           /* A_n */
     double *ysum = A + N;          /* ungated route sum y_l (gate only) */
     for (int64_t d = 0; d < D; ++d) {
-        const float *xc = x + (b * D + d) * L;
+        const float *xc = u_routes ? NULL : x + (b * D + d) * L;
         const float *gc = dy + (b * D + d) * L;
         const float *zc = z ? z + (b * D + d) * L : NULL;
         for (int64_t l = 0; l < L; ++l)
@@ -484,12 +484,13 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
             const float *dt = dt_raw + ((b * K + k) * D + d) * L;
             const float *Bk = Bs + (b * K + k) * N * L;
             const float *Ck = Cs + (b * K + k) * N * L;
+            const float *uk = u_routes ? u_routes + ((b * K + k) * D + d) * L : NULL;
             for (int64_t n = 0; n < N; ++n)
                 A[n] = -exp((double)A_log[(k * D + d) * N + n]);
             /* forward, keeping every state */
             for (int64_t t = 0; t < L; ++t) {
                 const int64_t l = route_position(K, k, t, H, W);
-                const double u = xc[l];
+                const double u = uk ? (double)uk[t] : (double)xc[l];
                 delta[t] = softplus((double)dt[t] + bias);
                 double yroute = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
@@ -509,7 +510,7 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                 lam[n] = 0.0;
             for (int64_t t = L - 1; t >= 0; --t) {
                 const int64_t l = route_position(K, k, t, H, W);
-                const double u = xc[l];
+                const double u = uk ? (double)uk[t] : (double)xc[l];
                 const double g = zc ? (double)gc[l] * silu((double)zc[l]) : (double)gc[l];
                 double ddelta = 0.0, du = g * Dk;
                 pD[k * D + d] += g * u;
@@ -538,7 +539,10 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
                 const double dr = ddelta * sigmoid((double)dt[t] + bias);
                 ddt_b[(k * D + d) * L + t] = dr;
                 pbias[k * D + d] += dr;
-                dx_b[d * L + l] += du;
+                if (uk)
+                    dx_b[(k * D + d) * L + t] = du; /* du per route, in scan order */
+                else
+                    dx_b[d * L + l] += du;
             }
         }
         if (zc)
@@ -553,12 +557,12 @@ static void image_backward(int K, const float *x, const float *dt_raw, const flo
  *   and dz (B, D, H, W) receives its gradient with respect to z; flags is 0 or ORACLE_ZOH
  *   (the zero-order-hold operator).
  * Returns the number of threads used, or -1 on bad arguments / allocation failure. */
-int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
-                       const float *Bs, const float *Cs, const float *Ds,
-                       const float *dt_bias, const float *z, int flags, const float *dy,
-                       double *dx, double *ddt_raw, double *dA_log, double *dBs, double *dCs,
-                       double *dDs, double *ddt_bias, double *dz, int64_t B, int64_t D,
-                       int64_t H, int64_t W, int64_t N, int nthreads) {
+static int backward_all(int K, const float *x, const float *u_routes, const float *dt_raw,
+                        const float *A_log, const float *Bs, const float *Cs, const float *Ds,
+                        const float *dt_bias, const float *z, int flags, const float *dy,
+                        double *dx, double *ddt_raw, double *dA_log, double *dBs, double *dCs,
+                        double *dDs, double *ddt_bias, double *dz, int64_t B, int64_t D,
+                        int64_t H, int64_t W, int64_t N, int nthreads) {
     if ((K != 2 && K != 4) || B < 0 || D < 0 || H < 0 || W < 0 || N <= 0)
         return -1;
     if (flags & ~ORACLE_ZOH)
@@ -573,7 +577,7 @@ int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *
     double *part = (double *)calloc((size_t)(B > 0 ? B : 1) * (size_t)np, sizeof(double));
     if (!part)
         return -1;
-    for (int64_t i = 0; i < B * D * L; ++i)
+    for (int64_t i = 0; i < (u_routes ? K : 1) * B * D * L; ++i)
         dx[i] = 0.0;
     for (int64_t i = 0; i < B * K * N * L; ++i) {
         dBs[i] = 0.0;
@@ -593,8 +597,9 @@ int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *
 #endif
             for (int64_t b = 0; b < B; ++b) {
                 double *p = part + b * np;
-                image_backward(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, dy, D, H,
-                               W, N, b, dx + b * D * L, ddt_raw + b * K * D * L,
+                image_backward(K, x, u_routes, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags,
+                               dy, D, H, W, N, b,
+                               dx + b * (u_routes ? K : 1) * D * L, ddt_raw + b * K * D * L,
                                dBs + b * K * N * L, dCs + b * K * N * L, p, p + K * D * N,
                                p + K * D * N + K * D, z ? dz + b * D * L : NULL, ws);
             }
@@ -618,6 +623,35 @@ int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *
     }
     free(part);
     return failed ? -1 : threads;
+}
+
+int oracle_backward_ex(int K, const float *x, const float *dt_raw, const float *A_log,
+                       const float *Bs, const float *Cs, const float *Ds,
+                       const float *dt_bias, const float *z, int flags, const float *dy,
+                       double *dx, double *ddt_raw, double *dA_log, double *dBs, double *dCs,
+                       double *dDs, double *ddt_bias, double *dz, int64_t B, int64_t D,
+                       int64_t H, int64_t W, int64_t N, int nthreads) {
+    return backward_all(K, x, NULL, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, dy, dx,
+                        ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias, dz, B, D, H, W, N,
+                        nthreads);
+}
+
+/* The same for the operator over per-route inputs (oracle_forward_routes_ex): u (B, K, D, L)
+ * in each route's scan order in place of x, and du (B, K, D, L), the gradient of each
+ * route's own input at each step, in place of dx (the routes do not share their input, so
+ * nothing is summed across routes). */
+int oracle_backward_routes_ex(int K, const float *u, const float *dt_raw, const float *A_log,
+                              const float *Bs, const float *Cs, const float *Ds,
+                              const float *dt_bias, const float *z, int flags,
+                              const float *dy, double *du, double *ddt_raw, double *dA_log,
+                              double *dBs, double *dCs, double *dDs, double *ddt_bias,
+                              double *dz, int64_t B, int64_t D, int64_t H, int64_t W,
+                              int64_t N, int nthreads) {
+    if (!u)
+        return -1;
+    return backward_all(K, NULL, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, flags, dy, du,
+                        ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias, dz, B, D, H, W, N,
+                        nthreads);
 }
 
 /* The plain operator's gradients (no gate). */

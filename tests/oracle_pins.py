@@ -32,6 +32,8 @@ What pins what:
                     z = 0 and z = 40 reduce them to closed forms of the plain operator's
   backward zoh      the zero-order hold's gradients against finite differences (both sides
                     of the power series in delta A); A -> 0 reduces them to the plain ones
+  backward routes   the operator over per-route inputs: fed the gathers of one x it gives
+                    the plain backward exactly; its gradients against finite differences
   project impulse   a unit impulse through the per-route causal conv gives the reversed taps
                     on the KW steps from the one that visits it, the bias elsewhere
   project brute     numpy.convolve, scipy.special.expit and matrix products on tiny inputs
@@ -615,6 +617,68 @@ def pin_backward_zoh(orc):
                 _close(zoh0[name], plain0[name], 1e-11, 1e-14, f"ZOH at A -> 0: d/d{name}")
 
 
+def pin_backward_routes(orc):
+    """Gradients of the operator over per-route inputs: fed every route's gather of one x,
+    each route's du summed back at the positions it visits (in route order) is the plain
+    backward's dx, and every other gradient is the plain backward's, exactly (the same
+    double arithmetic), with the gate and the hold as well; and with four different inputs,
+    every gradient (u's per route and step) against central finite differences of the
+    routes operator."""
+    for K, H, W in ((4, 3, 4), (2, 1, 7)):
+        B, D, N = 2, 2, 2
+        L = H * W
+        rng = _rng(20 + K)
+        xshape = (B, D, H, W) if K == 4 else (B, D, L)
+        routes = _routes(H, W, K)
+        x, dt, A_log, Bs, Cs, Ds, bias = _random_inputs(rng, B, K, D, N, L, xshape=xshape)
+        dy = rng.standard_normal(xshape).astype(np.float32)
+        z = (1.5 * rng.standard_normal(xshape)).astype(np.float32)
+        xf = x.reshape(B, D, L)
+        u = np.stack([xf[:, :, routes[k]] for k in range(K)], axis=1)
+        for zoh, gate in ((False, None), (True, z)):
+            want = orc.backward(K, x, dt, A_log, Bs, Cs, Ds, bias, dy, z=gate, zoh=zoh)
+            got = orc.backward_routes(K, u, dt, A_log, Bs, Cs, Ds, bias, dy, H, W, z=gate,
+                                      zoh=zoh)
+            dx = np.zeros((B, D, L))
+            for k in range(K):
+                dx[:, :, routes[k]] = dx[:, :, routes[k]] + got["u"][:, k]
+            _close(dx.reshape(xshape), want["x"], 0.0, 0.0, f"routes du -> dx, K={K}")
+            for name in BWD_NAMES[1:] + (("z",) if gate is not None else ()):
+                _close(got[name], want[name], 0.0, 0.0, f"routes d/d{name}, K={K}, zoh={zoh}")
+
+        u = rng.standard_normal((B, K, D, L)).astype(np.float32)
+        gate = z if K == 4 else None
+        got = orc.backward_routes(K, u, dt, A_log, Bs, Cs, Ds, bias, dy, H, W, z=gate,
+                                  zoh=True)
+        args = [u, dt, A_log, Bs, Cs, Ds, bias]
+        dyd = dy.astype(np.float64)
+
+        def loss(a, zz):
+            return float(np.sum(orc.forward_routes(K, a[0], *a[1:], H, W, z=zz, zoh=True)
+                                * dyd))
+
+        names = ("u",) + BWD_NAMES[1:] + (("z",) if gate is not None else ())
+        for i, name in enumerate(names):
+            base_arr = gate if name == "z" else args[i]
+            flat = base_arr.reshape(-1)
+            fd = np.empty(flat.size)
+            for j in range(flat.size):
+                base = float(flat[j])
+                step = 1e-3 * max(1.0, abs(base))
+                hi, lo = np.float32(base + step), np.float32(base - step)
+                vals = []
+                for v in (hi, lo):
+                    pert = [a.copy() for a in args]
+                    zz = None if gate is None else gate.copy()
+                    (zz if name == "z" else pert[i]).reshape(-1)[j] = v
+                    vals.append(loss(pert, zz))
+                fd[j] = (vals[0] - vals[1]) / (float(hi) - float(lo))
+            g = got[name].reshape(-1)
+            scale = max(float(np.max(np.abs(fd))), 1e-12)
+            err = float(np.max(np.abs(g - fd))) / scale
+            assert err < 2e-5, f"routes d/d{name} (K={K}) differs from finite differences: {err:.2e}"
+
+
 # ---- per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj) -----------------
 def _front_weights(rng, K, D, N, R, KW):
     conv_w = rng.standard_normal((K, D, KW)).astype(np.float32)
@@ -791,6 +855,7 @@ def pin_routes_lowrank(orc):
 ALL_PINS = [pin_brute_force, pin_geometric, pin_convolve, pin_lfilter, pin_halving,
             pin_small_delta, pin_memoryless, pin_routes, pin_flip, pin_transpose, pin_rot180,
             pin_linearity, pin_channels, pin_gate, pin_zoh_exact, pin_backward_fd,
-            pin_backward_adjoint, pin_backward_gate, pin_backward_zoh, pin_project_impulse,
+            pin_backward_adjoint, pin_backward_gate, pin_backward_zoh, pin_backward_routes,
+            pin_project_impulse,
             pin_project_brute,
             pin_project_select, pin_routes_variant, pin_routes_lowrank]

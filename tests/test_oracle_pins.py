@@ -68,6 +68,14 @@ MUTATIONS = [
      "(da * a * delta[t]) * A[n];"),
     ("bwd zoh: psi closed form sign", "return (x * exp(x) - expm1(x)) / (x * x);",
      "return (x * exp(x) + expm1(x)) / (x * x);"),
+    ("bwd routes: every route reads route 0's input",
+     "const float *uk = u_routes ? u_routes + ((b * K + k) * D + d) * L : NULL;\n"
+     "            for (int64_t n = 0; n < N; ++n)\n                A[n] = -exp(",
+     "const float *uk = u_routes ? u_routes + ((b * K) * D + d) * L : NULL;\n"
+     "            for (int64_t n = 0; n < N; ++n)\n                A[n] = -exp("),
+    ("bwd routes: du written at the image position",
+     "dx_b[(k * D + d) * L + t] = du; /* du per route, in scan order */",
+     "dx_b[(k * D + d) * L + route_position(K, k, t, H, W)] = du;"),
     ("bwd zoh: B term of the recomputed forward left at delta",
      "                    if (zoh && A[n] != 0.0)\n                        bb = expm1(delta[t] * A[n]) / A[n];\n                    as[t * N + n] = a;",
      "                    as[t * N + n] = a;"),
@@ -77,8 +85,8 @@ MUTATIONS = [
      "\n        const double Dk = Ds[(d * K + k) % (K * D)];"),
     ("dt_bias shared by routes", "\n        const double bias = dt_bias[k * D + d];",
      "\n        const double bias = dt_bias[d];"),
-    ("x ignores batch", "const float *xc = u_routes ? NULL : x + (b * D + d) * L;",
-     "const float *xc = u_routes ? NULL : x + d * L;"),
+    ("x ignores batch", "const float *xc = u_routes ? NULL : x + (b * D + d) * L;\n    const",
+     "const float *xc = u_routes ? NULL : x + d * L;\n    const"),
     ("Cs ignores batch", "\n        const float *Ck = Cs + (b * K + k) * N * L;",
      "\n        const float *Ck = Cs + k * N * L;"),
     ("state not reset per route", "            h[n] = 0.0;\n", "\n"),
@@ -127,8 +135,8 @@ MUTATIONS = [
      "\n            const double Dk = Ds[(d * K + k) % (K * D)];"),
     ("bwd: dt_bias shared by routes", "\n            const double bias = dt_bias[k * D + d];",
      "\n            const double bias = dt_bias[d];"),
-    ("bwd: x ignores batch", "const float *xc = x + (b * D + d) * L;\n        const float *gc",
-     "const float *xc = x + d * L;\n        const float *gc"),
+    ("bwd: x ignores batch", "u_routes ? NULL : x + (b * D + d) * L;\n        const float *gc",
+     "u_routes ? NULL : x + d * L;\n        const float *gc"),
     ("bwd: Cs ignores batch", "\n            const float *Ck = Cs + (b * K + k) * N * L;",
      "\n            const float *Ck = Cs + k * N * L;"),
     ("bwd: dy ignores batch", "const float *gc = dy + (b * D + d) * L;",
@@ -153,7 +161,8 @@ MUTATIONS = [
     ("project: B and C swapped", "Bs[(i * N + n) * L + t] = xd[R + n];",
      "Bs[(i * N + n) * L + t] = xd[R + N + n];"),
     ("routes: every route reads route 0's input",
-     "u_routes + ((b * K + k) * D + d) * L : NULL;", "u_routes + ((b * K) * D + d) * L : NULL;"),
+     "u_routes + ((b * K + k) * D + d) * L : NULL;\n        for (int64_t t",
+     "u_routes + ((b * K) * D + d) * L : NULL;\n        for (int64_t t"),
     ("routes: input read in reverse", "const double u = uk ? uk[t] : xc[l];",
      "const double u = uk ? uk[L - 1 - t] : xc[l];"),
     ("low rank: dt_w's first column for every r", "dtv += (double)wr[r] * (double)lr[r * L + t];",
