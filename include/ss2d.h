@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 6
+#define SS2D_ABI_VERSION 7
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -200,6 +200,28 @@ int ss1d_bidir_backward_ex(const void *x, const void *dt_raw, const float *A_log
                            void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
                            float *ddt_bias, void *dz, int64_t B, int64_t D, int64_t L,
                            int64_t N, int dtype, int flags, void *stream);
+
+/* ---- backward of the operator over per-route inputs ---------------------------------------
+ * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output
+ * of ss2d_forward_routes (ss1d_bidir_forward_routes) on the same inputs, gate z and flags:
+ * the gradients of ss2d_backward_ex, but with each route's own input u (B, K, D, L, in scan
+ * order, the data type) in place of x, and du of that shape (the gradient of route k's
+ * input at step t; the routes share no input, so nothing is summed across them) in place of
+ * dx.  This is the gradient that the per-route front end (ss2d_project) continues with.
+ * Every other argument, error and convention is that of ss2d_backward_ex. */
+int ss2d_backward_routes(const void *u, const void *dt_raw, const float *A_log, const void *Bs,
+                         const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                         const void *dy, void *du, void *ddt_raw, float *dA_log, void *dBs,
+                         void *dCs, float *dDs, float *ddt_bias, void *dz, int64_t B,
+                         int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
+                         void *stream);
+
+int ss1d_bidir_backward_routes(const void *u, const void *dt_raw, const float *A_log,
+                               const void *Bs, const void *Cs, const float *Ds,
+                               const float *dt_bias, const void *z, const void *dy, void *du,
+                               void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
+                               float *ddt_bias, void *dz, int64_t B, int64_t D, int64_t L,
+                               int64_t N, int dtype, int flags, void *stream);
 
 /* ---- per-route front end and the operator over per-route inputs ---------------------------
  * In the pages' per-direction modules every scan direction carries its own input layers: the

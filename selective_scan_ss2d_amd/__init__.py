@@ -11,6 +11,7 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
                        SS2D_FLAG_ZOH, SS2D_OK, SIGNATURES, KERNEL_KINDS, SS2DError,
                        GRAD_NAMES, abi_version, load_library, ss1d_bidir_backward,
                        ss1d_bidir_backward_ex, ss2d_backward_ex,
+                       ss1d_bidir_backward_routes, ss2d_backward_routes,
                        ss1d_bidir_forward, ss1d_bidir_forward_ex, ss1d_bidir_forward_routes,
                        ss1d_bidir_forward_routes_lr, ss1d_bidir_project,
                        ss1d_bidir_project_lr, ss2d_backward, ss2d_forward, ss2d_forward_ex,
@@ -20,6 +21,7 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
 __all__ = [
     "ss2d_forward", "ss1d_bidir_forward", "ss2d_forward_ex", "ss1d_bidir_forward_ex",
     "ss2d_backward", "ss1d_bidir_backward", "ss2d_backward_ex", "ss1d_bidir_backward_ex",
+    "ss2d_backward_routes", "ss1d_bidir_backward_routes",
     "GRAD_NAMES", "ss2d_project", "ss1d_bidir_project",
     "ss2d_forward_routes", "ss1d_bidir_forward_routes", "ss2d_project_lr",
     "ss1d_bidir_project_lr", "ss2d_forward_routes_lr", "ss1d_bidir_forward_routes_lr",

@@ -37,6 +37,9 @@ SIGNATURES = {
     "ss1d_bidir_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 4 + [ctypes.c_int, _P]),
     "ss2d_backward_ex": (ctypes.c_int, [_P] * 17 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_backward_ex": (ctypes.c_int, [_P] * 17 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_backward_routes": (ctypes.c_int, [_P] * 17 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_backward_routes": (ctypes.c_int,
+                                   [_P] * 17 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_project": (ctypes.c_int, [_P] * 9 + [_I64] * 7 + [ctypes.c_int, _P]),
     "ss1d_bidir_project": (ctypes.c_int, [_P] * 9 + [_I64] * 6 + [ctypes.c_int, _P]),
     "ss2d_forward_routes": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
@@ -489,6 +492,58 @@ def ss1d_bidir_backward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None, zo
     B, D, L = x.shape
     return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L, z=z,
                      zoh=zoh, ex=True)
+
+
+def _backward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, z, zoh, stream):
+    torch = _torch()
+    lib = load_library()
+    if u.device.type != "cuda":
+        raise ValueError("u must be a GPU tensor")
+    if u.dim() != 4 or u.shape[1] != K:
+        raise ValueError(f"u must be (B, {K}, D, L)")
+    B, _, D, L = u.shape
+    N = A_log.shape[-1] if A_log.dim() == 3 else -1
+    dt, dev = u.dtype, u.device
+    _dtype_code(u)
+    _expect("u", u, (B, K, D, L), dt, dev)
+    _expect("dt_raw", dt_raw, (B, K, D, L), dt, dev)
+    _expect("A_log", A_log, (K, D, N), torch.float32, dev)
+    _expect("Bs", Bs, (B, K, N, L), dt, dev)
+    _expect("Cs", Cs, (B, K, N, L), dt, dev)
+    _expect("Ds", Ds, (K, D), torch.float32, dev)
+    _expect("dt_bias", dt_bias, (K, D), torch.float32, dev)
+    _expect("dy", dy, xshape, dt, dev)
+    ins = (u, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+    names = ("u",) + GRAD_NAMES[1:]
+    grads = {name: torch.empty_like(t) for name, t in zip(names, ins)}
+    if z is not None:
+        _expect("z", z, xshape, u.dtype, u.device)
+        grads["z"] = torch.empty_like(z)
+    args = [t.data_ptr() for t in ins] + [None if z is None else z.data_ptr(), dy.data_ptr()] + \
+        [grads[n].data_ptr() for n in names] + [None if z is None else grads["z"].data_ptr()]
+    fn = lib.ss2d_backward_routes if K == 4 else lib.ss1d_bidir_backward_routes
+    dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
+    _check(fn(*args, *dims, N, _dtype_code(u), SS2D_FLAG_ZOH if zoh else 0,
+              _stream_handle(u.device, stream)))
+    return grads
+
+
+def ss2d_backward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, H, W, z=None, zoh=False,
+                         stream=None):
+    """Gradients of sum(dy * y) for y = ss2d_forward_routes(u, ..., H, W, z=z, zoh=zoh): a
+    dict with the gradient of every input under its name, u's per route and step (B, 4, D,
+    L), and z's when the gate is given."""
+    B, D = u.shape[0], u.shape[2]
+    return _backward_routes(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, H, W), z, zoh,
+                            stream)
+
+
+def ss1d_bidir_backward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None, zoh=False,
+                               stream=None):
+    """ss2d_backward_routes for y = ss1d_bidir_forward_routes(u, ...), u (B, 2, D, L)."""
+    B, D, L = u.shape[0], u.shape[2], u.shape[3]
+    return _backward_routes(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, L), z, zoh,
+                            stream)
 
 
 def timing_enable(enable: bool = True) -> bool:

@@ -342,11 +342,13 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
 // ---- backward ----------------------------------------------------------------------------
 // z (not NULL): gradients of the gated output y SiLU(z); dz receives z's gradient.
 // flags: SS2D_FLAG_ZOH for the zero-order-hold operator.
+// routes: x is every route's own input u (B, K, D, L) in scan order, and dx receives du of
+// that shape (per route and step) instead of the image gradient.
 int backward(int K, const void* x, const void* dt_raw, const float* A_log, const void* Bs,
              const void* Cs, const float* Ds, const float* dt_bias, const void* dy, void* dx,
              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
              int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream,
-             const void* z = nullptr, void* dz = nullptr, int flags = 0) {
+             const void* z = nullptr, void* dz = nullptr, int flags = 0, bool routes = false) {
   const bool gated = z != nullptr;
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
@@ -379,9 +381,10 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
                           static_cast<const void*>(dt_bias), static_cast<const void*>(dA_log),
                           static_cast<const void*>(dDs), static_cast<const void*>(ddt_bias)})
     if (reinterpret_cast<uintptr_t>(ptr) & 3u) return SS2D_ERR_ALIGN;
-  const int64_t in_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
+  const int64_t n_in0 = routes ? n_dt : n_x;  // elements of x (u) and of dx (du)
+  const int64_t in_bytes[] = {n_in0 * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
                               int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e, n_x * e};
-  const int64_t out_bytes[] = {n_x * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
+  const int64_t out_bytes[] = {n_in0 * e, n_dt * e, int64_t(K) * D * N * 4, n_bc * e, n_bc * e,
                                int64_t(K) * D * 4, int64_t(K) * D * 4, n_x * e};
   for (int i = 0; i < n_out; ++i) {
     for (int j = 0; j < n_in; ++j)
@@ -404,10 +407,11 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   const int64_t tiles = (L + 31) / 32;
   const int64_t n_cb = (D + 63) / 64;
   const bool need_t = (K == 4) && H > 1 && W > 1;
+  const bool need_xt = need_t && !routes;  // per-route inputs are read in scan order
   const int64_t ge = gated ? 4 : e;  // bytes per element of g
   size_t off = 0;
   const size_t off_xt = off;
-  if (need_t) off = align256(off + size_t(n_x * e));
+  if (need_xt) off = align256(off + size_t(n_x * e));
   const size_t off_gt = off;
   if (need_t) off = align256(off + size_t(n_x * ge));
   const size_t off_g = off;
@@ -431,9 +435,9 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   int err = 0;
   // g: the gradient every route's output receives (dy, or dy SiLU(z) with the gate)
   const void* g_img = gated ? static_cast<const void*>(ws + off_g) : dy;
-  const void* xt = need_t ? static_cast<const void*>(ws + off_xt) : x;
+  const void* xt = need_xt ? static_cast<const void*>(ws + off_xt) : x;
   const void* gt = need_t ? static_cast<const void*>(ws + off_gt) : g_img;
-  if (need_t)
+  if (need_xt)
     err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
       return ss2d::launch_transpose(x, ws + off_xt, int(B), int(D), int(H), int(W), dtype, st);
     });
@@ -461,6 +465,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     a.chunks_in_launch = 1;
     a.ck_tiles = int(tiles);
     a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
+    a.x_routes = routes ? 1 : 0;
     if (gated) a.y_route = reinterpret_cast<float*>(ws + off_du);
     Plan p;
     p.split = 4;
@@ -483,8 +488,11 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   for (int64_t b0 = 0; !err && rc == SS2D_OK && b0 < B; b0 += kMaxGridZ) {
     const int64_t nb = (B - b0 < kMaxGridZ) ? (B - b0) : kMaxGridZ;
     ss2d::BwdArgs g{};
-    g.x_row = static_cast<const char*>(x) + b0 * D * L * e;
-    g.x_col = static_cast<const char*>(xt) + b0 * D * L * e;
+    const int64_t x_per_b = (routes ? K : 1) * D * L * e;
+    g.x_row = static_cast<const char*>(x) + b0 * x_per_b;
+    g.x_col = static_cast<const char*>(xt) + b0 * x_per_b;
+    g.x_routes = routes ? 1 : 0;
+    g.du_out = routes ? static_cast<char*>(dx) + b0 * x_per_b : nullptr;
     g.g_row = static_cast<const char*>(g_img) + b0 * D * L * ge;
     g.g_col = static_cast<const char*>(gt) + b0 * D * L * ge;
     g.g_f32 = gated ? 1 : 0;
@@ -526,7 +534,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
           reinterpret_cast<const float*>(ws + off_pb), dA_log, dDs, ddt_bias, int(B), K, int(D),
           int(N), st);
     });
-  if (!err && rc == SS2D_OK)
+  if (!err && rc == SS2D_OK && !routes)
     err = timed(SS2D_KERNEL_MERGE, st, [&] {
       const float* du = reinterpret_cast<const float*>(ws + off_du);
       return (K == 4) ? ss2d::launch_merge4(du, nullptr, dx, int(B), int(D), int(H), int(W),
@@ -712,6 +720,26 @@ int ss1d_bidir_backward_ex(const void* x, const void* dt_raw, const float* A_log
                            int64_t N, int dtype, int flags, void* stream) {
   return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags);
+}
+
+int ss2d_backward_routes(const void* u, const void* dt_raw, const float* A_log, const void* Bs,
+                         const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                         const void* dy, void* du, void* ddt_raw, float* dA_log, void* dBs,
+                         void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B,
+                         int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
+                         void* stream) {
+  return backward(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, du, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, flags, true);
+}
+
+int ss1d_bidir_backward_routes(const void* u, const void* dt_raw, const float* A_log,
+                               const void* Bs, const void* Cs, const float* Ds,
+                               const float* dt_bias, const void* z, const void* dy, void* du,
+                               void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs,
+                               float* ddt_bias, void* dz, int64_t B, int64_t D, int64_t L,
+                               int64_t N, int dtype, int flags, void* stream) {
+  return backward(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, du, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags, true);
 }
 
 int ss2d_project(const void* x, const float* conv_w, const float* conv_b,

@@ -202,6 +202,10 @@ struct BwdArgs {
   int n_cb;               // channel blocks per (b, k): ceil(D / 64)
   int g_f32;              // nonzero: g is fp32 whatever the data type
   int zoh;                // nonzero: the zero-order-hold operator
+  int x_routes;           // nonzero: x_row holds each route's own input (B, K, D, L) in scan
+                          // order, and du goes to du_out (same shape, element type) instead
+                          // of du_route
+  void* du_out;
 };
 
 // Arguments of the per-route front end (causal depthwise conv + SiLU, x_proj, dt_proj).

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 6
+    assert lib.ss2d_abi_version() == 7
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -251,6 +251,42 @@ def test_backward_ex_argument_errors(lib):
     import torch
     if not torch.cuda.is_available():
         assert call_bwd_ex(lib, ptrs) == bnd.SS2D_ERR_HIP
+
+
+def test_backward_routes_argument_errors(lib):
+    # u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, dy | du, ddt_raw, dA_log, dBs, dCs, dDs,
+    # ddt_bias, dz; u and du are (B, K, D, L)
+    ptrs = fake_ptrs(17)
+    for K in (4, 2):
+        def call(p, **kw):
+            B, D, H, W, N = kw.get("B", 1), 8, 8, 8, kw.get("N", 4)
+            if K == 4:
+                return lib.ss2d_backward_routes(*p, B, D, H, W, N, kw.get("dtype", 0),
+                                                kw.get("flags", 0), None)
+            return lib.ss1d_bidir_backward_routes(*p, B, D, H * W, N, kw.get("dtype", 0),
+                                                  kw.get("flags", 0), None)
+        for i in range(17):
+            if i == 7:  # z = NULL: no gate
+                continue
+            p = list(ptrs)
+            p[i] = None
+            assert call(p) == bnd.SS2D_ERR_NULL, (K, i)
+        assert call(ptrs, N=32) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call(ptrs, flags=2) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call(ptrs, B=-1) == bnd.SS2D_ERR_SHAPE
+        assert call([None] * 17, B=0) == bnd.SS2D_OK
+        for i in range(17):
+            p = list(ptrs)
+            p[i] += 1
+            assert call(p) == bnd.SS2D_ERR_ALIGN, (K, i)
+        # fp32: du (K * D * L elements) starting at u's last element, and u starting at
+        # du's last route
+        p = list(ptrs)
+        p[9] = p[0] + 4 * (K * 8 * 64 - 1)
+        assert call(p) == bnd.SS2D_ERR_ALIAS
+        p = list(ptrs)
+        p[0] = p[9] + 4 * (K - 1) * 8 * 64
+        assert call(p) == bnd.SS2D_ERR_ALIAS
 
 
 # ---- per-route front end and the operator over per-route inputs ---------------------------
