@@ -116,7 +116,7 @@ def measured_traffic(workload: str, front: bool = False, R: int = 1, KW: int = 4
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None, zoh=False) -> dict:
+def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None, zoh=False, u=None) -> dict:
     """The float64 oracle's backward (gated with z), as it is, on all host cores, over a
     bounded sample of whole images (its unit of work: dBs and dCs sum over every channel of
     an image)."""
@@ -126,9 +126,13 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None, zoh=False) -> di
 
     def run(n):
         sl = [inp[k][:n] if k in ("x", "dt_raw", "Bs", "Cs") else inp[k] for k in ARGS]
+        zs = None if z is None else z[:n]
         t0 = time.perf_counter()
-        orc.backward(wl.K, *sl, dy[:n], threads=cores, z=None if z is None else z[:n],
-                     zoh=zoh)
+        if u is None:
+            orc.backward(wl.K, *sl, dy[:n], threads=cores, z=zs, zoh=zoh)
+        else:  # the operator over per-route inputs u (B, K, D, L)
+            orc.backward_routes(wl.K, u[:n], *sl[1:], dy[:n], wl.H, wl.W, threads=cores, z=zs,
+                                zoh=zoh)
         return time.perf_counter() - t0
 
     n = min(wl.B, max(1, cores))
@@ -140,7 +144,8 @@ def cpu_baseline_backward(wl, inp, dy, target_s: float, z=None, zoh=False) -> di
     return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
             "kind": "oracle",
             "sample": f"{'gated ' if z is not None else ''}{'zero-order-hold ' if zoh else ''}"
-                      f"backward of {n} of {wl.B} images "
+                      f"{'per-route-input ' if u is not None else ''}backward of {n} of {wl.B} "
+                      f"images "
                       f"of {wl.name} (all {wl.K} routes and {wl.D} channels), {upd:.3e} state "
                       f"updates in {dt:.2f} s"}
 
@@ -236,7 +241,8 @@ def main() -> int:
                          "--gate and/or --zoh, of that operator's output, z included)")
     ap.add_argument("--front", action="store_true",
                     help="per-route front end: time ss2d_project (causal conv + SiLU, x_proj, "
-                         "dt_proj) followed by ss2d_forward_routes on its outputs")
+                         "dt_proj) followed by ss2d_forward_routes on its outputs; with "
+                         "--backward, time ss2d_backward_routes on those outputs")
     ap.add_argument("--front-r", type=int, default=1, metavar="R",
                     help="dt rank R of the front end (x_proj rows R + 2N)")
     ap.add_argument("--front-kw", type=int, default=4, metavar="KW",
@@ -291,9 +297,13 @@ def main() -> int:
         dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
     y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    if args.backward and args.front:
-        log("the backward entry points cover the operator, not the front end")
+    if args.backward and args.front_lowrank:
+        log("no backward for the operator with dt_proj folded in")
         return 2
+    # --backward --front: the backward of the operator over the front end's per-route
+    # outputs (computed once, outside the timed region; the front end's own layers have no
+    # backward here)
+    routes_bwd = args.backward and args.front
     z = None
     if gate is not None:
         z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
@@ -315,6 +325,17 @@ def main() -> int:
                 o = proj(dev["x"], *fw[:3], args.front_r)
                 return fwd(o["u"], o["dt_lr"], fw[3], dev["A_log"], o["Bs"], o["Cs"],
                            dev["Ds"], dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
+        elif routes_bwd:
+            proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
+            bwd = ss.ss2d_backward_routes if wl.K == 4 else ss.ss1d_bidir_backward_routes
+            po = proj(dev["x"], *fw)
+            g = workloads.make_output_grad(wl, 0)
+            dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
+                  if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
+
+            def call():
+                return bwd(po["u"], po["dt_raw"], dev["A_log"], po["Bs"], po["Cs"], dev["Ds"],
+                           dev["dt_bias"], dy, *hw, z=z, zoh=args.zoh)
         else:
             proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
             fwd = ss.ss2d_forward_routes if wl.K == 4 else ss.ss1d_bidir_forward_routes
@@ -370,7 +391,7 @@ def main() -> int:
     proj_bytes = (e * (wl.B * wl.D * wl.L + BKL * wl.D + 2 * BKL * wl.N)
                   + 4 * wl.K * wl.D * (args.front_kw + 1 + M))
     proj_bytes += e * BKL * R if args.front_lowrank else e * BKL * wl.D + 4 * wl.K * wl.D * R
-    if args.front:  # the scan then reads u (B, K, D, L) in place of x (B, D, L)
+    if args.front and not routes_bwd:  # the scan then reads u (B, K, D, L), not x (B, D, L)
         alg_bytes += proj_bytes + e * (wl.K - 1) * wl.B * wl.D * wl.L
     if args.front_lowrank:  # ... and dt_lr (B, K, R, L) and dt_w (K, D, R) for dt_raw
         alg_bytes += e * BKL * R + 4 * wl.K * wl.D * R - e * BKL * wl.D
@@ -406,7 +427,7 @@ def main() -> int:
                 "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
 
     roofline_front = None
-    if args.front:
+    if args.front and not routes_bwd:
         p_ms, p_n = kernels["project"]
         p_avg_s = p_ms / max(p_n, 1) / 1e3
         p_gbps = proj_bytes / p_avg_s / 1e9
@@ -424,7 +445,11 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        if args.front:
+        if routes_bwd:  # seeded per-route inputs of the same shape (not the GPU's outputs)
+            cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds,
+                                        z=gate["z"] if gate else None, zoh=args.zoh,
+                                        u=workloads.make_route_inputs(wl, 0)["u"])
+        elif args.front:
             cpu = cpu_baseline_front(wl, inp, front_w, args.cpu_seconds,
                                      z=gate["z"] if gate else None, zoh=args.zoh,
                                      lowrank=args.front_lowrank)
@@ -453,7 +478,8 @@ def main() -> int:
                    "L": wl.L, "N": wl.N, "K": wl.K, "io_dtype": wl.dtype,
                    "state_dtype": "f32", "A_log": args.a_log, "gate": bool(args.gate),
                    "zoh": bool(args.zoh),
-                   "pass": ("backward" if args.backward else
+                   "pass": ("backward (per-route inputs from the front end)" if routes_bwd
+                            else "backward" if args.backward else
                             "front(dt_proj in scan)+forward" if args.front_lowrank else
                             "front+forward" if args.front else "forward")},
         "hbm_gbps_algorithmic": round(gbps, 1),
