@@ -2,12 +2,15 @@
 """Benchmark of the SS2D forward operator on one MI355X.
 
 A step is one full forward call (transpose, scan, merge: every kernel of the operator) on
-one batch of seeded synthetic input already resident in HBM.  W untimed warm-up steps, then
-K timed steps between device synchronisations, timed with HIP events on the stream the
-library launches on.  Prints ONE JSON line on stdout (details go to stderr):
+one batch of seeded synthetic input already resident in HBM.  W untimed warm-up steps (then,
+if the GPU has been under load for less than --settle-ms, more untimed steps until it has:
+the clock ramps up over the first ~20 ms of load), then K timed steps between device
+synchronisations, timed with HIP events on the stream the library launches on.  Prints ONE
+JSON line on stdout (details go to stderr):
 
   value        state updates per second (B*K*D*L*N per step / seconds per step)
-  roofline     the dominant kernel (the scan) against the fp32 VALU peak
+  roofline     the dominant kernel (the scan) against MI355X's 8 TB/s HBM peak, with the
+               fp32 and issue-slot fractions as diagnostics beside it
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
@@ -27,40 +30,27 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = ("SS2D fwd state-updates/s (B·K·D·L·N) + achieved HBM GB/s, "
           "VMamba-T stage1")
-# ALU roofline of the state update on MI355X.  The VALU issues one wave64 instruction per
-# 4 cycles on each of 256 CUs x 4 SIMDs at 2.4 GHz: 256 * 4 * 16 * 2.4e9 = 3.93e13 lane-ops/s
-# (78.6 TFLOP/s counting an FMA as 2 flops; the published 157.3 assumes packed fp32, which
-# this build does not emit).  One state update must issue 2 multiplies and 2 FMAs (6 flops)
-# plus one v_exp_f32, which occupies the VALU for two issue slots (8 cycles): 6 slots per 6
-# flops, so the update's arithmetic peaks at 3.93e13 * 6 / 6 = 39.3 TFLOP/s.
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
-FMA_PEAK_TFLOPS = VALU_LANE_OPS * 2 / 1e12
-FLOPS_PER_UPDATE = 6
+# Diagnostics beside the HBM roofline.  fp32: MI355X's published vector fp32 peak,
+# 157.3 TFLOP/s, against the algorithmic 4 flops of one state update (delta*A, the decay
+# times h, (delta*u)*B, C*h) plus its exponential.  Issue slots: the VALU issues one wave64
+# instruction per 4 cycles on each of 256 CUs x 4 SIMDs at 2.4 GHz, 3.93e13 lane-slots/s
+# without packed fp32 (which this build does not emit); one update needs at least 2
+# multiplies, 2 FMAs and one v_exp_f32, which takes two issue slots: 6 slots.  The
+# issue-floor fraction is that floor's time over the measured time.
+FP32_PEAK_TFLOPS = 157.3
+ALG_FLOPS_PER_UPDATE = 4
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
 ISSUE_SLOTS_PER_UPDATE = 4 + 2
-UPDATE_PEAK_TFLOPS = VALU_LANE_OPS / ISSUE_SLOTS_PER_UPDATE * FLOPS_PER_UPDATE / 1e12
-# With zero-order hold the update is delta*A (1 flop), (a - 1) / A as one FMA (2), times B
-# and u (2), the h update (2) and C*h (2): 9 flops in at least 6 VALU slots plus the exp.
-ZOH_FLOPS_PER_UPDATE = 9
+# With zero-order hold: at least 6 VALU slots (delta*A, (a - 1) / A as one FMA, times B and
+# u, the h update, C*h) plus the exponential.
 ZOH_ISSUE_SLOTS_PER_UPDATE = 6 + 2
-ZOH_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / ZOH_ISSUE_SLOTS_PER_UPDATE * ZOH_FLOPS_PER_UPDATE
-                          / 1e12)
-# Backward, per state update: the forward recompute (delta*A, (delta*u)*B, the h update: 4
-# flops, one exp) and the adjoint (g*C and the lambda update: 3; dC, dB: 2; lambda*h_prev*a:
-# 2; the sums over n for ddelta and du: 4; dA: 2): 17 flops in at least 12 VALU slots plus
-# the exp.
-BWD_FLOPS_PER_UPDATE = 17
+# Backward, per state update: the forward recompute (3 VALU and the exp) and the adjoint
+# (g*C and the lambda update, dC, dB, lambda*h_prev*a, the sums over n for ddelta and du,
+# dA): at least 12 VALU slots plus the exp.
 BWD_ISSUE_SLOTS_PER_UPDATE = 12 + 2
-BWD_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / BWD_ISSUE_SLOTS_PER_UPDATE * BWD_FLOPS_PER_UPDATE
-                          / 1e12)
-# Backward with zero-order hold, per state update: the recompute (delta*A, (a - 1) / A as one
-# FMA, times u and B, the h update: 7 flops, one exp) and the adjoint (g*C and the lambda
-# update: 3; dC: 1; dB = lambda*(bb*u): 2; lambda*h_prev*a: 2; the sums over n for ddelta
-# (lambda h_prev a A and lambda a B) and du (lambda bb B): 8; dA with d bb / dA from a and
-# bb: 8): 31 flops in at least 22 VALU slots plus the exp.
-ZOH_BWD_FLOPS_PER_UPDATE = 31
+# Backward with zero-order hold: the recompute's 6 and the adjoint's 16: 22 VALU slots
+# plus the exp.
 ZOH_BWD_ISSUE_SLOTS_PER_UPDATE = 22 + 2
-ZOH_BWD_UPDATE_PEAK_TFLOPS = (VALU_LANE_OPS / ZOH_BWD_ISSUE_SLOTS_PER_UPDATE
-                              * ZOH_BWD_FLOPS_PER_UPDATE / 1e12)
 HBM_PEAK_GBPS = 8000.0
 ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
 
@@ -192,8 +182,21 @@ def cpu_baseline_front(wl, inp, w, target_s: float, z=None, zoh=False,
                       f"routes and {wl.D} channels), {upd:.3e} state updates in {dt:.2f} s"}
 
 
+def cpu_model() -> str:
+    try:
+        for line in pathlib.Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, target_s: float, z=None, zoh=False) -> dict:
-    """The float64 oracle, as it is, on all host cores, over a bounded sample of channels."""
+    """The float64 oracle, as it is, on all host cores, over a bounded sample of channels,
+    and on one core over a smaller sample (extrapolated to the whole workload).  Returns
+    the record and the sample (its (b, d) channels and the oracle's outputs there), which
+    the caller compares with the GPU's output."""
     import numpy as np
 
     import oracle
@@ -203,23 +206,80 @@ def cpu_baseline(wl, inp, target_s: float, z=None, zoh=False) -> dict:
     opts = dict(z=z, zoh=zoh)
     total = wl.B * wl.D
     rng = np.random.default_rng(0)
-    n = min(total, max(cores, 64))
     order = rng.permutation(total)
-    t0 = time.perf_counter()
-    sel = order[:n]
-    orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores, **opts)
-    dt = time.perf_counter() - t0
-    if n < total and dt < target_s:
-        n = int(min(total, max(n, n * target_s / max(dt, 1e-3))))
+
+    def run(n, threads):
         sel = order[:n]
         t0 = time.perf_counter()
-        orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=cores, **opts)
-        dt = time.perf_counter() - t0
+        ref = orc.forward_channels(wl.K, *args, sel // wl.D, sel % wl.D, threads=threads,
+                                   **opts)
+        return time.perf_counter() - t0, sel, ref
+
+    n = min(total, max(cores, 64))
+    dt, sel, ref = run(n, cores)
+    if n < total and dt < target_s:
+        n = int(min(total, max(n, n * target_s / max(dt, 1e-3))))
+        dt, sel, ref = run(n, cores)
+    threads = orc.last_threads
     upd = n * wl.K * wl.L * wl.N
-    return {"value": upd / dt, "unit": "state-updates/s", "cores": orc.last_threads,
-            "kind": "oracle",
-            "sample": f"{n} of {total} (b,d) channels of {wl.name} (all {wl.K} routes, full "
-                      f"L={wl.L}, N={wl.N}), {upd:.3e} state updates in {dt:.2f} s"}
+    # one core: a sample of about a tenth of the wall-time budget
+    n1 = max(1, min(total, int(n * min(1.0, 0.1 * target_s / max(dt * threads, 1e-3)))))
+    dt1, _, _ = run(n1, 1)
+    upd1 = n1 * wl.K * wl.L * wl.N
+    rec = {"value": upd / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n} of {total} (b,d) channels of {wl.name} (all {wl.K} routes, full "
+                     f"L={wl.L}, N={wl.N}), {upd:.3e} state updates in {dt:.2f} s",
+           "one_core_value": upd1 / dt1,
+           "one_core_sample": f"{n1} channels in {dt1:.2f} s on 1 thread",
+           "one_core_whole_workload_s_extrapolated": wl.updates / (upd1 / dt1)}
+    return rec, (sel // wl.D, sel % wl.D, ref)
+
+
+def sample_error(y, sample, dtype: str) -> dict:
+    """Parity of the GPU's output y (B, D, ...) on the oracle's sampled channels: the gate
+    metric max |y - y*| / max(|y*|, 0.01 RMS(y*)), the same unfloored, and the limit."""
+    import numpy as np
+    import torch
+    b_idx, d_idx, ref = sample
+    got = y.detach().to(torch.float32).cpu().numpy().astype(np.float64)[b_idx, d_idx]
+    ref = ref.reshape(got.shape)
+    floor = 0.01 * float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    return {"max_rel_err": float(np.max(err / np.maximum(np.abs(ref), max(floor, 1e-30)))),
+            "max_rel_err_unfloored": float(np.max(err / np.maximum(np.abs(ref), 1e-30))),
+            "tolerance": 1e-4 if dtype == "f32" else 2e-2,
+            "metric": "max |y - y*| / max(|y*|, 0.01 RMS(y*)) over the CPU sample's channels"}
+
+
+def copy_bandwidth_gbps(torch, mib: int = 1024) -> float:
+    """Best of 5 device-to-device copies of `mib` MiB (read + write bytes over the time),
+    timed with HIP events: the HBM rate a plain copy reaches on this GPU."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    return 2 * n * 4 / best / 1e9
+
+
+def backward_bytes(wl, gate: bool, routes: bool) -> int:
+    """Algorithmic bytes of one backward call: every input (x, or each route's u
+    (B, K, D, L) with routes, dt_raw, Bs, Cs, dy, z with the gate, the fp32 parameters) read
+    once and every gradient (of the same shapes; dz with the gate) written once."""
+    e, B, K, D, L, N = wl.elem_bytes, wl.B, wl.K, wl.D, wl.L, wl.N
+    xs = B * D * L * (K if routes else 1)
+    data = xs + B * K * D * L + 2 * B * K * N * L  # x (u), dt_raw, Bs, Cs
+    params = K * D * N + 2 * K * D
+    img = B * D * L * (2 if gate else 1)  # dy (and z)
+    return e * (2 * data + img + (B * D * L if gate else 0)) + 4 * 2 * params
 
 
 def main() -> int:
@@ -227,11 +287,17 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="keep warming up (untimed) until the GPU has run the step for this "
+                         "long: the clock reaches its sustained rate after ~20 ms of load")
     ap.add_argument("--workload", default="vmamba_t_stage1_bf16")
     ap.add_argument("--a-log", default="init", choices=["init", "random"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets used in turn (0: 3 when the working set is under 512 MB, "
+                         "twice the 256 MB Infinity Cache, else 1)")
     ap.add_argument("--gate", action="store_true",
                     help="gated entry point: y * SiLU(z), z of the shape of x")
     ap.add_argument("--zoh", action="store_true",
@@ -291,38 +357,65 @@ def main() -> int:
     wl = workloads.workload(args.workload)
     log(f"workload {wl.name}: {wl.as_dict()}; generating seeded inputs")
     inp = workloads.make_inputs(wl, seed=0, a_log=args.a_log)
-    dev = {}
-    for k in ("x", "dt_raw", "Bs", "Cs"):
-        if wl.dtype == "bf16":
-            dev[k] = torch.from_numpy(inp[k + "_bf16"].view(np.int16)).view(torch.bfloat16)
-        else:
-            dev[k] = torch.from_numpy(inp[k])
-        dev[k] = dev[k].to("cuda:0")
-    for k in ("A_log", "Ds", "dt_bias"):
-        dev[k] = torch.from_numpy(inp[k]).to("cuda:0")
-    y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
-    gate = workloads.make_gate(wl, 0) if args.gate else None
     if args.backward and args.front_lowrank:
         log("no backward for the operator with dt_proj folded in")
         return 2
-    # --backward --front: the backward of the operator over the front end's per-route
-    # outputs (computed once, outside the timed region; the front end's own layers have no
-    # backward here)
-    routes_bwd = args.backward and args.front
-    z = None
-    if gate is not None:
-        z = (torch.from_numpy(gate["z_bf16"].view(np.int16)).view(torch.bfloat16)
-             if wl.dtype == "bf16" else torch.from_numpy(gate["z"])).to("cuda:0")
-    front_w = None
     if args.front_lowrank and not args.front:
         log("--front-lowrank needs --front")
         return 2
-    if args.front:
-        front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw)
-        fw = [torch.from_numpy(front_w[k]).to("cuda:0")
-              for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")]
-        hw = (wl.H, wl.W) if wl.K == 4 else ()
-        if args.front_lowrank:
+    # --backward --front: the backward of the operator over the front end's per-route
+    # outputs (computed once per input set, outside the timed region; the front end's own
+    # layers have no backward here)
+    routes_bwd = args.backward and args.front
+    e, M, R = wl.elem_bytes, args.front_r + 2 * wl.N, args.front_r
+    # front end, per launch: x read once; u and dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L)
+    # written once; the fp32 weights read once.  With dt_proj folded into the scan, the
+    # front end writes the R dt rows (B, K, R, L) in place of dt_raw and reads no dt_proj_w.
+    BKL = wl.B * wl.K * wl.L
+    proj_bytes = (e * (wl.B * wl.D * wl.L + BKL * wl.D + 2 * BKL * wl.N)
+                  + 4 * wl.K * wl.D * (args.front_kw + 1 + M))
+    proj_bytes += e * BKL * R if args.front_lowrank else e * BKL * wl.D + 4 * wl.K * wl.D * R
+    if args.backward:
+        alg_bytes = backward_bytes(wl, args.gate, routes_bwd)
+    else:
+        alg_bytes = wl.algorithmic_bytes() + (e * wl.B * wl.D * wl.L if args.gate else 0)
+        if args.front:  # the scan then reads u (B, K, D, L), not x (B, D, L)
+            alg_bytes += proj_bytes + e * (wl.K - 1) * wl.B * wl.D * wl.L
+        if args.front_lowrank:  # ... and dt_lr (B, K, R, L) and dt_w (K, D, R) for dt_raw
+            alg_bytes += e * BKL * R + 4 * wl.K * wl.D * R - e * BKL * wl.D
+    # the kernel the roofline line describes moves the step's algorithmic bytes: its own
+    # share when the front end runs before it (its inputs u, dt_raw, Bs, Cs; y)
+    kernel_bytes = alg_bytes - proj_bytes if (args.front and not routes_bwd) else alg_bytes
+    rotate = args.rotate or (3 if alg_bytes < 512e6 else 1)
+
+    def upload(arrays):
+        d = {}
+        for k in ("x", "dt_raw", "Bs", "Cs"):
+            if wl.dtype == "bf16":
+                d[k] = torch.from_numpy(arrays[k + "_bf16"].view(np.int16)).view(torch.bfloat16)
+            else:
+                d[k] = torch.from_numpy(arrays[k])
+            d[k] = d[k].to("cuda:0")
+        for k in ("A_log", "Ds", "dt_bias"):
+            d[k] = torch.from_numpy(arrays[k]).to("cuda:0")
+        return d
+
+    def image(arr, arr_bf16):
+        return (torch.from_numpy(arr_bf16.view(np.int16)).view(torch.bfloat16)
+                if wl.dtype == "bf16" else torch.from_numpy(arr)).to("cuda:0")
+
+    gate = workloads.make_gate(wl, 0) if args.gate else None
+    z0 = image(gate["z"], gate["z_bf16"]) if gate is not None else None
+    g = workloads.make_output_grad(wl, 0) if args.backward else None
+    dy0 = image(g["dy"], g["dy_bf16"]) if g is not None else None
+    front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw) \
+        if args.front else None
+    fw = [torch.from_numpy(front_w[k]).to("cuda:0")
+          for k in ("conv_w", "conv_b", "x_proj_w", "dt_proj_w")] if args.front else None
+    hw = (wl.H, wl.W) if wl.K == 4 else ()
+
+    def make_call(dev, z, dy, y):
+        if args.front and args.front_lowrank:
             proj = ss.ss2d_project_lr if wl.K == 4 else ss.ss1d_bidir_project_lr
             fwd = ss.ss2d_forward_routes_lr if wl.K == 4 else ss.ss1d_bidir_forward_routes_lr
 
@@ -330,18 +423,14 @@ def main() -> int:
                 o = proj(dev["x"], *fw[:3], args.front_r)
                 return fwd(o["u"], o["dt_lr"], fw[3], dev["A_log"], o["Bs"], o["Cs"],
                            dev["Ds"], dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
-        elif routes_bwd:
+            return call
+        if routes_bwd:
             proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
             bwd = ss.ss2d_backward_routes if wl.K == 4 else ss.ss1d_bidir_backward_routes
             po = proj(dev["x"], *fw)
-            g = workloads.make_output_grad(wl, 0)
-            dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
-                  if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
-
-            def call():
-                return bwd(po["u"], po["dt_raw"], dev["A_log"], po["Bs"], po["Cs"], dev["Ds"],
-                           dev["dt_bias"], dy, *hw, z=z, zoh=args.zoh)
-        else:
+            return lambda: bwd(po["u"], po["dt_raw"], dev["A_log"], po["Bs"], po["Cs"],
+                               dev["Ds"], dev["dt_bias"], dy, *hw, z=z, zoh=args.zoh)
+        if args.front:
             proj = ss.ss2d_project if wl.K == 4 else ss.ss1d_bidir_project
             fwd = ss.ss2d_forward_routes if wl.K == 4 else ss.ss1d_bidir_forward_routes
 
@@ -349,27 +438,49 @@ def main() -> int:
                 o = proj(dev["x"], *fw)
                 return fwd(o["u"], o["dt_raw"], dev["A_log"], o["Bs"], o["Cs"], dev["Ds"],
                            dev["dt_bias"], *hw, z=z, zoh=args.zoh, y=y)
-    elif args.backward:
-        g = workloads.make_output_grad(wl, 0)
-        dy = (torch.from_numpy(g["dy_bf16"].view(np.int16)).view(torch.bfloat16)
-              if wl.dtype == "bf16" else torch.from_numpy(g["dy"])).to("cuda:0")
-        if z is None and not args.zoh:
-            fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
-            call = lambda: fn(*[dev[k] for k in ARGS], dy)  # noqa: E731
-        else:
+            return call
+        if args.backward:
+            if z is None and not args.zoh:
+                fn = ss.ss2d_backward if wl.K == 4 else ss.ss1d_bidir_backward
+                return lambda: fn(*[dev[k] for k in ARGS], dy)
             fn = ss.ss2d_backward_ex if wl.K == 4 else ss.ss1d_bidir_backward_ex
-            call = lambda: fn(*[dev[k] for k in ARGS], dy, z=z, zoh=args.zoh)  # noqa: E731
-    elif args.gate or args.zoh:
-        fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
-        call = lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)  # noqa: E731
-    else:
+            return lambda: fn(*[dev[k] for k in ARGS], dy, z=z, zoh=args.zoh)
+        if args.gate or args.zoh:
+            fn = ss.ss2d_forward_ex if wl.K == 4 else ss.ss1d_bidir_forward_ex
+            return lambda: fn(*[dev[k] for k in ARGS], z=z, zoh=args.zoh, y=y)
         fn = ss.ss2d_forward if wl.K == 4 else ss.ss1d_bidir_forward
-        call = lambda: fn(*[dev[k] for k in ARGS], y=y)  # noqa: E731
+        return lambda: fn(*[dev[k] for k in ARGS], y=y)
 
-    log(f"warm-up {args.warmup} steps")
+    # Input sets used in turn: each its own copy of every input and output, so that a step
+    # whose working set fits in the Infinity Cache does not find it there from the step
+    # before.
+    dev0 = upload(inp)
+    sets = []
+    for i in range(rotate):
+        dev = dev0 if i == 0 else {k: v.clone() for k, v in dev0.items()}
+        z = z0 if (i == 0 or z0 is None) else z0.clone()
+        dy = dy0 if (i == 0 or dy0 is None) else dy0.clone()
+        y = torch.empty(tuple(dev["x"].shape), dtype=dev["x"].dtype, device="cuda:0")
+        sets.append((make_call(dev, z, dy, y), y))
+    calls = [c for c, _ in sets]
+    log(f"{rotate} input set(s) in turn")
+
+    log(f"warm-up {args.warmup} steps, then until {args.settle_ms:.0f} ms of load")
+    t_start = time.perf_counter()
+    done = 0
     for _ in range(args.warmup):
-        call()
+        calls[done % rotate]()
+        done += 1
     torch.cuda.synchronize()
+    settle = 0
+    while (time.perf_counter() - t_start) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            calls[done % rotate]()
+            done += 1
+            settle += 1
+        torch.cuda.synchronize()
+    log(f"  {done} untimed steps ({settle} to settle the clock) in "
+        f"{(time.perf_counter() - t_start) * 1e3:.0f} ms")
 
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -383,32 +494,36 @@ def main() -> int:
     ev0.record(stream)
     for i in range(args.steps):
         ss.timing_enable(i % args.kernel_sample == 0)
-        call()
+        calls[(done + i) % rotate]()
     ss.timing_enable(False)
     ev1.record(stream)
     torch.cuda.synchronize()
+    done += args.steps
     kernels = ss.timing_read()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     upd_per_s = wl.updates / (ms_step / 1e3)
-    alg_bytes = wl.algorithmic_bytes() + (wl.elem_bytes * wl.B * wl.D * wl.L if args.gate else 0)
-    e, M, R = wl.elem_bytes, args.front_r + 2 * wl.N, args.front_r
-    # front end, per launch: x read once; u and dt_raw (B, K, D, L) and Bs, Cs (B, K, N, L)
-    # written once; the fp32 weights read once.  With dt_proj folded into the scan, the
-    # front end writes the R dt rows (B, K, R, L) in place of dt_raw and reads no dt_proj_w.
-    BKL = wl.B * wl.K * wl.L
-    proj_bytes = (e * (wl.B * wl.D * wl.L + BKL * wl.D + 2 * BKL * wl.N)
-                  + 4 * wl.K * wl.D * (args.front_kw + 1 + M))
-    proj_bytes += e * BKL * R if args.front_lowrank else e * BKL * wl.D + 4 * wl.K * wl.D * R
-    if args.front and not routes_bwd:  # the scan then reads u (B, K, D, L), not x (B, D, L)
-        alg_bytes += proj_bytes + e * (wl.K - 1) * wl.B * wl.D * wl.L
-    if args.front_lowrank:  # ... and dt_lr (B, K, R, L) and dt_w (K, D, R) for dt_raw
-        alg_bytes += e * BKL * R + 4 * wl.K * wl.D * R - e * BKL * wl.D
+    # The distribution of single steps, in a second timed run of K steps with an event
+    # between consecutive steps (not part of the line's value).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        calls[(done + i) % rotate]()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    ms_min = per_step[0]
     gbps = alg_bytes / (ms_step / 1e3) / 1e9
     for name, (ms, n) in kernels.items():
         if n:
             log(f"  kernel {name:10s}: {n} launches, {ms / n * 1e3:9.1f} us avg")
-    log(f"step {ms_step * 1e3:.1f} us, {upd_per_s:.4e} updates/s, algorithmic {gbps:.1f} GB/s")
+    log(f"step {ms_step * 1e3:.1f} us (median {ms_median * 1e3:.1f}, min {ms_min * 1e3:.1f}), "
+        f"{upd_per_s:.4e} updates/s, algorithmic {gbps:.1f} GB/s")
+    copy_gbps = copy_bandwidth_gbps(torch)
+    log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
 
     # Dominant kernel: the scan (with the chunked plan, both scan passes are counted).
     if args.backward:
@@ -418,23 +533,29 @@ def main() -> int:
         scan_ms, scan_n = kernels["scan"]
         agg_ms, _ = kernels["chunk_agg"]
     scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
-    flops, peak = ((ZOH_BWD_FLOPS_PER_UPDATE, ZOH_BWD_UPDATE_PEAK_TFLOPS)
-                   if args.backward and args.zoh
-                   else (BWD_FLOPS_PER_UPDATE, BWD_UPDATE_PEAK_TFLOPS) if args.backward
-                   else (ZOH_FLOPS_PER_UPDATE, ZOH_UPDATE_PEAK_TFLOPS) if args.zoh
-                   else (FLOPS_PER_UPDATE, UPDATE_PEAK_TFLOPS))
-    achieved = wl.updates * flops / scan_avg_s / 1e12
+    slots = (ZOH_BWD_ISSUE_SLOTS_PER_UPDATE if args.backward and args.zoh
+             else BWD_ISSUE_SLOTS_PER_UPDATE if args.backward
+             else ZOH_ISSUE_SLOTS_PER_UPDATE if args.zoh else ISSUE_SLOTS_PER_UPDATE)
+    achieved = kernel_bytes / scan_avg_s / 1e9
     traffic = measured_traffic(wl.name)
-    roofline = {"bound": "alu", "achieved": round(achieved, 3),
-                "peak": round(peak, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4),
-                "traffic": (traffic if not (args.gate or args.zoh or args.backward
-                                            or args.front) else None),
+    traffic = traffic if not (args.gate or args.zoh or args.backward or args.front) else None
+    fp32_tflops = wl.updates * ALG_FLOPS_PER_UPDATE / scan_avg_s / 1e12
+    issue_floor_s = wl.updates * slots / VALU_LANE_SLOTS
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic,
                 "kernel": "k_scan_bwd" if args.backward else "k_scan",
                 "kernel_avg_us": round(scan_avg_s * 1e6, 1),
                 "kernel_launches_timed": int(scan_n),
-                "frac_of_fma_peak": round(achieved / FMA_PEAK_TFLOPS, 4),
-                "hbm_gbps_algorithmic_in_kernel": round(alg_bytes / scan_avg_s / 1e9, 1)}
+                "algorithmic_bytes_per_launch": int(kernel_bytes),
+                "traffic_ratio": (round(traffic / kernel_bytes, 3) if traffic else None),
+                "copy_gbps_measured": round(copy_gbps, 1),
+                "frac_of_copy": round(achieved / copy_gbps, 4),
+                "fp32_tflops": round(fp32_tflops, 2),
+                "fp32_frac": round(fp32_tflops / FP32_PEAK_TFLOPS, 4),
+                "issue_slots_per_update": slots,
+                "issue_floor_us": round(issue_floor_s * 1e6, 1),
+                "issue_floor_frac": round(issue_floor_s / scan_avg_s, 4)}
 
     roofline_front = None
     if args.front and not routes_bwd:
@@ -453,6 +574,7 @@ def main() -> int:
                           "dt_proj_in_scan": bool(args.front_lowrank)}
 
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         if routes_bwd:  # seeded per-route inputs of the same shape (not the GPU's outputs)
@@ -467,8 +589,12 @@ def main() -> int:
             cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds,
                                         z=gate["z"] if gate else None, zoh=args.zoh)
         else:
-            cpu = cpu_baseline(wl, inp, args.cpu_seconds, z=gate["z"] if gate else None,
-                               zoh=args.zoh)
+            cpu, sample = cpu_baseline(wl, inp, args.cpu_seconds,
+                                       z=gate["z"] if gate else None, zoh=args.zoh)
+            parity = sample_error(sets[0][1], sample, wl.dtype)
+            log(f"  GPU output against the oracle on the sample: max_rel_err "
+                f"{parity['max_rel_err']:.3e} (limit {parity['tolerance']:.0e})")
+        cpu.setdefault("cpu_model", cpu_model())
         log(f"  {cpu['sample']} on {cpu['cores']} threads: {cpu['value']:.3e} updates/s")
 
     out = {
@@ -492,11 +618,16 @@ def main() -> int:
                             else "backward" if args.backward else
                             "front(dt_proj in scan)+forward" if args.front_lowrank else
                             "front+forward" if args.front else "forward")},
+        "ms_per_step_median": round(ms_median, 5),
+        "ms_per_step_min": round(ms_min, 5),
+        "clock_settle_steps": settle,
+        "input_sets_rotated": rotate,
         "hbm_gbps_algorithmic": round(gbps, 1),
         "hbm_frac_algorithmic": round(gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kernels.items() if n},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     if roofline_front is not None:
         out["roofline_front"] = roofline_front

@@ -48,9 +48,15 @@
  *     launched and y is untouched.  Nothing is printed and no exception crosses the ABI.
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default stream).
  *     Faults inside the kernels surface at the caller's next synchronisation.
- *   - The library keeps no state between calls.  Internal scratch (a transposed copy of x,
- *     per-route fp32 partial outputs, chunk carries) is taken from HIP's stream-ordered
- *     allocator on `stream` and released on `stream` in the same call.
+ *   - Calls keep no data between them.  Internal scratch (a transposed copy of x, per-route
+ *     fp32 partial outputs, chunk carries) is allocated on `stream` from a stream-ordered
+ *     memory pool of the library's own (one per device, created at the first call on that
+ *     device, held until the process ends) and released on `stream` in the same call.  The
+ *     pool keeps freed blocks for later calls (its release threshold is unlimited), so the
+ *     device memory of the largest scratch used so far stays reserved by the library; the
+ *     device's default pool and its attributes are not touched.  Under stream capture the
+ *     scratch becomes an allocation node of the graph (no synchronisation, copy or memset
+ *     is enqueued, so every entry point can be captured).
  *   - Results are deterministic: identical inputs, shapes and device give bitwise identical
  *     y (no atomics; the routes are summed in the fixed order 0, 1, 2, 3).
  *   - B == 0 or D == 0 is a valid empty call: it returns SS2D_OK, launches nothing and reads
@@ -68,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 7
+#define SS2D_ABI_VERSION 8
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -318,6 +324,18 @@ int ss1d_bidir_forward_routes_lr(const void *u, const void *dt_lr, const float *
                                  const float *Ds, const float *dt_bias, const void *z, void *y,
                                  int64_t B, int64_t D, int64_t L, int64_t N, int64_t R,
                                  int dtype, int flags, void *stream);
+
+/* ---- launch-plan override (testing and tuning, not part of the operator) ---------------
+ * Sets, for calls made later from the calling host thread only, the lanes that share one
+ * channel's states in the forward scan (split: 1, 2 or 4; 0 = automatic) and the chunk
+ * length of the chunked scan (chunk_len: 0 = one pass, > 0 = chunks of that many steps
+ * rounded up to a multiple of 32, -1 = automatic).  The override changes how the work is
+ * cut, not what is computed: any setting gives the operator's result (to rounding, which
+ * may differ with the cut).  A split that does not divide N, or split 2 with chunks, falls
+ * back to what the kernels support.  Returns SS2D_OK, SS2D_ERR_UNSUPPORTED for another
+ * split, or SS2D_ERR_SHAPE for chunk_len < -1 or >= 2^30.  The default on every thread is
+ * automatic (0, -1); no environment variable is read. */
+int ss2d_set_launch_plan(int split, int64_t chunk_len);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ss2d_status_string(int status);

@@ -54,6 +54,7 @@ SIGNATURES = {
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
+    "ss2d_set_launch_plan": (ctypes.c_int, [ctypes.c_int, _I64]),
     "ss2d_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "ss2d_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64)]),
@@ -533,6 +534,10 @@ def ss2d_backward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, H, W, z=None
     """Gradients of sum(dy * y) for y = ss2d_forward_routes(u, ..., H, W, z=z, zoh=zoh): a
     dict with the gradient of every input under its name, u's per route and step (B, 4, D,
     L), and z's when the gate is given."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 4, D, L)")
+    if u.shape[-1] != H * W:  # the library reads and writes rows of H * W steps
+        raise ValueError(f"u has {u.shape[-1]} steps, expected H * W = {H * W}")
     B, D = u.shape[0], u.shape[2]
     return _backward_routes(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, H, W), z, zoh,
                             stream)
@@ -544,6 +549,23 @@ def ss1d_bidir_backward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None
     B, D, L = u.shape[0], u.shape[2], u.shape[3]
     return _backward_routes(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, L), z, zoh,
                             stream)
+
+
+class launch_plan:
+    """Context manager: calls made inside it from this host thread use the given lanes per
+    channel (split 1, 2 or 4; 0 = automatic) and chunk length (0 = one pass, > 0 = chunks
+    of that many steps, -1 = automatic) in the forward scan; the automatic plan is restored
+    on exit.  For tests and tuning: the result is the operator's whatever the plan."""
+
+    def __init__(self, split: int = 0, chunk_len: int = -1):
+        self.split, self.chunk_len = int(split), int(chunk_len)
+
+    def __enter__(self):
+        _check(load_library().ss2d_set_launch_plan(self.split, self.chunk_len))
+        return self
+
+    def __exit__(self, *exc):
+        load_library().ss2d_set_launch_plan(0, -1)
 
 
 def timing_enable(enable: bool = True) -> bool:

@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -54,31 +53,56 @@ int hip_fail(hipError_t e) {
   return SS2D_ERR_HIP;
 }
 
-// Scratch comes from the device's default stream-ordered pool.  Keeping freed blocks in
-// the pool (instead of returning them to the driver at every synchronisation) makes the
-// per-call allocation a cheap pool hit after the first call.
-int prepare_pool(int device) {
+// Scratch comes from a stream-ordered memory pool that belongs to this library, one per
+// device, created on first use with an unlimited release threshold: freed blocks stay in
+// the pool for the next call instead of going back to the driver at every synchronisation,
+// so after the first call the per-call allocation is a pool hit.  The device's default pool
+// is left as it is.  Under stream capture the allocation becomes a node of the graph.
+constexpr int kMaxDevices = 64;
+int scratch_pool(int device, hipMemPool_t* out) {
   static std::mutex mu;
-  static bool done[64] = {};
+  static hipMemPool_t pools[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
   std::lock_guard<std::mutex> lock(mu);
-  if (device < 0 || device >= 64 || done[device]) return SS2D_OK;
-  hipMemPool_t pool;
-  hipError_t e = hipDeviceGetDefaultMemPool(&pool, device);
-  if (e != hipSuccess) return hip_fail(e);
-  uint64_t threshold = UINT64_MAX;
-  e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
-  if (e != hipSuccess) return hip_fail(e);
-  done[device] = true;
+  if (!pools[device]) {
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = device;
+    hipMemPool_t pool = nullptr;
+    hipError_t e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return hip_fail(e);
+    uint64_t threshold = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return hip_fail(e);
+    }
+    pools[device] = pool;
+  }
+  *out = pools[device];
   return SS2D_OK;
 }
 
-int64_t env_int(const char* name, int64_t fallback) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return fallback;
-  char* end = nullptr;
-  const long long r = std::strtoll(v, &end, 10);
-  return (end && *end == '\0') ? static_cast<int64_t>(r) : fallback;
+// Stream-ordered scratch of `bytes` on the current device, released by hipFreeAsync on the
+// same stream at the end of the call.
+int scratch_alloc(char** ws, size_t bytes, hipStream_t st) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e);
+  hipMemPool_t pool = nullptr;
+  const int rc = scratch_pool(device, &pool);
+  if (rc != SS2D_OK) return rc;
+  e = hipMallocFromPoolAsync(reinterpret_cast<void**>(ws), bytes < 256 ? 256 : bytes, pool, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return SS2D_OK;
 }
+
+// Launch-plan override of the calling host thread (ss2d_set_launch_plan): lanes per channel
+// (0: automatic) and chunk length (-1: automatic, 0: one pass).
+thread_local int g_split_override = 0;
+thread_local int64_t g_chunk_override = -1;
 
 constexpr int64_t kMaxL = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 62;
@@ -119,8 +143,7 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
   const int64_t L = H * W;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   int split = (N % 4 == 0) ? 4 : ((N % 2 == 0) ? 2 : 1);
-  const int64_t forced_split = env_int("SS2D_SPLIT", 0);
-  if (forced_split == 1 || forced_split == 2 || forced_split == 4) split = int(forced_split);
+  if (g_split_override != 0) split = g_split_override;
   if (split > N || N % split != 0) split = 1;
   const int64_t waves = B * K * ((D * split + 63) / 64);
   int64_t chunk = 0;
@@ -131,7 +154,7 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
     if (len < 64) len = 64;
     if (len < L) chunk = len;
   }
-  const int64_t forced_chunk = env_int("SS2D_CHUNK_LEN", -1);
+  const int64_t forced_chunk = g_chunk_override;
   if (forced_chunk >= 0) {
     int64_t len = ((forced_chunk + ss2d::kChunkAlign - 1) / ss2d::kChunkAlign) * ss2d::kChunkAlign;
     chunk = (len > 0 && len < L) ? len : 0;
@@ -261,15 +284,10 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
 
   // ---- plan and scratch --------------------------------------------------------------
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int device = 0;
-  hipError_t he = hipGetDevice(&device);
-  if (he != hipSuccess) return hip_fail(he);
-  int rc = prepare_pool(device);
-  if (rc != SS2D_OK) return rc;
   const Plan p = make_plan(K, B, D, H, W, N, dtype, routes);
   char* ws = nullptr;
-  he = hipMallocAsync(reinterpret_cast<void**>(&ws), p.bytes, st);
-  if (he != hipSuccess) return hip_fail(he);
+  int rc = scratch_alloc(&ws, p.bytes, st);
+  if (rc != SS2D_OK) return rc;
 
   ss2d::ScanArgs a{};
   a.x_row = x;
@@ -394,11 +412,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int device = 0;
-  hipError_t he = hipGetDevice(&device);
-  if (he != hipSuccess) return hip_fail(he);
-  int rc = prepare_pool(device);
-  if (rc != SS2D_OK) return rc;
+  int rc = SS2D_OK;
 
   // Scratch: transposes of x and of the route gradient g, checkpoints, per-route du, dB/dC
   // block partials and the per-image parameter partials; with the gate, g = dy SiLU(z) in
@@ -418,8 +432,11 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   if (gated) off = align256(off + size_t(n_x * 4));
   const size_t off_ck = off;
   off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
+  // per-route du in fp32: merged into dx, or (gate) first the route outputs; with per-route
+  // inputs and no gate the adjoint writes du straight to the output
+  const bool need_du = !routes || gated;
   const size_t off_du = off;
-  off = align256(off + size_t(n_dt) * 4);
+  if (need_du) off = align256(off + size_t(n_dt) * 4);
   const size_t off_bc = off;
   off = align256(off + size_t(B * K * n_cb) * size_t(2 * N * L) * 4);
   const size_t off_pa = off;
@@ -429,8 +446,8 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   const size_t off_pb = off;
   off = align256(off + size_t(B * K * D) * 4);
   char* ws = nullptr;
-  he = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
-  if (he != hipSuccess) return hip_fail(he);
+  rc = scratch_alloc(&ws, off, st);
+  if (rc != SS2D_OK) return rc;
 
   int err = 0;
   // g: the gradient every route's output receives (dy, or dy SiLU(z) with the gate)
@@ -504,7 +521,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     g.Ds = Ds;
     g.dt_bias = dt_bias;
     g.h_ck = reinterpret_cast<const float*>(ws + off_ck) + b0 * K * D * tiles * N;
-    g.du_route = reinterpret_cast<float*>(ws + off_du) + b0 * K * D * L;
+    g.du_route = need_du ? reinterpret_cast<float*>(ws + off_du) + b0 * K * D * L : nullptr;
     g.ddt_raw = static_cast<char*>(ddt_raw) + b0 * K * D * L * e;
     g.dbc_part = reinterpret_cast<float*>(ws + off_bc) + b0 * K * n_cb * 2 * N * L;
     g.dA_part = reinterpret_cast<float*>(ws + off_pa) + b0 * K * D * N;
@@ -606,13 +623,8 @@ int project(int K, const void* x, const float* conv_w, const float* conv_b,
       off_prep + ss2d::project_prep_bytes(K, int(D), int(N), int(R), dtype);
   char* ws = nullptr;
   {
-    int device = 0;
-    hipError_t he = hipGetDevice(&device);
-    if (he != hipSuccess) return hip_fail(he);
-    const int rc = prepare_pool(device);
+    const int rc = scratch_alloc(&ws, ws_bytes, st);
     if (rc != SS2D_OK) return rc;
-    he = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, st);
-    if (he != hipSuccess) return hip_fail(he);
   }
   int err = 0;
   if (need_t)
@@ -823,6 +835,14 @@ const char* ss2d_status_string(int status) {
 }
 
 int ss2d_abi_version(void) { return SS2D_ABI_VERSION; }
+
+int ss2d_set_launch_plan(int split, int64_t chunk_len) {
+  if (split != 0 && split != 1 && split != 2 && split != 4) return SS2D_ERR_UNSUPPORTED;
+  if (chunk_len < -1 || chunk_len >= kMaxL) return SS2D_ERR_SHAPE;
+  g_split_override = split;
+  g_chunk_override = chunk_len;
+  return SS2D_OK;
+}
 
 int ss2d_last_hip_error(void) { return g_last_hip_error; }
 

@@ -82,20 +82,16 @@ def assert_parity(y, ref, dtype: str, what: str, tol: dict = TOL) -> dict:
 
 
 class env_override:
-    """Temporarily set the library's launch-plan overrides (read at every call)."""
+    """Force the library's launch plan for calls from this thread inside the block:
+    SS2D_SPLIT (lanes per channel) and SS2D_CHUNK_LEN (0: one pass) as keyword arguments,
+    set through ss2d_set_launch_plan (the library reads no environment variable)."""
 
-    def __init__(self, **kv):
-        self.kv = {k: str(v) for k, v in kv.items()}
-        self.old = {}
+    def __init__(self, SS2D_SPLIT=0, SS2D_CHUNK_LEN=-1):
+        import selective_scan_ss2d_amd as ss
+        self.ctx = ss.launch_plan(int(SS2D_SPLIT), int(SS2D_CHUNK_LEN))
 
     def __enter__(self):
-        for k, v in self.kv.items():
-            self.old[k] = os.environ.get(k)
-            os.environ[k] = v
+        return self.ctx.__enter__()
 
     def __exit__(self, *exc):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        return self.ctx.__exit__(*exc)

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 7
+    assert lib.ss2d_abi_version() == 8
     seen = set()
     for code in range(7):
         s = lib.ss2d_status_string(code)
@@ -287,6 +287,51 @@ def test_backward_routes_argument_errors(lib):
         p = list(ptrs)
         p[0] = p[9] + 4 * (K - 1) * 8 * 64
         assert call(p) == bnd.SS2D_ERR_ALIAS
+
+
+def test_backward_routes_binding_checks_steps_against_map():
+    """The C entry point knows only H and W and takes rows of H * W steps; the binding must
+    refuse a u whose rows are of another length before anything reaches the library."""
+    import torch
+    import selective_scan_ss2d_amd as ss
+    B, K, D, N, H, W = 1, 4, 8, 4, 4, 5
+    for L in (H * W - 1, H * W + 1):
+        u = torch.zeros(B, K, D, L)
+        dt = torch.zeros(B, K, D, L)
+        bc = torch.zeros(B, K, N, L)
+        A = torch.zeros(K, D, N)
+        p = torch.zeros(K, D)
+        dy = torch.zeros(B, D, H, W)
+        with pytest.raises(ValueError, match="H \\* W"):
+            ss.ss2d_backward_routes(u, dt, A, bc, bc, p, p, dy, H, W)
+        with pytest.raises(ValueError, match="H \\* W"):
+            ss.ss2d_forward_routes(u, dt, A, bc, bc, p, p, H, W)
+
+
+def test_launch_plan_override_arguments(lib):
+    """ss2d_set_launch_plan accepts split 0/1/2/4 and chunk_len >= -1 (below 2^30), rejects
+    the rest without changing the setting, and the context manager restores automatic."""
+    import selective_scan_ss2d_amd as ss
+    for split in (0, 1, 2, 4):
+        for chunk in (-1, 0, 32, 100):
+            assert lib.ss2d_set_launch_plan(split, chunk) == bnd.SS2D_OK
+    for split in (-1, 3, 8, 16):
+        assert lib.ss2d_set_launch_plan(split, -1) == bnd.SS2D_ERR_UNSUPPORTED
+    for chunk in (-2, 1 << 30):
+        assert lib.ss2d_set_launch_plan(0, chunk) == bnd.SS2D_ERR_SHAPE
+    assert lib.ss2d_set_launch_plan(0, -1) == bnd.SS2D_OK
+    with pytest.raises(ss.SS2DError):
+        with ss.launch_plan(3, 0):
+            pass
+    with ss.launch_plan(4, 64):
+        pass
+
+
+def test_library_reads_no_environment():
+    """The launch plan is not steered by environment variables: the library's source holds
+    no getenv."""
+    for f in (ROOT / "selective_scan_ss2d_amd" / "csrc").iterdir():
+        assert "getenv" not in f.read_text(), f.name
 
 
 # ---- per-route front end and the operator over per-route inputs ---------------------------

@@ -115,13 +115,12 @@ def test_backward_ex_full_size(orc, name, gate, zoh):
 
 @pytest.mark.parametrize("zoh", [False, True], ids=["plain", "zoh"])
 @pytest.mark.parametrize("K", [4, 2])
-def test_backward_gated_at_zero(monkeypatch, K, zoh):
+def test_backward_gated_at_zero(K, zoh):
     """At z = 0 the gate passes nothing on (SiLU(0) = 0): every input's gradient is exactly
     zero, and dz = dy * y * SiLU'(0) = dy * y / 2, bit for bit the forward entry point's y
     (fp32, the same one-pass scan) times dy, halved."""
     import torch
     import selective_scan_ss2d_amd as ss
-    monkeypatch.setenv("SS2D_CHUNK_LEN", "0")  # the forward in one pass, as the checkpoints
     wl = workloads.custom(2, 96, 8, 12, 16, 4, "f32") if K == 4 else \
         workloads.custom(2, 96, 1, 100, 16, 2, "f32")
     log(f"case gated backward at z = 0, K={K} zoh={zoh}")
@@ -130,7 +129,8 @@ def test_backward_gated_at_zero(monkeypatch, K, zoh):
     z = torch.zeros_like(dy)
     grads = run_bwd_ex(dev, wl, dy, z, zoh)
     fwd = ss.ss2d_forward_ex if K == 4 else ss.ss1d_bidir_forward_ex
-    y = fwd(*[dev[k] for k in ARGS], zoh=zoh)
+    with ss.launch_plan(0, 0):  # the forward in one pass, as the checkpoints
+        y = fwd(*[dev[k] for k in ARGS], zoh=zoh)
     torch.cuda.synchronize()
     for name in ARGS:
         assert torch.count_nonzero(grads[name]).item() == 0, name

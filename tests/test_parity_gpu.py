@@ -2,7 +2,7 @@
 
 Element-by-element on sizes the oracle finishes in seconds (ragged channel counts, odd and
 non-square maps, every supported state size, every launch variant forced through the
-plan overrides); on sampled whole channels at the full benchmark sizes, in the launch
+plan overrides); at the full benchmark sizes, every output element, in the launch
 configuration the benchmark times.  Plus determinism, NaN propagation, streams, empty
 inputs and argument errors.
 """
@@ -103,35 +103,28 @@ def test_bidir_variants(orc, var):
                **var)
 
 
-# ---- full benchmark sizes, sampled whole channels, default launch plan -------------
-def sample_channels(B, D, count=12, seed=0):
-    rng = np.random.default_rng(seed)
-    pairs = {(0, 0), (B - 1, D - 1), (0, D - 1), (B - 1, 0)}
-    while len(pairs) < min(count, B * D):
-        pairs.add((int(rng.integers(B)), int(rng.integers(D))))
-    pairs = sorted(pairs)
-    return np.array([p[0] for p in pairs]), np.array([p[1] for p in pairs])
-
-
-@pytest.mark.parametrize("name,a_log", [("vmamba_t_stage1_f32", "init"),
+# ---- full benchmark sizes, every output element, default launch plan ----------------
+@pytest.mark.parametrize("name,a_log", [("tiny_f32", "init"),
+                                        ("vmamba_t_stage1_f32", "init"),
                                         ("vmamba_t_stage1_bf16", "init"),
                                         ("vmamba_t_stage1_bf16", "random"),
                                         ("highres_1024px_bf16", "init"),
                                         ("vim_bidir_bf16", "init")])
-def test_full_size_sampled(orc, name, a_log):
+def test_full_size(orc, name, a_log):
+    """The whole output of every benchmark workload, in the launch plan the benchmark times,
+    against the oracle's whole output (computed on all host cores)."""
     import torch
     wl = workloads.workload(name)
     log(f"case full-size {name} a_log={a_log}: generating inputs")
     inp = workloads.make_inputs(wl, seed=0, a_log=a_log)
     dev = to_device(inp, wl)
     log(f"case full-size {name}: GPU run")
-    y = run_gpu(dev, wl)
+    y = to_numpy_f64(run_gpu(dev, wl))
     torch.cuda.synchronize()
-    bi, di = sample_channels(wl.B, wl.D)
-    ys = to_numpy_f64(y[torch.as_tensor(bi), torch.as_tensor(di)])
-    ref = orc.forward_channels(wl.K, *[inp[k] for k in ARGS], bi, di)
-    del dev, y
-    assert_parity(ys, ref, wl.dtype, f"{name} ({len(bi)} sampled channels)")
+    del dev
+    log(f"case full-size {name}: oracle")
+    ref = oracle_full(orc, inp, wl)
+    assert_parity(y, ref, wl.dtype, f"{name} a_log={a_log} (all {y.size} outputs)")
 
 
 # ---- determinism -------------------------------------------------------------------
