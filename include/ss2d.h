@@ -87,6 +87,8 @@ extern "C" {
 #define SS2D_ERR_ALIGN 4       /* a pointer not aligned to its element size                 */
 #define SS2D_ERR_HIP 5         /* a HIP runtime call failed (see ss2d_last_hip_error)       */
 #define SS2D_ERR_ALIAS 6       /* an output overlaps an input (or another output)            */
+#define SS2D_ERR_SCRATCH 7     /* ss2d_forward_noalloc: the call needs more scratch than
+                                  SS2D_NOALLOC_SCRATCH_BYTES                               */
 
 /* Data types of x, dt_raw, Bs, Cs and y. */
 #define SS2D_F32 0
@@ -134,6 +136,33 @@ int ss1d_bidir_forward_ex(const void *x, const void *dt_raw, const float *A_log,
                           const void *Bs, const void *Cs, const float *Ds,
                           const float *dt_bias, const void *z, void *y, int64_t B, int64_t D,
                           int64_t L, int64_t N, int dtype, int flags, void *stream);
+
+/* ---- the forward without allocation ----------------------------------------------------------
+ * For callers that cannot allocate device memory during the call: code under HIP graph
+ * capture that must not record allocation nodes, tight serving loops, harnesses that forbid
+ * hipMalloc.  ss2d_forward_noalloc is ss2d_forward_ex (same arguments, same kernels, same
+ * result bit for bit) except for its scratch (the transposed copy of x, the per-route fp32
+ * outputs, chunk carries): instead of the stream-ordered pool it uses a fixed device array
+ * of SS2D_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until the
+ * process ends.  The call allocates and frees nothing (no hipMalloc, hipFree or stream-
+ * ordered allocation; the array's address is looked up once per device at its first call).
+ *
+ * Size limit: the scratch a call needs is about 2 bytes per element of x for the
+ * transposed copy (4 for fp32 data) plus 16 bytes per element of x for the four routes'
+ * fp32 outputs, plus chunk carries when the plan cuts long sequences (e.g. the fp32
+ * VMamba-T stage-1 shape with B = 8, D = 192, 56 x 56, N = 16 needs ~103 MB); a call needing
+ * more returns SS2D_ERR_SCRATCH before anything is enqueued.  Use ss2d_forward_ex for
+ * larger calls.
+ *
+ * Every call on one device shares that device's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): two calls that overlap in time on one
+ * device (on different streams, or from different host threads) race on it and give
+ * undefined results.  Calls on one stream are ordered and safe. */
+#define SS2D_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int ss2d_forward_noalloc(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                         const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                         void *y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                         int dtype, int flags, void *stream);
 
 /* ---- backward ---------------------------------------------------------------------------
  * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output

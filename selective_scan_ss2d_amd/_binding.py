@@ -21,6 +21,7 @@ SS2D_ERR_UNSUPPORTED = 3
 SS2D_ERR_ALIGN = 4
 SS2D_ERR_HIP = 5
 SS2D_ERR_ALIAS = 6
+SS2D_ERR_SCRATCH = 7
 SS2D_F32 = 0
 SS2D_BF16 = 1
 SS2D_FLAG_ZOH = 1
@@ -33,6 +34,7 @@ SIGNATURES = {
     "ss1d_bidir_forward": (ctypes.c_int, [_P] * 8 + [_I64] * 4 + [ctypes.c_int, _P]),
     "ss2d_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_forward_ex": (ctypes.c_int, [_P] * 9 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_forward_noalloc": (ctypes.c_int, [_P] * 9 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 5 + [ctypes.c_int, _P]),
     "ss1d_bidir_backward": (ctypes.c_int, [_P] * 15 + [_I64] * 4 + [ctypes.c_int, _P]),
     "ss2d_backward_ex": (ctypes.c_int, [_P] * 17 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),

@@ -99,6 +99,33 @@ int scratch_alloc(char** ws, size_t bytes, hipStream_t st) {
   return SS2D_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing ---------------------------------------
+// A file-scope device array: every device the library runs on holds its own copy, from the
+// time the library's code is loaded on it until the process ends.  In host code the array's
+// name is only a handle for hipGetSymbolAddress: its device address is looked up once per
+// device (with that device current) and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = SS2D_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(char** out) {
+  static std::mutex mu;
+  static char* ptrs[kMaxDevices] = {};
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e);
+  if (device < 0 || device >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[device]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+    ptrs[device] = static_cast<char*>(ptr);
+  }
+  *out = ptrs[device];
+  return SS2D_OK;
+}
+
 // Launch-plan override of the calling host thread (ss2d_set_launch_plan): lanes per channel
 // (0: automatic) and chunk length (-1: automatic, 0: one pass).
 thread_local int g_split_override = 0;
@@ -244,7 +271,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
             const void* Bs, const void* Cs, const float* Ds, const float* dt_bias, const void* z,
             void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
             int flags, void* stream, const void* dt_lr = nullptr, const float* dt_w = nullptr,
-            int64_t R = 0) {
+            int64_t R = 0, bool noalloc = false) {
   const bool lr = dt_lr != nullptr || dt_w != nullptr || R != 0;
   // ---- validation (nothing is enqueued before all of it passes) -------------------------
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
@@ -285,8 +312,10 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   // ---- plan and scratch --------------------------------------------------------------
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan p = make_plan(K, B, D, H, W, N, dtype, routes);
+  // noalloc: the scratch is the fixed device array (size checked before any HIP call)
+  if (noalloc && p.bytes > kNoAllocScratchBytes) return SS2D_ERR_SCRATCH;
   char* ws = nullptr;
-  int rc = scratch_alloc(&ws, p.bytes, st);
+  int rc = noalloc ? noalloc_scratch(&ws) : scratch_alloc(&ws, p.bytes, st);
   if (rc != SS2D_OK) return rc;
 
   ss2d::ScanArgs a{};
@@ -350,7 +379,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
                       : ss2d::launch_merge2(a.y_route, z, y, a.B, a.D, a.L, dtype, st);
     });
   }
-  const hipError_t fe = hipFreeAsync(ws, st);
+  const hipError_t fe = noalloc ? hipSuccess : hipFreeAsync(ws, st);
   if (err) return hip_fail(static_cast<hipError_t>(err));
   if (rc != SS2D_OK) return rc;
   if (fe != hipSuccess) return hip_fail(fe);
@@ -689,6 +718,14 @@ int ss2d_forward_ex(const void* x, const void* dt_raw, const float* A_log, const
                  stream);
 }
 
+int ss2d_forward_noalloc(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                         const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                         void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                         int dtype, int flags, void* stream) {
+  return forward(4, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype, flags,
+                 stream, nullptr, nullptr, 0, true);
+}
+
 int ss1d_bidir_forward_ex(const void* x, const void* dt_raw, const float* A_log,
                           const void* Bs, const void* Cs, const float* Ds,
                           const float* dt_bias, const void* z, void* y, int64_t B, int64_t D,
@@ -830,6 +867,8 @@ const char* ss2d_status_string(int status) {
     case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SS2D_ERR_HIP: return "a HIP runtime call failed";
     case SS2D_ERR_ALIAS: return "the output overlaps an input";
+    case SS2D_ERR_SCRATCH:
+      return "the call needs more scratch than the fixed array of ss2d_forward_noalloc holds";
     default: return "unknown status";
   }
 }

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_abi_version_and_status_strings(lib):
     assert lib.ss2d_abi_version() == 8
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = lib.ss2d_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -325,6 +325,29 @@ def test_launch_plan_override_arguments(lib):
             pass
     with ss.launch_plan(4, 64):
         pass
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_hip_call(lib):
+    """ss2d_forward_noalloc checks the scratch the plan needs against its fixed array
+    before it touches the HIP runtime: on a machine without a GPU, a call that is too large
+    returns SS2D_ERR_SCRATCH (not SS2D_ERR_HIP), and its argument errors are those of
+    ss2d_forward_ex."""
+    import torch
+    ptrs = fake_ptrs(9)
+    ptrs[7] = None  # no gate
+
+    def call(B, D, H, W, N=16, dtype=bnd.SS2D_BF16, flags=0, p=ptrs):
+        return lib.ss2d_forward_noalloc(*p, B, D, H, W, N, dtype, flags, None)
+    assert call(64, 192, 56, 56) == bnd.SS2D_ERR_SCRATCH      # ~694 MB
+    assert call(16, 192, 56, 56, dtype=bnd.SS2D_F32) == bnd.SS2D_ERR_SCRATCH
+    assert call(1, 8, 8, 8, flags=2) == bnd.SS2D_ERR_UNSUPPORTED
+    p = list(ptrs)
+    p[0] = None
+    assert call(1, 8, 8, 8, p=p) == bnd.SS2D_ERR_NULL
+    assert call(0, 8, 8, 8) == bnd.SS2D_OK
+    if not torch.cuda.is_available():  # within the limit the call reaches the runtime
+        assert call(8, 192, 56, 56, dtype=bnd.SS2D_F32) == bnd.SS2D_ERR_HIP
+    assert b"scratch" in lib.ss2d_status_string(bnd.SS2D_ERR_SCRATCH)
 
 
 def test_library_reads_no_environment():
