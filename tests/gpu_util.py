@@ -16,10 +16,13 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 # Gradients chain two fp32 recurrences (the recomputed forward and the adjoint) and sum up
 # to B * L terms of both signs for the parameters: twice the forward bar for fp32 data.
 TOL_BWD = {"f32": 2e-4, "bf16": 2e-2}
-# The front end's x_proj outputs are D-term fp32 sums (relative error ~ sqrt(D) 2^-24 of
-# their scale), and dt_raw combines R of them with either sign: entries that cancel to
-# below the 1% floor carry that error against the floor.  Twice the forward bar for fp32.
-TOL_FRONT = {"f32": 2e-4, "bf16": 2e-2}
+# The front end's outputs (u, x_proj's B, C and dt rows) and the chained forward meet the
+# forward bar.  dt_raw = dt_proj(x_proj's R dt rows) combines R fp32 D-term sums with either
+# sign: its entries that cancel to below the 1% floor carry those sums' rounding against
+# the floor, and a plain fp32 implementation already reaches 1e-4 there for some summation
+# orders (tests/test_front_fp32_floor.py): twice the forward bar for fp32 dt_raw.
+TOL_FRONT = {"f32": 1e-4, "bf16": 2e-2}
+TOL_DT_RAW = {"f32": 2e-4, "bf16": 2e-2}
 
 
 def log(msg: str) -> None:
