@@ -183,8 +183,11 @@ int ss2d_forward_noalloc(const void *x, const void *dt_raw, const float *A_log, 
  * taken in a fixed order, so results are deterministic.
  *
  * Supported: the plain operator (no gate, delta * B; ss2d_backward_ex below takes the gate
- * and the zero-order hold) with N in {4, 8, 16}; other N give
- * SS2D_ERR_UNSUPPORTED.  Otherwise the conventions of ss2d_forward apply. */
+ * and the zero-order hold) with N in {1, 2, 4, 8, 16, 32}, as the forward; other N give
+ * SS2D_ERR_UNSUPPORTED.  The kernels split each channel's states over four lanes: N = 1
+ * and 2 run as four states, the extra ones with zero B and C rows, which keep them exactly
+ * zero (scratch: padded copies of Bs, Cs and A_log and of their gradients); N = 32 runs at
+ * two waves per SIMD.  Otherwise the conventions of ss2d_forward apply. */
 int ss2d_backward(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
                   const void *Cs, const float *Ds, const float *dt_bias, const void *dy,
                   void *dx, void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,

@@ -400,7 +400,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
   if (B < 0 || D < 0 || H < 1 || W < 1 || N < 1) return SS2D_ERR_SHAPE;
-  if (N != 4 && N != 8 && N != 16) return SS2D_ERR_UNSUPPORTED;
+  if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS2D_ERR_UNSUPPORTED;
   if (H >= kMaxL || W >= kMaxL || H * W >= kMaxL) return SS2D_ERR_SHAPE;
   const int64_t L = H * W;
   if (D >= (int64_t(1) << 31) / 4 || B >= (int64_t(1) << 31)) return SS2D_ERR_SHAPE;
@@ -442,6 +442,54 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   int rc = SS2D_OK;
+
+  if (N < 4) {
+    // N = 1 or 2: the kernels split a channel's states over four lanes, so the call runs
+    // with four states, the extra ones with zero B and C rows (and A_log 0).  Their states
+    // and adjoints stay exactly zero, so they add exactly nothing to any sum over states:
+    // the gradients of the real states are those of the N-state operator.  Padded copies of
+    // Bs, Cs and A_log and the padded dBs, dCs and dA_log live in scratch; the first N rows
+    // of the latter are copied out.
+    constexpr int64_t NP = 4;
+    const int64_t n_pad = B * K * NP * L;
+    size_t po = 0;
+    const size_t o_bs = po;
+    po = align256(po + size_t(n_pad * e));
+    const size_t o_cs = po;
+    po = align256(po + size_t(n_pad * e));
+    const size_t o_dbs = po;
+    po = align256(po + size_t(n_pad * e));
+    const size_t o_dcs = po;
+    po = align256(po + size_t(n_pad * e));
+    const size_t o_al = po;
+    po = align256(po + size_t(K * D * NP) * 4);
+    const size_t o_dal = po;
+    po = align256(po + size_t(K * D * NP) * 4);
+    char* pw = nullptr;
+    rc = scratch_alloc(&pw, po, st);
+    if (rc != SS2D_OK) return rc;
+    const int ni = static_cast<int>(N);
+    int err = ss2d::launch_copy_rows(Bs, pw + o_bs, B * K, ni, 4, L, int(e), st);
+    if (!err) err = ss2d::launch_copy_rows(Cs, pw + o_cs, B * K, ni, 4, L, int(e), st);
+    if (!err) err = ss2d::launch_copy_rows(A_log, pw + o_al, int64_t(K) * D, ni, 4, 1, 4, st);
+    if (!err) {
+      rc = backward(K, x, dt_raw, reinterpret_cast<const float*>(pw + o_al), pw + o_bs,
+                    pw + o_cs, Ds, dt_bias, dy, dx, ddt_raw,
+                    reinterpret_cast<float*>(pw + o_dal), pw + o_dbs, pw + o_dcs, dDs, ddt_bias,
+                    B, D, H, W, NP, dtype, stream, z, dz, flags, routes);
+    }
+    if (!err && rc == SS2D_OK) {
+      err = ss2d::launch_copy_rows(pw + o_dbs, dBs, B * K, 4, ni, L, int(e), st);
+      if (!err) err = ss2d::launch_copy_rows(pw + o_dcs, dCs, B * K, 4, ni, L, int(e), st);
+      if (!err)
+        err = ss2d::launch_copy_rows(pw + o_dal, dA_log, int64_t(K) * D, 4, ni, 1, 4, st);
+    }
+    const hipError_t fe = hipFreeAsync(pw, st);
+    if (err) return hip_fail(static_cast<hipError_t>(err));
+    if (rc != SS2D_OK) return rc;
+    if (fe != hipSuccess) return hip_fail(fe);
+    return SS2D_OK;
+  }
 
   // Scratch: transposes of x and of the route gradient g, checkpoints, per-route du, dB/dC
   // block partials and the per-image parameter partials; with the gate, g = dy SiLU(z) in

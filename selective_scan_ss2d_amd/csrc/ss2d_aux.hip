@@ -595,6 +595,23 @@ k_bwd_reduce_params(const float* __restrict__ dA_part, const float* __restrict__
   *dst = static_cast<float>(v);
 }
 
+// Rows of `len` elements in blocks of rows_in rows to blocks of rows_out rows (outer blocks in
+// order): row r of a block is copied when r < rows_in, zero-filled otherwise.  With
+// rows_out < rows_in the first rows_out rows of each block are kept.
+template <typename E>
+__global__ void __launch_bounds__(256)
+k_copy_rows(const E* __restrict__ src, E* __restrict__ dst, int64_t outer, int rows_in,
+            int rows_out, int64_t len) {
+  const int64_t total = outer * rows_out * len;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = i % len;
+    const int64_t r = (i / len) % rows_out;
+    const int64_t o = i / (len * rows_out);
+    dst[i] = r < rows_in ? src[(o * rows_in + r) * len + t] : E(0);
+  }
+}
+
 }  // namespace
 
 int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, int N, int L,
@@ -622,6 +639,23 @@ int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, 
     hipLaunchKernelGGL(k_bwd_reduce_bc<uint16_t>, dim3(blocks), dim3(256), 0, st, part,
                        static_cast<uint16_t*>(dBs), static_cast<uint16_t*>(dCs), N, L, n_cb,
                        total);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_copy_rows(const void* src, void* dst, int64_t outer, int rows_in, int rows_out,
+                     int64_t len, int elem_bytes, hipStream_t st) {
+  const int64_t total = outer * rows_out * len;
+  if (total <= 0) return 0;
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_copy_rows<uint16_t>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), outer,
+                       rows_in, rows_out, len);
+  else
+    hipLaunchKernelGGL(k_copy_rows<float>, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const float*>(src), static_cast<float*>(dst), outer, rows_in,
+                       rows_out, len);
   return static_cast<int>(hipGetLastError());
 }
 

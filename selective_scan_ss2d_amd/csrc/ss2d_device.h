@@ -253,6 +253,10 @@ int launch_scan_bwd_bf16_zoh(const BwdArgs& a, hipStream_t st);
 // images (fixed order).
 int launch_bwd_reduce_bc(const float* part, void* dBs, void* dCs, int B, int K, int N, int L,
                          int n_cb, int dtype, hipStream_t st);
+// Copies blocks of rows_in rows of len elements (2 or 4 bytes each) into blocks of rows_out
+// rows, zero-filling rows past rows_in (or keeping the first rows_out rows).
+int launch_copy_rows(const void* src, void* dst, int64_t outer, int rows_in, int rows_out,
+                     int64_t len, int elem_bytes, hipStream_t st);
 int launch_bwd_reduce_params(const float* dA_part, const float* dD_part,
                              const float* dbias_part, float* dA_log, float* dDs,
                              float* ddt_bias, int B, int K, int D, int N, hipStream_t st);

@@ -179,7 +179,7 @@ def test_backward_argument_errors(lib):
             p = list(ptrs)
             p[i] = None
             assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
-        for N in (1, 2, 32, 3):
+        for N in (3, 5, 64, 12):
             assert call_bwd(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
         assert call_bwd(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
         assert call_bwd(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
@@ -197,7 +197,8 @@ def test_backward_argument_errors(lib):
         assert call_bwd(lib, p, K=K) == bnd.SS2D_ERR_ALIAS
     import torch
     if not torch.cuda.is_available():
-        assert call_bwd(lib, ptrs) == bnd.SS2D_ERR_HIP
+        for N in (1, 2, 4, 8, 16, 32):
+            assert call_bwd(lib, ptrs, N=N) == bnd.SS2D_ERR_HIP, N
 
 
 def call_bwd_ex(lib, ptrs, B=1, D=8, H=8, W=8, N=4, dtype=0, K=4, flags=0):
@@ -217,7 +218,7 @@ def test_backward_ex_argument_errors(lib):
             p = list(ptrs)
             p[i] = None
             assert call_bwd_ex(lib, p, K=K) == bnd.SS2D_ERR_NULL, (K, i)
-        for N in (1, 2, 32, 3):
+        for N in (3, 5, 64, 12):
             assert call_bwd_ex(lib, ptrs, N=N, K=K) == bnd.SS2D_ERR_UNSUPPORTED
         assert call_bwd_ex(lib, ptrs, dtype=5, K=K) == bnd.SS2D_ERR_UNSUPPORTED
         assert call_bwd_ex(lib, ptrs, B=-1, K=K) == bnd.SS2D_ERR_SHAPE
@@ -271,7 +272,7 @@ def test_backward_routes_argument_errors(lib):
             p = list(ptrs)
             p[i] = None
             assert call(p) == bnd.SS2D_ERR_NULL, (K, i)
-        assert call(ptrs, N=32) == bnd.SS2D_ERR_UNSUPPORTED
+        assert call(ptrs, N=64) == bnd.SS2D_ERR_UNSUPPORTED
         assert call(ptrs, flags=2) == bnd.SS2D_ERR_UNSUPPORTED
         assert call(ptrs, B=-1) == bnd.SS2D_ERR_SHAPE
         assert call([None] * 17, B=0) == bnd.SS2D_OK

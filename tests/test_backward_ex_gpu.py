@@ -74,6 +74,10 @@ SHAPES = [  # B, D, H, W, N, K, dtype
     (1, 65, 1, 37, 4, 2, "f32"),
     (1, 33, 1, 40, 8, 4, "f32"),      # degenerate maps: the column routes need no transpose
     (2, 24, 17, 1, 16, 4, "bf16"),
+    (2, 70, 5, 7, 1, 4, "f32"),       # N = 1, 2: four states with zero-padded B and C
+    (1, 40, 1, 100, 2, 2, "bf16"),
+    (2, 70, 5, 7, 32, 4, "f32"),      # N = 32: two waves per SIMD
+    (2, 64, 1, 197, 32, 2, "bf16"),
 ]
 
 

@@ -64,6 +64,13 @@ SHAPES = [  # B, D, H, W, N, K, dtype
     (1, 65, 1, 37, 4, 2, "f32"),
     (1, 33, 1, 40, 8, 4, "f32"),      # degenerate maps: the column routes need no transpose
     (2, 24, 17, 1, 16, 4, "bf16"),
+    # N = 1 and 2 (run as four states with zero-padded B and C), N = 32 (two waves per SIMD)
+    (2, 70, 5, 7, 1, 4, "f32"),
+    (2, 70, 5, 7, 2, 4, "bf16"),
+    (1, 33, 1, 150, 2, 2, "f32"),
+    (2, 70, 5, 7, 32, 4, "f32"),
+    (2, 130, 12, 20, 32, 4, "bf16"),
+    (2, 64, 1, 197, 32, 2, "bf16"),
 ]
 
 

@@ -69,6 +69,8 @@ SHAPES = [  # B, D, H, W, N, K, dtype
     (1, 33, 1, 40, 8, 4, "f32"),
     (3, 100, 1, 197, 16, 2, "bf16"),
     (2, 64, 1, 320, 16, 2, "f32"),
+    (2, 70, 5, 7, 2, 4, "f32"),       # N = 2: four states with zero-padded B and C
+    (2, 70, 5, 7, 32, 4, "bf16"),     # N = 32
 ]
 
 
