@@ -388,7 +388,8 @@ int ss2d_last_hip_error(void);
 #define SS2D_KERNEL_TRANSPOSE 0 /* per-plane transpose of x for the column routes      */
 #define SS2D_KERNEL_SCAN 1      /* selective scan producing per-route outputs          */
 #define SS2D_KERNEL_CHUNK_AGG 2 /* chunked scan, first pass (chunk end states)         */
-#define SS2D_KERNEL_CARRY 3     /* chunk carries                                       */
+#define SS2D_KERNEL_CARRY 3     /* not launched: chunk start states are composed in the
+                                   scan's second pass (the kind keeps its number)        */
 #define SS2D_KERNEL_MERGE 4     /* cross-merge into y (backward: route gradients into dx) */
 #define SS2D_KERNEL_CHECKPOINT 5 /* backward: forward pass storing states every 32 steps */
 #define SS2D_KERNEL_SCAN_BWD 6  /* backward: adjoint scan                               */

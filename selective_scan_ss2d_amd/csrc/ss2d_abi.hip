@@ -154,7 +154,7 @@ struct Plan {
   int num_chunks = 1;
   int chunk_len = 0;
   bool need_xt = false;
-  size_t off_xt = 0, off_yr = 0, off_hend = 0, off_dsum = 0, off_hin = 0, bytes = 0;
+  size_t off_xt = 0, off_yr = 0, off_hend = 0, off_dsum = 0, bytes = 0;
 };
 
 // Launch plan.  The scan wants about three resident waves per SIMD (256 CUs x 4 SIMDs)
@@ -210,8 +210,6 @@ Plan make_plan(int K, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int
     off = align256(off + rows * size_t(N) * 4);
     p.off_dsum = off;
     off = align256(off + rows * 4);
-    p.off_hin = off;
-    off = align256(off + rows * size_t(N) * 4);
   }
   p.bytes = off;
   return p;
@@ -353,19 +351,16 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   if (!err && p.num_chunks > 1) {
     a.h_end = reinterpret_cast<float*>(ws + p.off_hend);
     a.delta_sum = reinterpret_cast<float*>(ws + p.off_dsum);
-    a.h_in = reinterpret_cast<float*>(ws + p.off_hin);
     ss2d::ScanArgs agg = a;  // aggregates of chunks 0 .. C-2
     agg.chunk_base = 0;
     agg.chunks_in_launch = p.num_chunks - 1;
     rc = scan_pass(agg, dtype, p, ss2d::kModeAgg, e, st);
-    if (rc == SS2D_OK) {
-      err = timed(SS2D_KERNEL_CARRY, st, [&] { return ss2d::launch_carry(a, st); });
-      if (!err) {
-        ss2d::ScanArgs out = a;
-        out.chunk_base = 0;
-        out.chunks_in_launch = p.num_chunks;
-        rc = scan_pass(out, dtype, p, ss2d::kModeOut, e, st);
-      }
+    if (rc == SS2D_OK) {  // the second pass composes the aggregates into chunk start states
+      ss2d::ScanArgs out = a;
+      out.h_in = nullptr;
+      out.chunk_base = 0;
+      out.chunks_in_launch = p.num_chunks;
+      rc = scan_pass(out, dtype, p, ss2d::kModeOut, e, st);
     }
   } else if (!err) {
     a.chunk_base = 0;

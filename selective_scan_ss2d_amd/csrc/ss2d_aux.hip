@@ -1,6 +1,6 @@
 // Support kernels of the SS2D forward operator (gfx950): the per-plane transpose that turns
-// the column routes into contiguous walks, the chunk-carry pass of the chunked scan, and the
-// cross-merge that undoes each route's permutation and sums the routes in a fixed order.
+// the column routes into contiguous walks, and the cross-merge that undoes each route's
+// permutation and sums the routes in a fixed order.
 #include <type_traits>
 
 #include "ss2d_device.h"
@@ -180,28 +180,6 @@ k_transpose_f32_4x4(const float* __restrict__ x, float* __restrict__ xt, int H, 
     *reinterpret_cast<float4*>(dst + H) = make_float4(r0.y, r1.y, r2.y, r3.y);
     *reinterpret_cast<float4*>(dst + 2 * H) = make_float4(r0.z, r1.z, r2.z, r3.z);
     *reinterpret_cast<float4*>(dst + 3 * H) = make_float4(r0.w, r1.w, r2.w, r3.w);
-  }
-}
-
-// Start state of every chunk c >= 1 of every (b, k, d) scan, one thread per state n:
-//   h_in[c + 1] = exp(A_n * sum of delta over chunk c) * h_in[c] + h_end[c],  h_in[0] = 0,
-// where h_end[c] is chunk c's end state from a zero start.  This is the composition of the
-// affine maps h -> a h + b of consecutive chunks, applied in order.
-__global__ void __launch_bounds__(256) k_carry(const ScanArgs a) {
-  const int64_t total = static_cast<int64_t>(a.B) * a.K * a.D * a.N;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int n = static_cast<int>(i % a.N);
-  const int64_t row = i / a.N;                 // (b * K + k) * D + d
-  const int d = static_cast<int>(row % a.D);
-  const int k = static_cast<int>((row / a.D) % a.K);
-  const float Ap = -expf(a.A_log[(static_cast<int64_t>(k) * a.D + d) * a.N + n]) * kLog2e;
-  const int C = a.num_chunks;
-  float h = 0.0f;
-  for (int c = 0; c + 1 < C; ++c) {
-    const float decay = exp2_hw(Ap * a.delta_sum[row * C + c]);
-    h = fmaf(decay, h, a.h_end[(row * C + c) * a.N + n]);
-    a.h_in[(row * C + c + 1) * a.N + n] = h;
   }
 }
 
@@ -706,13 +684,6 @@ int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dt
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, block, 0, st,
                        static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xt), H, W,
                        planes);
-  return static_cast<int>(hipGetLastError());
-}
-
-int launch_carry(const ScanArgs& a, hipStream_t st) {
-  const int64_t total = static_cast<int64_t>(a.B) * a.K * a.D * a.N;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(k_carry, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
   return static_cast<int>(hipGetLastError());
 }
 

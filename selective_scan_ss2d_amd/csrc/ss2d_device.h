@@ -161,7 +161,7 @@ struct ScanArgs {
   float* y_route;         // (B, K, D, L) fp32 per-route outputs in scan order
   float* h_end;           // (B, K, D, C, N) chunk end states from a zero start
   float* delta_sum;       // (B, K, D, C) sum of delta over each chunk
-  float* h_in;            // (B, K, D, C, N) chunk start states (chunk 0 starts at zero)
+  float* h_in;            // kModeCkpt(Out): the states before each 32-step tile
   int B, K, D, L, N;
   int num_chunks;         // C
   int chunk_len;          // steps per chunk, a multiple of kChunkAlign (>= L when C == 1)
@@ -244,7 +244,6 @@ int launch_scan_f32_zoh_lr(const ScanArgs& a, int split, int mode, hipStream_t s
 int launch_scan_bf16_zoh_lr(const ScanArgs& a, int split, int mode, hipStream_t st);
 int launch_transpose(const void* x, void* xt, int B, int D, int H, int W, int dtype,
                      hipStream_t st);
-int launch_carry(const ScanArgs& a, hipStream_t st);
 int launch_scan_bwd_f32(const BwdArgs& a, hipStream_t st);
 int launch_scan_bwd_bf16(const BwdArgs& a, hipStream_t st);
 int launch_scan_bwd_f32_zoh(const BwdArgs& a, hipStream_t st);
