@@ -400,14 +400,16 @@ def main() -> int:
             d[k] = torch.from_numpy(arrays[k]).to("cuda:0")
         return d
 
-    def image(arr, arr_bf16):
-        return (torch.from_numpy(arr_bf16.view(np.int16)).view(torch.bfloat16)
-                if wl.dtype == "bf16" else torch.from_numpy(arr)).to("cuda:0")
+    def image(arrays, key):
+        """An image-shaped input (B, D, ...) on the device: its bf16 bit patterns for bf16
+        workloads, else the fp32 array."""
+        return (torch.from_numpy(arrays[key + "_bf16"].view(np.int16)).view(torch.bfloat16)
+                if wl.dtype == "bf16" else torch.from_numpy(arrays[key])).to("cuda:0")
 
     gate = workloads.make_gate(wl, 0) if args.gate else None
-    z0 = image(gate["z"], gate["z_bf16"]) if gate is not None else None
+    z0 = image(gate, "z") if gate is not None else None
     g = workloads.make_output_grad(wl, 0) if args.backward else None
-    dy0 = image(g["dy"], g["dy_bf16"]) if g is not None else None
+    dy0 = image(g, "dy") if g is not None else None
     front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw) \
         if args.front else None
     fw = [torch.from_numpy(front_w[k]).to("cuda:0")
