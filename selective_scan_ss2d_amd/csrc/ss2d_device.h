@@ -112,11 +112,14 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// DPP quad_perm helpers (lanes exchange values inside groups of four).
+// DPP quad_perm helpers (lanes exchange values inside groups of four).  Every lane reads a
+// lane of its own quad, so no lane is out of bounds and the old value never shows through:
+// bound_ctrl lets the compiler drop the move that would initialise it (or fold the
+// permutation into the instruction that consumes it).
 template <int P0, int P1, int P2, int P3>
 __device__ __forceinline__ float quad_perm(float v) {
   constexpr int ctrl = P0 | (P1 << 2) | (P2 << 4) | (P3 << 6);
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, true));
 }
 
 // Value of `v` held by lane q of this lane's channel group (S lanes per channel).
