@@ -5,6 +5,7 @@ status codes can be checked on a machine without a GPU, using fake (never derefe
 pointers.
 """
 import ctypes
+import os
 import pathlib
 import re
 import subprocess
@@ -21,6 +22,11 @@ HEADER = ROOT / "include" / "ss2d.h"
 
 @pytest.fixture(scope="module")
 def lib():
+    # tests/test_sanitizers_cpu.py reruns this file against a build whose host code carries
+    # AddressSanitizer and UBSan, named by SS2D_TEST_LIBRARY
+    other = os.environ.get("SS2D_TEST_LIBRARY")
+    if other:
+        return bnd.load_library(other)
     if not bnd.LIBRARY_PATH.exists():
         from selective_scan_ss2d_amd import build
         build.build()

@@ -1,6 +1,7 @@
 """CPU tests of the oracle: its pins, planted mistakes that the pins must catch, thread
 determinism, and the stored golden output of the smallest workload."""
 import json
+import os
 import pathlib
 import shutil
 import subprocess
@@ -17,6 +18,11 @@ GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
 
 @pytest.fixture(scope="module")
 def orc():
+    # tests/test_sanitizers_cpu.py reruns the pins against an oracle built with
+    # AddressSanitizer and UBSan, named by SS2D_TEST_ORACLE_LIBRARY
+    other = os.environ.get("SS2D_TEST_ORACLE_LIBRARY")
+    if other:
+        return oracle.Oracle(other)
     oracle.build()
     return oracle.Oracle()
 
