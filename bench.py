@@ -318,6 +318,10 @@ def main() -> int:
     ap.add_argument("--front-lowrank", action="store_true",
                     help="with --front: dt_proj folded into the scan (ss2d_project_lr, then "
                          "ss2d_forward_routes_lr on its R dt rows)")
+    ap.add_argument("--plan", default="", metavar="SPLIT,CHUNK",
+                    help="launch-plan override of the forward scan for this run (lanes per "
+                         "channel, chunk length; 0,-1 is automatic), for comparing plans; "
+                         "the line then names the plan in its config")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 device-to-device copies of MIB "
                          "MiB (a plain copy kernel of known size, for scaling the HBM byte "
@@ -343,6 +347,13 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    plan = None
+    if args.plan:
+        plan = [int(v) for v in args.plan.split(",")]
+        if len(plan) != 2:
+            log("--plan takes SPLIT,CHUNK")
+            return 2
+        ss.launch_plan(*plan).__enter__()  # this thread, for the rest of the run
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -619,7 +630,8 @@ def main() -> int:
                    "pass": ("backward (per-route inputs from the front end)" if routes_bwd
                             else "backward" if args.backward else
                             "front(dt_proj in scan)+forward" if args.front_lowrank else
-                            "front+forward" if args.front else "forward")},
+                            "front+forward" if args.front else "forward"),
+                   **({"plan": {"split": plan[0], "chunk_len": plan[1]}} if plan else {})},
         "ms_per_step_median": round(ms_median, 5),
         "ms_per_step_min": round(ms_min, 5),
         "clock_settle_steps": settle,
