@@ -1,0 +1,103 @@
+"""CPU evidence for the backward's fp32 parity bar on dA_log (no GPU, no library).
+
+dA_log[k, d, n] = A_n sum_b sum_t (lambda h_{t-1} a_t delta_t + lambda B_t u_t dbb/dA) sums
+B * L terms of either sign per entry.  A plain fp32 version of the zero-order-hold operator's
+gated backward -- states, adjoint and terms rounded to fp32 at every operation, summed per
+32-step tile and then over tiles and images, as the kernel orders its sums -- is compared with
+the float64 oracle on the full-size bidirectional workload the GPU suite checks (128 images
+of 197 steps, gated, zero-order hold).  It stays within the backward bar 2e-4 and crosses 1e-4 on the entries whose terms
+cancel: the bar is the fp32 floor of the recurrences, not slack for the kernel.
+"""
+import numpy as np
+
+import oracle
+import workloads
+from tests.gpu_util import TOL_BWD, parity_error
+
+F32 = np.float32
+ARGS = ("x", "dt_raw", "A_log", "Bs", "Cs", "Ds", "dt_bias")
+
+
+def psi(v):
+    """(v e^v - (e^v - 1)) / v^2, the A-derivative factor of (e^v - 1) / A, in fp32: the
+    direct form for |v| >= 1/4 (its cancellation costs at most ~1e-6 relative there), its
+    power series sum_k v^k (k + 1) / (k + 2)! to v^5 below."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        direct = (v * np.exp(v) - np.expm1(v)) / (v * v)
+    series = F32(0.5) + v * (F32(1 / 3) + v * (F32(1 / 8) + v * (F32(1 / 30) + v * (
+        F32(1 / 144) + v * F32(1 / 840)))))
+    return np.where(np.abs(v) < F32(0.25), series, direct)
+
+
+def dA_log_fp32(inp, dy, z, chunk=128, tile=32):  # -> (tiled, sequential)
+    """dA_log (2, D, N) of sum(dy * y) for y = (y_0 + y_1 reversed) SiLU(z), zero-order hold,
+    every operation in fp32 (one rounding each, no fused multiply-add): the states forwards,
+    the adjoint backwards, each step's terms ((lambda h_{t-1}) a_t) delta_t and
+    ((lambda B_t) u_t) dbb/dA summed over tiles of `tile` steps, the tile sums over the
+    sequence and the images in order.  Arrays are laid out (step, image, channel, state);
+    what needs no recurrence is formed for all steps at once."""
+    x, dt_raw, A_log = inp["x"].astype(F32), inp["dt_raw"].astype(F32), inp["A_log"]
+    Bs, Cs, bias = inp["Bs"].astype(F32), inp["Cs"].astype(F32), inp["dt_bias"]
+    B, D, L = x.shape
+    zf = z.astype(F32)
+    g = dy.astype(F32) * (zf / (F32(1) + np.exp(-zf)))  # the gradient reaching every route
+    out = np.zeros((2, 2, D, A_log.shape[-1]), F32)
+    for k in range(2):
+        rev = (k == 1)
+        u = x[..., ::-1] if rev else x
+        gk = g[..., ::-1] if rev else g
+        Bt = np.ascontiguousarray(Bs[:, k].transpose(2, 0, 1))[:, :, None, :]   # (L, B, 1, N)
+        Ct = np.ascontiguousarray(Cs[:, k].transpose(2, 0, 1))[:, :, None, :]
+        for d0 in range(0, D, chunk):
+            sl = slice(d0, min(D, d0 + chunk))
+            A = -np.exp(A_log[k, sl].astype(F32))                               # (d, N)
+            zr = dt_raw[:, k, sl] + bias[k, sl][None, :, None]                   # (B, d, L)
+            dl = np.ascontiguousarray(np.logaddexp(F32(0), zr).astype(F32).transpose(2, 0, 1))
+            dl = dl[..., None]                                                   # (L, B, d, 1)
+            ut = np.ascontiguousarray(u[:, sl].transpose(2, 0, 1))[..., None]    # (L, B, d, 1)
+            gt = np.ascontiguousarray(gk[:, sl].transpose(2, 0, 1))[..., None]
+            v = dl * A                                                           # (L, B, d, N)
+            a = np.exp(v)
+            inc = (np.expm1(v) / A) * (ut * Bt)                                  # bb u_t B_t
+            h = np.empty((L + 1,) + v.shape[1:], F32)                            # h[t + 1]: after step t
+            h[0] = 0
+            for t in range(L):
+                h[t + 1] = a[t] * h[t] + inc[t]
+            del inc
+            dbb = (dl * dl) * psi(v)
+            del v
+            lam = np.zeros(h.shape[1:], F32)
+            acc = np.zeros(h.shape[1:], F32)   # tile sums added over the tiles
+            seq = np.zeros(h.shape[1:], F32)   # every term added in turn
+            for t0 in range(((L - 1) // tile) * tile, -1, -tile):
+                part = np.zeros(h.shape[1:], F32)
+                for t in range(min(L, t0 + tile) - 1, t0 - 1, -1):
+                    lam = gt[t] * Ct[t] + (a[t + 1] * lam if t + 1 < L else F32(0) * lam)
+                    t1 = ((lam * h[t]) * a[t]) * dl[t]
+                    t2 = ((lam * Bt[t]) * ut[t]) * dbb[t]
+                    part = (part + t1) + t2
+                    seq = (seq + t1) + t2
+                acc = acc + part
+            for i, s_ in enumerate((acc, seq)):
+                tot = np.zeros(s_.shape[1:], F32)
+                for b in range(B):
+                    tot = tot + s_[b]
+                out[i, k, sl] = A * tot
+    return out[0], out[1]
+
+
+def test_plain_fp32_backward_reaches_the_dA_log_bar():
+    wl = workloads.workload("vim_bidir_bf16")
+    inp = workloads.make_inputs(wl, seed=0, a_log="init")  # the GPU suite's full-size inputs
+    dy = workloads.make_output_grad(wl, 0)["dy"]
+    z = workloads.make_gate(wl, 0)["z"]
+    ref = oracle.Oracle().backward(2, *[inp[k] for k in ARGS], dy, z=z, zoh=True)["A_log"]
+    worst = 0.0
+    for name, got in zip(("tiled sums", "sequential sums"), dA_log_fp32(inp, dy, z)):
+        err = parity_error(got.astype(np.float64), ref)
+        print(f"plain fp32 dA_log, {name}: gate {err['gate']:.3e}, "
+              f"normwise {err['normwise']:.3e}")
+        assert err["gate"] <= TOL_BWD["f32"], (name, err)
+        worst = max(worst, err["gate"])
+    # a correct fp32 implementation does not meet 1e-4 on this gradient in every order
+    assert worst > 1e-4, worst
