@@ -10,7 +10,8 @@ JSON line on stdout (details go to stderr):
 
   value        state updates per second (B*K*D*L*N per step / seconds per step)
   roofline     the dominant kernel (the scan) against MI355X's 8 TB/s HBM peak, with the
-               fp32 and issue-slot fractions as diagnostics beside it
+               fp32 and issue-slot fractions as diagnostics beside it, the latter also
+               priced at the instruction rates the library's probe measures on the chip
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same workload
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
@@ -536,6 +537,14 @@ def main() -> int:
     log(f"step {ms_step * 1e3:.1f} us (median {ms_median * 1e3:.1f}, min {ms_min * 1e3:.1f}), "
         f"{upd_per_s:.4e} updates/s, algorithmic {gbps:.1f} GB/s")
     copy_gbps = copy_bandwidth_gbps(torch)
+    # The rates the issue-slot model assumes, measured on this chip: fused multiply-adds and
+    # v_exp_f32 alone, and one update's mix (4 multiply-adds + 1 exponential) at full occupancy.
+    rates = ss.probe_issue_rates()
+    exp_slots = rates["fma_per_s"] / rates["exp_per_s"]
+    mix_slots = rates["fma_per_s"] / rates["update_mix_per_s"]
+    log(f"issue rates: {rates['fma_per_s']:.4g} FMA/s, {rates['exp_per_s']:.4g} exp/s "
+        f"({exp_slots:.2f} FMA slots each), update mix {rates['update_mix_per_s']:.4g}/s "
+        f"({mix_slots:.2f} slots), clock {rates['clock_hz'] / 1e9:.2f} GHz")
     log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
 
     # Dominant kernel: the scan (with the chunked plan, both scan passes are counted).
@@ -554,6 +563,8 @@ def main() -> int:
     traffic = traffic if not (args.gate or args.zoh or args.backward or args.front) else None
     fp32_tflops = wl.updates * ALG_FLOPS_PER_UPDATE / scan_avg_s / 1e12
     issue_floor_s = wl.updates * slots / VALU_LANE_SLOTS
+    # the same floor priced at the measured multiply-add rate (the sustained clock's)
+    issue_floor_meas_s = wl.updates * slots / rates["fma_per_s"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
@@ -568,7 +579,22 @@ def main() -> int:
                 "fp32_frac": round(fp32_tflops / FP32_PEAK_TFLOPS, 4),
                 "issue_slots_per_update": slots,
                 "issue_floor_us": round(issue_floor_s * 1e6, 1),
-                "issue_floor_frac": round(issue_floor_s / scan_avg_s, 4)}
+                "issue_floor_frac": round(issue_floor_s / scan_avg_s, 4),
+                "issue_rates_measured": {
+                    "fma_per_s": float(f"{rates['fma_per_s']:.4g}"),
+                    "exp_per_s": float(f"{rates['exp_per_s']:.4g}"),
+                    "update_mix_per_s": float(f"{rates['update_mix_per_s']:.4g}"),
+                    "exp_fma_slots": round(exp_slots, 3),
+                    "update_mix_slots": round(mix_slots, 3),
+                    "clock_ghz": round(rates["clock_hz"] / 1e9, 3),
+                    "compute_units": rates["compute_units"]},
+                "issue_floor_us_measured": round(issue_floor_meas_s * 1e6, 1),
+                "issue_floor_frac_measured": round(issue_floor_meas_s / scan_avg_s, 4)}
+    if not (args.backward or args.zoh):
+        # the plain update is exactly the probe's mix: its measured rate is the scan's ceiling
+        mix_s = wl.updates / rates["update_mix_per_s"]
+        roofline["update_mix_floor_us_measured"] = round(mix_s * 1e6, 1)
+        roofline["update_mix_floor_frac_measured"] = round(mix_s / scan_avg_s, 4)
 
     roofline_front = None
     if args.front and not routes_bwd:

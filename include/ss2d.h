@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 8
+#define SS2D_ABI_VERSION 9
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -398,6 +398,23 @@ int ss2d_last_hip_error(void);
 #define SS2D_KERNEL_KINDS 9
 int ss2d_timing_enable(int enable);
 int ss2d_timing_read(double *ms, int64_t *launches);
+
+/* ---- issue-rate probe (measurement support, not part of the operator) ------------------
+ * Measures, on the current device and `stream`, the instruction rates that bound the scan
+ * kernel (whose state update issues 2 multiplies, 2 fused multiply-adds and one v_exp_f32
+ * per state and step): three probe kernels at full occupancy (8 waves per SIMD, 8
+ * independent chains per lane), after ~0.1 s of warm-up load, best of 3 runs each.  Writes
+ *   out[0]  fp32 fused multiply-adds per second (lane operations),
+ *   out[1]  v_exp_f32 per second (lane operations),
+ *   out[2]  groups of 4 fused multiply-adds and 1 v_exp_f32 per second (one update's mix:
+ *           a multiply issues like a fused multiply-add),
+ *   out[3]  the shader clock the chip sustained during the grouped probe (Hz), from the
+ *           shader and the 100 MHz reference counters,
+ *   out[4]  the device's compute units,
+ * to out[SS2D_PROBE_OUTPUTS] (caller-owned host memory).  Synchronises `stream`; takes
+ * ~0.2 s.  Returns SS2D_OK, SS2D_ERR_NULL, or SS2D_ERR_HIP. */
+#define SS2D_PROBE_OUTPUTS 5
+int ss2d_probe_issue_rates(double *out, void *stream);
 
 #ifdef __cplusplus
 }

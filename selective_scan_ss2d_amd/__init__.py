@@ -17,7 +17,7 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
                        ss1d_bidir_project_lr, ss2d_backward, ss2d_forward, ss2d_forward_ex,
                        ss2d_forward_routes, ss2d_forward_routes_lr, ss2d_project,
                        ss2d_project_lr, status_string, timing_enable, timing_read,
-                       launch_plan)
+                       launch_plan, probe_issue_rates)
 
 __all__ = [
     "ss2d_forward", "ss1d_bidir_forward", "ss2d_forward_ex", "ss1d_bidir_forward_ex",
@@ -30,4 +30,5 @@ __all__ = [
     "SS2DError", "LIBRARY_PATH", "SIGNATURES", "SS2D_OK", "SS2D_ERR_NULL", "SS2D_ERR_SHAPE",
     "SS2D_ERR_UNSUPPORTED", "SS2D_ERR_ALIGN", "SS2D_ERR_HIP", "SS2D_ERR_ALIAS", "SS2D_F32",
     "SS2D_BF16", "KERNEL_KINDS", "timing_enable", "timing_read", "launch_plan",
+    "probe_issue_rates",
 ]

@@ -57,6 +57,7 @@ SIGNATURES = {
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
     "ss2d_set_launch_plan": (ctypes.c_int, [ctypes.c_int, _I64]),
+    "ss2d_probe_issue_rates": (ctypes.c_int, [_P, _P]),
     "ss2d_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "ss2d_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64)]),
@@ -568,6 +569,19 @@ class launch_plan:
 
     def __exit__(self, *exc):
         load_library().ss2d_set_launch_plan(0, -1)
+
+
+def probe_issue_rates(stream=None) -> dict:
+    """Measured instruction rates that bound the scan (ss2d_probe_issue_rates): fused
+    multiply-adds and v_exp_f32 per second (lane operations), groups of 4 fused multiply-adds
+    and 1 v_exp_f32 per second (one state update's mix), the sustained shader clock (Hz) and
+    the compute units.  Runs on the current device; synchronises the stream."""
+    import torch
+    out = (ctypes.c_double * 5)()
+    st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(load_library().ss2d_probe_issue_rates(out, ctypes.c_void_p(st)))
+    return {"fma_per_s": out[0], "exp_per_s": out[1], "update_mix_per_s": out[2],
+            "clock_hz": out[3], "compute_units": int(out[4])}
 
 
 def timing_enable(enable: bool = True) -> bool:

@@ -1,8 +1,9 @@
 // C ABI of the SS2D forward library: argument validation, the launch plan, stream-ordered
-// scratch, and the kernel sequence (transpose -> scan [-> carry -> scan] -> merge).
+// scratch, and the kernel sequence (transpose -> [chunk aggregates ->] scan -> merge).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -927,6 +928,77 @@ int ss2d_set_launch_plan(int split, int64_t chunk_len) {
 }
 
 int ss2d_last_hip_error(void) { return g_last_hip_error; }
+
+int ss2d_probe_issue_rates(double* out, void* stream) {
+  if (!out) return SS2D_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0, cus = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e);
+  // 8 blocks of 4 waves per CU: 8 waves per SIMD, far more than needed to keep it issuing
+  const int blocks = 8 * cus, block = ss2d::probe_block();
+  const size_t sink_bytes = align256(size_t(blocks) * block * sizeof(float));
+  const size_t clock_bytes = size_t(blocks) * 4 * sizeof(unsigned long long);
+  char* ws = nullptr;
+  int rc = scratch_alloc(&ws, sink_bytes + clock_bytes, st);
+  if (rc != SS2D_OK) return rc;
+  float* sink = reinterpret_cast<float*>(ws);
+  auto* clocks = reinterpret_cast<unsigned long long*>(ws + sink_bytes);
+  std::vector<unsigned long long> host(size_t(blocks) * 4);
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  const int iters = 2048;  // a few milliseconds per launch
+  double rate[3] = {0.0, 0.0, 0.0}, hz = 0.0;
+  // warm-up: ~0.1 s of the fused multiply-add probe brings the clock to its loaded rate
+  for (int i = 0; i < 40 && e == hipSuccess; ++i)
+    e = static_cast<hipError_t>(ss2d::launch_probe(0, blocks, iters, sink, clocks, st));
+  for (int rep = 0; rep < 3 && e == hipSuccess; ++rep) {
+    for (int kind = 0; kind < 3 && e == hipSuccess; ++kind) {
+      e = hipEventRecord(ev[0], st);
+      if (e == hipSuccess)
+        e = static_cast<hipError_t>(ss2d::launch_probe(kind, blocks, iters, sink, clocks, st));
+      if (e == hipSuccess) e = hipEventRecord(ev[1], st);
+      if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+      float ms = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+      if (e != hipSuccess || ms <= 0.0f) break;
+      int fmas = 0, exps = 0;
+      ss2d::probe_counts(kind, &fmas, &exps);
+      const double per_lane = double(iters) * (kind == 0 ? fmas : kind == 1 ? exps : exps);
+      const double r = double(blocks) * block * per_lane / (double(ms) * 1e-3);
+      if (r > rate[kind]) rate[kind] = r;
+      if (kind == 2 && e == hipSuccess) {  // the sustained clock, from the last launch
+        e = hipMemcpyAsync(host.data(), clocks, clock_bytes, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e == hipSuccess) {
+          std::vector<double> f;
+          for (int b = 0; b < blocks; ++b) {
+            const double cyc = double(host[4 * b + 1] - host[4 * b + 0]);
+            const double ref = double(host[4 * b + 3] - host[4 * b + 2]);
+            if (ref > 0) f.push_back(cyc / ref * 1e8);  // the reference counter runs at 100 MHz
+          }
+          if (!f.empty()) {
+            std::nth_element(f.begin(), f.begin() + f.size() / 2, f.end());
+            hz = f[f.size() / 2];
+          }
+        }
+      }
+    }
+  }
+  for (hipEvent_t x : ev)
+    if (x) (void)hipEventDestroy(x);
+  const hipError_t fe = hipFreeAsync(ws, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (fe != hipSuccess) return hip_fail(fe);
+  out[0] = rate[0];   // fused multiply-adds per second (lane operations)
+  out[1] = rate[1];   // v_exp_f32 per second (lane operations)
+  out[2] = rate[2];   // groups of 4 fused multiply-adds + 1 v_exp_f32 per second
+  out[3] = hz;        // shader clock during the grouped probe (Hz)
+  out[4] = cus;       // compute units
+  return SS2D_OK;
+}
 
 int ss2d_timing_enable(int enable) {
   const int prev = g_timing.enabled ? 1 : 0;

@@ -274,6 +274,14 @@ int launch_merge4_gate_bwd(const float* y_route, const void* z, const void* dy, 
                            void* dz, int B, int D, int H, int W, int dtype, hipStream_t st);
 int launch_merge2_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
                            void* dz, int B, int D, int L, int dtype, hipStream_t st);
+// Issue-rate probes: kind 0 (fp32 fused multiply-adds), 1 (v_exp_f32), 2 (groups of 4 fused
+// multiply-adds and 1 v_exp_f32); `blocks` blocks of probe_block() threads, `iters` loop
+// iterations of probe_counts() instructions per lane; sink takes blocks * probe_block()
+// floats, clocks 4 per block (shader and reference counters at the start and end).
+void probe_counts(int kind, int* fmas, int* exps);
+int probe_block();
+int launch_probe(int kind, int blocks, int iters, float* sink, unsigned long long* clocks,
+                 hipStream_t st);
 // Bytes of the prepared weight images of one call (K * ceil(D / 64) images).
 size_t project_prep_bytes(int K, int D, int N, int R, int dtype);
 // Fills a.wprep (which must hold project_prep_bytes) from the weights, then runs the front
