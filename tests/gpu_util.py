@@ -84,14 +84,14 @@ def assert_parity(y, ref, dtype: str, what: str, tol: dict = TOL) -> dict:
     return e
 
 
-class env_override:
-    """Force the library's launch plan for calls from this thread inside the block:
-    SS2D_SPLIT (lanes per channel) and SS2D_CHUNK_LEN (0: one pass) as keyword arguments,
-    set through ss2d_set_launch_plan (the library reads no environment variable)."""
+class plan_override:
+    """Force the library's launch plan for calls from this thread inside the block: split
+    (lanes per channel; 0 automatic) and chunk_len (0: one pass; -1 automatic), set through
+    ss2d_set_launch_plan."""
 
-    def __init__(self, SS2D_SPLIT=0, SS2D_CHUNK_LEN=-1):
+    def __init__(self, split=0, chunk_len=-1):
         import selective_scan_ss2d_amd as ss
-        self.ctx = ss.launch_plan(int(SS2D_SPLIT), int(SS2D_CHUNK_LEN))
+        self.ctx = ss.launch_plan(int(split), int(chunk_len))
 
     def __enter__(self):
         return self.ctx.__enter__()

@@ -2,11 +2,12 @@
 
 dA_log[k, d, n] = A_n sum_b sum_t (lambda h_{t-1} a_t delta_t + lambda B_t u_t dbb/dA) sums
 B * L terms of either sign per entry.  A plain fp32 version of the zero-order-hold operator's
-gated backward -- states, adjoint and terms rounded to fp32 at every operation, summed per
-32-step tile and then over tiles and images, as the kernel orders its sums -- is compared with
-the float64 oracle on the full-size bidirectional workload the GPU suite checks (128 images
-of 197 steps, gated, zero-order hold).  It stays within the backward bar 2e-4 and crosses 1e-4 on the entries whose terms
-cancel: the bar is the fp32 floor of the recurrences, not slack for the kernel.
+gated backward (states, adjoint and terms rounded to fp32 at every operation) is compared
+with the float64 oracle on the full-size bidirectional workload the GPU suite checks (128
+images of 197 steps, gated, zero-order hold), its terms summed in two orders: per 32-step
+tile, then over tiles (the kernel's order), and one after another.  Both stay within the
+backward bar 2e-4; the second crosses 1e-4 on the entries whose terms cancel: the bar is
+the fp32 floor of the recurrences, not slack for the kernel.
 """
 import numpy as np
 
@@ -59,7 +60,7 @@ def dA_log_fp32(inp, dy, z, chunk=128, tile=32):  # -> (tiled, sequential)
             v = dl * A                                                           # (L, B, d, N)
             a = np.exp(v)
             inc = (np.expm1(v) / A) * (ut * Bt)                                  # bb u_t B_t
-            h = np.empty((L + 1,) + v.shape[1:], F32)                            # h[t + 1]: after step t
+            h = np.empty((L + 1,) + v.shape[1:], F32)  # h[t + 1]: the state after step t
             h[0] = 0
             for t in range(L):
                 h[t + 1] = a[t] * h[t] + inc[t]

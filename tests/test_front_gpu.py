@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import (TOL_DT_RAW, TOL_FRONT, assert_parity, env_override, log, to_device,
+from tests.gpu_util import (TOL_DT_RAW, TOL_FRONT, assert_parity, plan_override, log, to_device,
                             to_numpy_f64)
 
 pytestmark = pytest.mark.gpu
@@ -137,7 +137,7 @@ def check_routes(orc, wl, gate, zoh, seed=0, **overrides):
                              z=g["z"] if gate else None, zoh=zoh)
     dev = to_device(inp, wl)
     z = _dev(g["z"], wl.dtype) if gate else None
-    with env_override(**overrides):
+    with plan_override(**overrides):
         y = run_routes(route_inputs_to_device(ri, wl), dev, wl, z=z, zoh=zoh)
     torch.cuda.synchronize()
     assert_parity(to_numpy_f64(y), ref.reshape(y.shape), wl.dtype, what)
@@ -161,9 +161,9 @@ def test_routes_small(orc, case, gate, zoh):
     check_routes(orc, workloads.custom(B, D, H, W, N, K, dt), gate, zoh, seed=32)
 
 
-@pytest.mark.parametrize("var", [dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
-                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96),
-                                 dict(SS2D_SPLIT=2, SS2D_CHUNK_LEN=0)],
+@pytest.mark.parametrize("var", [dict(split=1, chunk_len=64),
+                                 dict(split=4, chunk_len=96),
+                                 dict(split=2, chunk_len=0)],
                          ids=["S1_C64", "S4_C96", "S2_C0"])
 def test_routes_launch_variants(orc, var):
     """Chunked passes (chunk states and carries) and the lane splits on per-route inputs."""
@@ -284,7 +284,7 @@ def check_routes_lr(orc, wl, R, gate, zoh, seed=0, **overrides):
     dev = to_device(inp, wl)
     z = _dev(g["z"], wl.dtype) if gate else None
     dtw = torch.from_numpy(lr["dt_w"]).to("cuda:0")
-    with env_override(**overrides):
+    with plan_override(**overrides):
         y = run_routes_lr(route_inputs_to_device(ri, wl), _dev(lr["dt_lr"], wl.dtype), dtw,
                           dev, wl, z=z, zoh=zoh)
     torch.cuda.synchronize()
@@ -311,9 +311,9 @@ def test_routes_lr_small(orc, case, gate, zoh):
     check_routes_lr(orc, workloads.custom(B, D, H, W, N, K, dt), R, gate, zoh, seed=37)
 
 
-@pytest.mark.parametrize("var", [dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
-                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96),
-                                 dict(SS2D_SPLIT=2, SS2D_CHUNK_LEN=0)],
+@pytest.mark.parametrize("var", [dict(split=1, chunk_len=64),
+                                 dict(split=4, chunk_len=96),
+                                 dict(split=2, chunk_len=0)],
                          ids=["S1_C64", "S4_C96", "S2_C0"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_routes_lr_launch_variants(orc, var, dt):

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import assert_parity, env_override, log, to_device, to_numpy_f64
+from tests.gpu_util import assert_parity, plan_override, log, to_device, to_numpy_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def check(orc, wl, gate, zoh, a_log="random", seed=0, inp=None, what=None, **ove
     ref = orc.forward(wl.K, *[inp[k] for k in ARGS], z=g["z"] if gate else None, zoh=zoh)
     dev = to_device(inp, wl)
     z = gate_to_device(g, wl) if gate else None
-    with env_override(**overrides):
+    with plan_override(**overrides):
         y = run_ex(dev, wl, z, zoh)
     torch.cuda.synchronize()
     return assert_parity(to_numpy_f64(y), ref, wl.dtype, what)
@@ -67,13 +67,13 @@ def test_options_small(orc, case, gate, zoh):
     check(orc, workloads.custom(B, D, H, W, N, K, dt), gate, zoh, seed=21)
 
 
-VARIANTS = [dict(SS2D_SPLIT=s, SS2D_CHUNK_LEN=0) for s in (1, 2, 4)] + [
-    dict(SS2D_SPLIT=sp, SS2D_CHUNK_LEN=c) for sp in (1, 4) for c in (64, 96)]
+VARIANTS = [dict(split=s, chunk_len=0) for s in (1, 2, 4)] + [
+    dict(split=sp, chunk_len=c) for sp in (1, 4) for c in (64, 96)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "S{}_C{}".format(
-    v["SS2D_SPLIT"], v["SS2D_CHUNK_LEN"]))
+    v["split"], v["chunk_len"]))
 def test_zoh_launch_variants(orc, dt, var):
     check(orc, workloads.custom(2, 72, 13, 11, 16, 4, dt), True, True, seed=22, **var)
 

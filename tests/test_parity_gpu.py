@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import (TOL, assert_parity, env_override, log, parity_error, run_gpu,
+from tests.gpu_util import (TOL, assert_parity, plan_override, log, parity_error, run_gpu,
                             to_device, to_numpy_f64)
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def check_case(orc, wl, a_log="init", seed=0, what=None, **overrides):
     ref = oracle_full(orc, inp, wl)
     dev = to_device(inp, wl)
     import torch
-    with env_override(**overrides):
+    with plan_override(**overrides):
         y = run_gpu(dev, wl)
     torch.cuda.synchronize()
     return assert_parity(to_numpy_f64(y), ref, wl.dtype, what)
@@ -70,13 +70,13 @@ def test_small_shapes(orc, case):
 
 
 # ---- every launch variant: lanes per channel and chunked scans ----------------------
-VARIANTS = [dict(SS2D_SPLIT=s, SS2D_CHUNK_LEN=0) for s in (1, 2, 4)] + [
-    dict(SS2D_SPLIT=sp, SS2D_CHUNK_LEN=c) for sp in (1, 4) for c in (32, 64, 96, 160)]
+VARIANTS = [dict(split=s, chunk_len=0) for s in (1, 2, 4)] + [
+    dict(split=sp, chunk_len=c) for sp in (1, 4) for c in (32, 64, 96, 160)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "S{}_C{}".format(
-    v["SS2D_SPLIT"], v["SS2D_CHUNK_LEN"]))
+    v["split"], v["chunk_len"]))
 def test_launch_variants(orc, dt, var):
     wl = workloads.custom(2, 130, 24, 24, 16, 4, dt)  # L = 576: vector loads, 3 waves/(b,k)
     check_case(orc, wl, a_log="random", seed=11, **var)
@@ -93,10 +93,10 @@ def test_bidir_small(orc, case):
     check_case(orc, workloads.custom(B, D, 1, L, N, 2, dt), a_log="random", seed=3)
 
 
-@pytest.mark.parametrize("var", [dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=0),
-                                 dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=0),
-                                 dict(SS2D_SPLIT=1, SS2D_CHUNK_LEN=64),
-                                 dict(SS2D_SPLIT=4, SS2D_CHUNK_LEN=96)],
+@pytest.mark.parametrize("var", [dict(split=4, chunk_len=0),
+                                 dict(split=1, chunk_len=0),
+                                 dict(split=1, chunk_len=64),
+                                 dict(split=4, chunk_len=96)],
                          ids=["S4", "S1", "S1_chunk64", "S4_chunk96"])
 def test_bidir_variants(orc, var):
     check_case(orc, workloads.custom(2, 96, 1, 300, 16, 2, "bf16"), a_log="random", seed=5,

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.gpu_util import env_override, log
+from tests.gpu_util import plan_override, log
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def test_chunked_forward_bf16_is_rounded_fp32():
     wl = workloads.custom(2, 72, 13, 11, 16, 4, "bf16")
     log("case forward rounding, chunked plan")
     bf, f32 = _pair(wl, 52)
-    with env_override(SS2D_SPLIT=4, SS2D_CHUNK_LEN=64):
+    with plan_override(split=4, chunk_len=64):
         y_bf = ss.ss2d_forward(*[bf[k] for k in ARGS])
         y_32 = ss.ss2d_forward(*[f32[k] for k in ARGS])
     torch.cuda.synchronize()
