@@ -313,6 +313,30 @@ __global__ __launch_bounds__(256) void k_project_prep(ProjArgs a) {
   }
 }
 
+// The block's image b, route k and first step t0.  The grid is (tiles, K, B); blocks are
+// taken in an order that keeps a block's halo (the KW - 1 steps before its tile, in the
+// previous tile's cache lines) in the L2 of its XCD: each XCD runs a contiguous range of
+// (image, route pair) groups, tile after tile (the pair's two routes in turn at each tile),
+// so the block of the previous tile has just fetched those lines there.  In launch order
+// the tiles of a row go round the 8 XCDs and every halo is a miss.  (Mirroring the odd
+// route's tiles as well, so that both routes of a pair read the same rows together, halves
+// the rows fetched from memory but was measured slower.)
+struct ProjBlock {
+  int b, k, t0;
+};
+__device__ __forceinline__ ProjBlock proj_block() {
+  const unsigned T = gridDim.x, K = gridDim.y;
+  const unsigned lin = blockIdx.x + T * (blockIdx.y + K * blockIdx.z);
+  unsigned q = xcd_local_order(lin, T * K * gridDim.z);
+  const unsigned r = q % 2;  // route within the pair
+  q /= 2;
+  const unsigned tile = q % T;
+  q /= T;
+  const unsigned pair = q % (K / 2);
+  return {static_cast<int>(q / (K / 2)), static_cast<int>(2 * pair + r),
+          static_cast<int>(tile) * kTT};
+}
+
 // Everything a chunk of 64 channels loads into registers.
 struct ProjStage {
   float v[16];       // the wave's 16 input rows at this lane's step
@@ -333,7 +357,8 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
   // wave is uniform across a wave: saying so keeps row addresses in scalar registers
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int k = blockIdx.y, b = blockIdx.z;
+  const ProjBlock blk = proj_block();
+  const int k = blk.k, b = blk.b;
   const int L = a.L, D = a.D, N = a.N, R = a.R;
   const int KW = KWC > 0 ? KWC : a.KW;
   const int M = R + 2 * N;
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(256) void k_project(ProjArgs a) {
   const int img_bytes = a.img_bytes;
   float (*sXd)[kTT] = reinterpret_cast<float (*)[kTT]>(smem);
 
-  const int t0 = blockIdx.x * kTT;
+  const int t0 = blk.t0;
   const int t = t0 + lane;
   const bool col = (a.K == 4) && (k >= 2);
   const bool rev = (k & 1) != 0;
@@ -544,7 +569,8 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int k = blockIdx.y, b = blockIdx.z;
+  const ProjBlock blk = proj_block();
+  const int k = blk.k, b = blk.b;
   const int L = a.L, D = a.D, N = a.N, R = a.R;
   const int M = R + 2 * N;
   constexpr int MT = MTC;
@@ -556,7 +582,7 @@ __global__ __launch_bounds__(256) void k_project4(ProjArgs a) {
   const int img_bytes = a.img_bytes;
   float (*sXd)[kTT] = reinterpret_cast<float (*)[kTT]>(smem);
 
-  const int t0 = blockIdx.x * kTT;
+  const int t0 = blk.t0;
   const bool col = (a.K == 4) && (k >= 2);
   const bool rev = (k & 1) != 0;
   const T* xplanes = static_cast<const T*>(col ? a.x_col : a.x_row) + int64_t(b) * D * L;
