@@ -2,7 +2,9 @@
 """Benchmark of the SS2D forward operator on one MI355X.
 
 A step is one full forward call (transpose, scan, merge: every kernel of the operator) on
-one batch of seeded synthetic input already resident in HBM.  W untimed warm-up steps (then,
+one batch of seeded synthetic input already resident in HBM (with --backward, one backward
+call; with --train, a training step: the forward that keeps the scan's tile states, then the
+backward from them).  W untimed warm-up steps (then,
 if the GPU has been under load for less than --settle-ms, more untimed steps until it has:
 the clock ramps up over the first ~20 ms of load), then K timed steps between device
 synchronisations, timed with HIP events on the stream the library launches on.  Prints ONE
@@ -308,6 +310,10 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time the backward entry point (gradients of sum(dy * y); with "
                          "--gate and/or --zoh, of that operator's output, z included)")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step of the operator: ss2d_forward_save (y, and the "
+                         "scan's tile states kept) then ss2d_backward_saved from those states "
+                         "(with --gate and/or --zoh, of that operator)")
     ap.add_argument("--front", action="store_true",
                     help="per-route front end: time ss2d_project (causal conv + SiLU, x_proj, "
                          "dt_proj) followed by ss2d_forward_routes on its outputs; with "
@@ -372,6 +378,10 @@ def main() -> int:
     if args.backward and args.front_lowrank:
         log("no backward for the operator with dt_proj folded in")
         return 2
+    if args.train and (args.backward or args.front):
+        log("--train times the forward and the backward together: without --backward "
+            "or --front")
+        return 2
     if args.front_lowrank and not args.front:
         log("--front-lowrank needs --front")
         return 2
@@ -389,6 +399,9 @@ def main() -> int:
     proj_bytes += e * BKL * R if args.front_lowrank else e * BKL * wl.D + 4 * wl.K * wl.D * R
     if args.backward:
         alg_bytes = backward_bytes(wl, args.gate, routes_bwd)
+    elif args.train:  # the forward's bytes and the backward's (the kept state is scratch)
+        alg_bytes = (wl.algorithmic_bytes() + (e * wl.B * wl.D * wl.L if args.gate else 0)
+                     + backward_bytes(wl, args.gate, False))
     else:
         alg_bytes = wl.algorithmic_bytes() + (e * wl.B * wl.D * wl.L if args.gate else 0)
         if args.front:  # the scan then reads u (B, K, D, L), not x (B, D, L)
@@ -397,7 +410,9 @@ def main() -> int:
             alg_bytes += e * BKL * R + 4 * wl.K * wl.D * R - e * BKL * wl.D
     # the kernel the roofline line describes moves the step's algorithmic bytes: its own
     # share when the front end runs before it (its inputs u, dt_raw, Bs, Cs; y)
-    kernel_bytes = alg_bytes - proj_bytes if (args.front and not routes_bwd) else alg_bytes
+    kernel_bytes = (alg_bytes - proj_bytes if (args.front and not routes_bwd)
+                    else backward_bytes(wl, args.gate, False) if args.train else alg_bytes)
+    bwd_kernel = args.backward or args.train  # the adjoint scan is the dominant kernel
     rotate = args.rotate or (3 if alg_bytes < 512e6 else 1)
 
     def upload(arrays):
@@ -420,7 +435,7 @@ def main() -> int:
 
     gate = workloads.make_gate(wl, 0) if args.gate else None
     z0 = image(gate, "z") if gate is not None else None
-    g = workloads.make_output_grad(wl, 0) if args.backward else None
+    g = workloads.make_output_grad(wl, 0) if (args.backward or args.train) else None
     dy0 = image(g, "dy") if g is not None else None
     front_w = workloads.make_front_weights(wl, 0, R=args.front_r, KW=args.front_kw) \
         if args.front else None
@@ -429,6 +444,18 @@ def main() -> int:
     hw = (wl.H, wl.W) if wl.K == 4 else ()
 
     def make_call(dev, z, dy, y):
+        if args.train:
+            fs = ss.ss2d_forward_save if wl.K == 4 else ss.ss1d_bidir_forward_save
+            bs = ss.ss2d_backward_saved if wl.K == 4 else ss.ss1d_bidir_backward_saved
+            saved = torch.empty(ss.saved_state_bytes(wl.K, wl.B, wl.D, wl.L, wl.N,
+                                                     z is not None) // 4,
+                                dtype=torch.float32, device="cuda:0")
+            a = [dev[k] for k in ARGS]
+
+            def call():
+                fs(*a, z=z, zoh=args.zoh, y=y, saved=saved)
+                return bs(*a, dy, saved, z=z, zoh=args.zoh)
+            return call
         if args.front and args.front_lowrank:
             proj = ss.ss2d_project_lr if wl.K == 4 else ss.ss1d_bidir_project_lr
             fwd = ss.ss2d_forward_routes_lr if wl.K == 4 else ss.ss1d_bidir_forward_routes_lr
@@ -548,19 +575,19 @@ def main() -> int:
     log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
 
     # Dominant kernel: the scan (with the chunked plan, both scan passes are counted).
-    if args.backward:
+    if bwd_kernel:
         scan_ms, scan_n = kernels["scan_bwd"]
         agg_ms = 0.0
     else:
         scan_ms, scan_n = kernels["scan"]
         agg_ms, _ = kernels["chunk_agg"]
     scan_avg_s = (scan_ms + agg_ms) / max(scan_n, 1) / 1e3
-    slots = (ZOH_BWD_ISSUE_SLOTS_PER_UPDATE if args.backward and args.zoh
-             else BWD_ISSUE_SLOTS_PER_UPDATE if args.backward
+    slots = (ZOH_BWD_ISSUE_SLOTS_PER_UPDATE if bwd_kernel and args.zoh
+             else BWD_ISSUE_SLOTS_PER_UPDATE if bwd_kernel
              else ZOH_ISSUE_SLOTS_PER_UPDATE if args.zoh else ISSUE_SLOTS_PER_UPDATE)
     achieved = kernel_bytes / scan_avg_s / 1e9
     traffic = measured_traffic(wl.name)
-    traffic = traffic if not (args.gate or args.zoh or args.backward or args.front) else None
+    traffic = traffic if not (args.gate or args.zoh or bwd_kernel or args.front) else None
     fp32_tflops = wl.updates * ALG_FLOPS_PER_UPDATE / scan_avg_s / 1e12
     issue_floor_s = wl.updates * slots / VALU_LANE_SLOTS
     # the same floor priced at the measured multiply-add rate (the sustained clock's)
@@ -568,7 +595,7 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "k_scan_bwd" if args.backward else "k_scan",
+                "kernel": "k_scan_bwd" if bwd_kernel else "k_scan",
                 "kernel_avg_us": round(scan_avg_s * 1e6, 1),
                 "kernel_launches_timed": int(scan_n),
                 "algorithmic_bytes_per_launch": int(kernel_bytes),
@@ -590,7 +617,7 @@ def main() -> int:
                     "compute_units": rates["compute_units"]},
                 "issue_floor_us_measured": round(issue_floor_meas_s * 1e6, 1),
                 "issue_floor_frac_measured": round(issue_floor_meas_s / scan_avg_s, 4)}
-    if not (args.backward or args.zoh):
+    if not (bwd_kernel or args.zoh):
         # the plain update is exactly the probe's mix: its measured rate is the scan's ceiling
         mix_s = wl.updates / rates["update_mix_per_s"]
         roofline["update_mix_floor_us_measured"] = round(mix_s * 1e6, 1)
@@ -624,7 +651,7 @@ def main() -> int:
             cpu = cpu_baseline_front(wl, inp, front_w, args.cpu_seconds,
                                      z=gate["z"] if gate else None, zoh=args.zoh,
                                      lowrank=args.front_lowrank)
-        elif args.backward:
+        elif bwd_kernel:  # the oracle's backward runs its own forward recurrence first
             cpu = cpu_baseline_backward(wl, inp, g["dy"], args.cpu_seconds,
                                         z=gate["z"] if gate else None, zoh=args.zoh)
         else:
@@ -655,6 +682,8 @@ def main() -> int:
                    "zoh": bool(args.zoh),
                    "pass": ("backward (per-route inputs from the front end)" if routes_bwd
                             else "backward" if args.backward else
+                            "training step (forward keeping the tile states, backward "
+                            "from them)" if args.train else
                             "front(dt_proj in scan)+forward" if args.front_lowrank else
                             "front+forward" if args.front else "forward"),
                    **({"plan": {"split": plan[0], "chunk_len": plan[1]}} if plan else {})},

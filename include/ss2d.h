@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 9
+#define SS2D_ABI_VERSION 10
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -238,6 +238,59 @@ int ss1d_bidir_backward_ex(const void *x, const void *dt_raw, const float *A_log
                            void *ddt_raw, float *dA_log, void *dBs, void *dCs, float *dDs,
                            float *ddt_bias, void *dz, int64_t B, int64_t D, int64_t L,
                            int64_t N, int dtype, int flags, void *stream);
+
+/* ---- training: a forward that keeps the backward's checkpoints ---------------------------
+ * In training the forward and the backward run on the same inputs.  The backward restarts
+ * every 32-step tile of the scan from the state before it, which ss2d_backward_ex obtains by
+ * running the forward scan once more (the Vim summary, section 4.4: states are recomputed,
+ * not kept in HBM per step); ss2d_forward_save keeps those tile states while it computes y,
+ * and ss2d_backward_saved starts from them, so that the pair does the scan's forward work
+ * once.
+ *
+ * saved: caller-owned device memory of ss2d_saved_state_bytes(K, B, D, L, N, gated) bytes
+ * (K = 4 with L = H * W for the image operators, K = 2 for the bidirectional one; gated:
+ * whether z is given), 16-byte aligned.  Layout: the state before every 32-step tile,
+ * (B, K, D, ceil(L / 32), N) fp32 (the first tile's, zero, is not written), then with the
+ * gate the ungated route sum ((y_0 + y_1) + y_2) + y_3, (B, D, L) fp32, from which the
+ * gate's backward forms g and dz.  ss2d_saved_state_bytes returns -1 for sizes the
+ * operator rejects and for N not a multiple of 4.
+ *
+ * ss2d_forward_save: y as ss2d_forward_ex with the same arguments (bit for bit when that
+ * call runs in one pass, i.e. without the chunked plan it takes for batches too small to
+ * fill the chip; the training forward always runs one pass), and `saved` filled.
+ * ss2d_backward_saved: every gradient as ss2d_backward_ex, bit for bit, reading `saved`
+ * instead of recomputing it.  The backward's inputs, z, flags and shapes must be those of
+ * the forward that filled `saved`, and `saved` unchanged since; the library cannot check
+ * this (the state lives on the device), and other contents give undefined gradients.
+ * `saved` overlaps no other argument.  N must be a multiple of 4 (SS2D_ERR_UNSUPPORTED
+ * otherwise); everything else is as in ss2d_forward_ex and ss2d_backward_ex. */
+int64_t ss2d_saved_state_bytes(int K, int64_t B, int64_t D, int64_t L, int64_t N, int gated);
+
+int ss2d_forward_save(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                      const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                      void *y, float *saved, int64_t B, int64_t D, int64_t H, int64_t W,
+                      int64_t N, int dtype, int flags, void *stream);
+
+int ss1d_bidir_forward_save(const void *x, const void *dt_raw, const float *A_log,
+                            const void *Bs, const void *Cs, const float *Ds,
+                            const float *dt_bias, const void *z, void *y, float *saved,
+                            int64_t B, int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                            void *stream);
+
+int ss2d_backward_saved(const void *x, const void *dt_raw, const float *A_log, const void *Bs,
+                        const void *Cs, const float *Ds, const float *dt_bias, const void *z,
+                        const float *saved, const void *dy, void *dx, void *ddt_raw,
+                        float *dA_log, void *dBs, void *dCs, float *dDs, float *ddt_bias,
+                        void *dz, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                        int dtype, int flags, void *stream);
+
+int ss1d_bidir_backward_saved(const void *x, const void *dt_raw, const float *A_log,
+                              const void *Bs, const void *Cs, const float *Ds,
+                              const float *dt_bias, const void *z, const float *saved,
+                              const void *dy, void *dx, void *ddt_raw, float *dA_log, void *dBs,
+                              void *dCs, float *dDs, float *ddt_bias, void *dz, int64_t B,
+                              int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                              void *stream);
 
 /* ---- backward of the operator over per-route inputs ---------------------------------------
  * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output

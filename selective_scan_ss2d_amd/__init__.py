@@ -1,5 +1,5 @@
-"""SS2D operator (VMamba 2D selective scan) for MI355X / gfx950: forward, backward, and the
-per-route front end (causal conv + SiLU, x_proj, dt_proj), also with dt_proj folded into
+"""SS2D operator (VMamba 2D selective scan) for MI355X / gfx950: forward, backward (also
+starting from the state a training forward kept), and the per-route front end (causal conv + SiLU, x_proj, dt_proj), also with dt_proj folded into
 the scan.
 
 The operator runs in hand-written HIP kernels behind the C ABI of ``libss2d.so``
@@ -17,7 +17,9 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
                        ss1d_bidir_project_lr, ss2d_backward, ss2d_forward, ss2d_forward_ex,
                        ss2d_forward_routes, ss2d_forward_routes_lr, ss2d_project,
                        ss2d_project_lr, status_string, timing_enable, timing_read,
-                       launch_plan, probe_issue_rates)
+                       launch_plan, probe_issue_rates, saved_state_bytes,
+                       ss2d_forward_save, ss1d_bidir_forward_save, ss2d_backward_saved,
+                       ss1d_bidir_backward_saved)
 
 __all__ = [
     "ss2d_forward", "ss1d_bidir_forward", "ss2d_forward_ex", "ss1d_bidir_forward_ex",
@@ -30,5 +32,6 @@ __all__ = [
     "SS2DError", "LIBRARY_PATH", "SIGNATURES", "SS2D_OK", "SS2D_ERR_NULL", "SS2D_ERR_SHAPE",
     "SS2D_ERR_UNSUPPORTED", "SS2D_ERR_ALIGN", "SS2D_ERR_HIP", "SS2D_ERR_ALIAS", "SS2D_F32",
     "SS2D_BF16", "KERNEL_KINDS", "timing_enable", "timing_read", "launch_plan",
-    "probe_issue_rates",
+    "probe_issue_rates", "saved_state_bytes", "ss2d_forward_save", "ss1d_bidir_forward_save",
+    "ss2d_backward_saved", "ss1d_bidir_backward_saved",
 ]

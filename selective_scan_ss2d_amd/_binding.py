@@ -53,6 +53,13 @@ SIGNATURES = {
                                [_P] * 10 + [_I64] * 6 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_forward_routes_lr": (ctypes.c_int,
                                      [_P] * 10 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_saved_state_bytes": (_I64, [ctypes.c_int] + [_I64] * 4 + [ctypes.c_int]),
+    "ss2d_forward_save": (ctypes.c_int, [_P] * 10 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_forward_save": (ctypes.c_int,
+                                [_P] * 10 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_backward_saved": (ctypes.c_int, [_P] * 18 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_backward_saved": (ctypes.c_int,
+                                  [_P] * 18 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -496,6 +503,105 @@ def ss1d_bidir_backward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None, zo
     B, D, L = x.shape
     return _backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, stream, (B, D, L), L, z=z,
                      zoh=zoh, ex=True)
+
+
+def saved_state_bytes(K, B, D, L, N, gated=False) -> int:
+    """Bytes of the state a training forward keeps for its backward (see ss2d_forward_save);
+    raises ValueError for sizes the operator rejects or N not a multiple of 4."""
+    n = load_library().ss2d_saved_state_bytes(int(K), int(B), int(D), int(L), int(N),
+                                              1 if gated else 0)
+    if n < 0:
+        raise ValueError(f"no saved state for K={K}, B={B}, D={D}, L={L}, N={N}")
+    return n
+
+
+def _saved_tensor(saved, nbytes, device):
+    """The saved-state buffer: fp32, contiguous, of exactly nbytes (allocated if None)."""
+    torch = _torch()
+    if saved is None:
+        return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    _expect("saved", saved, (nbytes // 4,), torch.float32, device)
+    return saved
+
+
+def _forward_save(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, saved, stream, xshape,
+                  L):
+    lib = load_library()
+    B, D, N, y = _common(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, y, xshape, L)
+    zp = _gate_ptr(z, xshape, x)
+    saved = _saved_tensor(saved, saved_state_bytes(K, B, D, L, N, z is not None), x.device)
+    dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
+    fn = lib.ss2d_forward_save if K == 4 else lib.ss1d_bidir_forward_save
+    _check(fn(x.data_ptr(), dt_raw.data_ptr(), A_log.data_ptr(), Bs.data_ptr(), Cs.data_ptr(),
+              Ds.data_ptr(), dt_bias.data_ptr(), zp, y.data_ptr(), saved.data_ptr(), *dims, N,
+              _dtype_code(x), SS2D_FLAG_ZOH if zoh else 0, _stream_handle(x.device, stream)))
+    return y, saved
+
+
+def ss2d_forward_save(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False, y=None,
+                      saved=None, stream=None):
+    """The training forward: y as ss2d_forward_ex(..., z=z, zoh=zoh), and the state its
+    backward starts from (the scan's state before every 32-step tile, and with the gate the
+    ungated route sum), for ss2d_backward_saved.  Returns (y, saved); saved is an fp32
+    tensor of saved_state_bytes(4, B, D, H * W, N, z is not None) / 4 elements."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    return _forward_save(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, saved, stream,
+                         (B, D, H, W), H * W)
+
+
+def ss1d_bidir_forward_save(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False, y=None,
+                            saved=None, stream=None):
+    """ss2d_forward_save for the bidirectional operator (K = 2)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    return _forward_save(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, saved, stream,
+                         (B, D, L), L)
+
+
+def _backward_saved(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z, zoh, stream,
+                    xshape, L):
+    torch = _torch()
+    lib = load_library()
+    B, D, N, _ = _common(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, L)
+    saved = _saved_tensor(saved, saved_state_bytes(K, B, D, L, N, z is not None), x.device)
+    ins = (x, dt_raw, A_log, Bs, Cs, Ds, dt_bias)
+    grads = {name: torch.empty_like(t) for name, t in zip(GRAD_NAMES, ins)}
+    if z is not None:
+        _expect("z", z, xshape, x.dtype, x.device)
+        grads["z"] = torch.empty_like(z)
+    args = [t.data_ptr() for t in ins] + [None if z is None else z.data_ptr(),
+                                          saved.data_ptr(), dy.data_ptr()] + \
+        [grads[n].data_ptr() for n in GRAD_NAMES] + \
+        [None if z is None else grads["z"].data_ptr()]
+    dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
+    fn = lib.ss2d_backward_saved if K == 4 else lib.ss1d_bidir_backward_saved
+    _check(fn(*args, *dims, N, _dtype_code(x), SS2D_FLAG_ZOH if zoh else 0,
+              _stream_handle(x.device, stream)))
+    return grads
+
+
+def ss2d_backward_saved(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z=None, zoh=False,
+                        stream=None):
+    """The gradients of ss2d_backward_ex(..., z=z, zoh=zoh), starting from the state that
+    ss2d_forward_save kept in `saved` for the same inputs, gate and option."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    return _backward_saved(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z, zoh, stream,
+                           (B, D, H, W), H * W)
+
+
+def ss1d_bidir_backward_saved(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z=None,
+                              zoh=False, stream=None):
+    """ss2d_backward_saved for the bidirectional operator (K = 2)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    return _backward_saved(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z, zoh, stream,
+                           (B, D, L), L)
 
 
 def _backward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, z, zoh, stream):

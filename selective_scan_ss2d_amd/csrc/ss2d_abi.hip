@@ -9,6 +9,7 @@
 
 #include "ss2d.h"
 #include "ss2d_device.h"
+#include "ss2d_gate.h"
 
 namespace {
 
@@ -263,6 +264,23 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
   return SS2D_OK;
 }
 
+// The state a training forward keeps for its backward (ss2d_forward_save): the scan's state
+// before every 32-step tile, (B, K, D, ceil(L / 32), N) fp32 (the first tile's, zero, is not
+// written), then with the gate the ungated route sum v, (B, D, L) fp32.  Sizes in bytes;
+// -1 for sizes the operator rejects or N not a multiple of 4.
+int64_t saved_ck_bytes(int64_t B, int64_t K, int64_t D, int64_t L, int64_t N) {
+  return B * K * D * ((L + 31) / 32) * N * 4;
+}
+int64_t saved_bytes(int K, int64_t B, int64_t D, int64_t L, int64_t N, bool gated) {
+  if ((K != 2 && K != 4) || B < 0 || D < 0 || L < 1 || L >= kMaxL || N < 4 || N > 32 ||
+      (N & (N - 1)) != 0)
+    return -1;
+  int64_t ck, t, v = 0;
+  if (!mul_ok(B * K, D, &t) || !mul_ok(t, ((L + 31) / 32) * N * 4, &ck)) return -1;
+  if (gated && (!mul_ok(B, D, &t) || !mul_ok(t, L * 4, &v))) return -1;
+  return ck + v;
+}
+
 // routes: x is every route's own input u (B, K, D, L) in scan order instead of the image x.
 // dt_lr (not NULL): dt_proj folded in; dt_raw is then ignored and each step's dt_raw is
 // dt_w (K, D, R) times the step's column of dt_lr (B, K, R, L).
@@ -270,7 +288,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
             const void* Bs, const void* Cs, const float* Ds, const float* dt_bias, const void* z,
             void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
             int flags, void* stream, const void* dt_lr = nullptr, const float* dt_w = nullptr,
-            int64_t R = 0, bool noalloc = false) {
+            int64_t R = 0, bool noalloc = false, float* saved = nullptr, bool save = false) {
   const bool lr = dt_lr != nullptr || dt_w != nullptr || R != 0;
   // ---- validation (nothing is enqueued before all of it passes) -------------------------
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
@@ -285,8 +303,12 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
   if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
   if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
   if (lr && (R < 1 || R > ss2d::kMaxLowRank)) return SS2D_ERR_UNSUPPORTED;
+  // save: the training forward (checkpoints need four lanes per channel)
+  if (save && N % 4 != 0) return SS2D_ERR_UNSUPPORTED;
   if (B == 0 || D == 0) return SS2D_OK;
   if (!x || !A_log || !Bs || !Cs || !Ds || !dt_bias || !y) return SS2D_ERR_NULL;
+  if (save && !saved) return SS2D_ERR_NULL;
+  if (save && (reinterpret_cast<uintptr_t>(saved) & 15u)) return SS2D_ERR_ALIGN;
   if (lr ? (!dt_lr || !dt_w) : !dt_raw) return SS2D_ERR_NULL;
   const int64_t e = dtype == SS2D_F32 ? 4 : 2;
   const uintptr_t emask = static_cast<uintptr_t>(e - 1);
@@ -307,10 +329,26 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
       overlaps(y, y_bytes, dt_bias, int64_t(K) * D * 4) ||
       (z && overlaps(y, y_bytes, z, n_x * e)))
     return SS2D_ERR_ALIAS;
+  const int64_t tiles = (L + 31) / 32;
+  if (save) {
+    const int64_t sb = saved_bytes(K, B, D, L, N, z != nullptr);
+    if (sb < 0) return SS2D_ERR_SHAPE;
+    const void* others[] = {x, dt_raw, Bs, Cs, A_log, Ds, dt_bias, z, y};
+    const int64_t other_bytes[] = {n_x * e, n_dt * e, n_bc * e, n_bc * e,
+                                   int64_t(K) * D * N * 4, int64_t(K) * D * 4,
+                                   int64_t(K) * D * 4, n_x * e, y_bytes};
+    for (int i = 0; i < 9; ++i)
+      if (others[i] && overlaps(saved, sb, others[i], other_bytes[i])) return SS2D_ERR_ALIAS;
+  }
 
   // ---- plan and scratch --------------------------------------------------------------
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const Plan p = make_plan(K, B, D, H, W, N, dtype, routes);
+  Plan p = make_plan(K, B, D, H, W, N, dtype, routes);
+  if (save) {  // one pass, four lanes per channel, storing the state before every tile
+    p.split = 4;
+    p.num_chunks = 1;
+    p.chunk_len = static_cast<int>(tiles * 32);
+  }
   // noalloc: the scratch is the fixed device array (size checked before any HIP call)
   if (noalloc && p.bytes > kNoAllocScratchBytes) return SS2D_ERR_SCRATCH;
   char* ws = nullptr;
@@ -349,7 +387,13 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
       return ss2d::launch_transpose(x, ws + p.off_xt, a.B, a.D, static_cast<int>(H),
                                     static_cast<int>(W), dtype, st);
     });
-  if (!err && p.num_chunks > 1) {
+  if (!err && save) {
+    a.h_in = saved;
+    a.ck_tiles = static_cast<int>(tiles);
+    a.chunk_base = 0;
+    a.chunks_in_launch = 1;
+    rc = scan_pass(a, dtype, p, ss2d::kModeCkptOut, e, st);
+  } else if (!err && p.num_chunks > 1) {
     a.h_end = reinterpret_cast<float*>(ws + p.off_hend);
     a.delta_sum = reinterpret_cast<float*>(ws + p.off_dsum);
     ss2d::ScanArgs agg = a;  // aggregates of chunks 0 .. C-2
@@ -368,7 +412,20 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
     a.chunks_in_launch = 1;
     rc = scan_pass(a, dtype, p, ss2d::kModeOut, e, st);
   }
-  if (!err && rc == SS2D_OK) {
+  if (!err && rc == SS2D_OK && save && z) {
+    // the gated training forward keeps the ungated route sum (fp32) for the gate's backward,
+    // then gates it: the same sum and products as the fused gated merge
+    float* v = saved + saved_ck_bytes(B, K, D, L, N) / 4;
+    err = timed(SS2D_KERNEL_MERGE, st, [&] {
+      return (K == 4) ? ss2d::launch_merge4(a.y_route, nullptr, v, a.B, a.D,
+                                            static_cast<int>(H), static_cast<int>(W), SS2D_F32,
+                                            st)
+                      : ss2d::launch_merge2(a.y_route, nullptr, v, a.B, a.D, a.L, SS2D_F32, st);
+    });
+    if (!err)
+      err = timed(SS2D_KERNEL_MERGE, st,
+                  [&] { return ss2d::launch_gate_fwd(v, z, y, n_x, dtype, st); });
+  } else if (!err && rc == SS2D_OK) {
     err = timed(SS2D_KERNEL_MERGE, st, [&] {
       return (K == 4) ? ss2d::launch_merge4(a.y_route, z, y, a.B, a.D, static_cast<int>(H),
                                             static_cast<int>(W), dtype, st)
@@ -391,7 +448,8 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
              const void* Cs, const float* Ds, const float* dt_bias, const void* dy, void* dx,
              void* ddt_raw, float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
              int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, void* stream,
-             const void* z = nullptr, void* dz = nullptr, int flags = 0, bool routes = false) {
+             const void* z = nullptr, void* dz = nullptr, int flags = 0, bool routes = false,
+             const float* saved = nullptr, bool from_saved = false) {
   const bool gated = z != nullptr;
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_UNSUPPORTED;
   if (flags & ~SS2D_FLAG_ZOH) return SS2D_ERR_UNSUPPORTED;
@@ -404,7 +462,11 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   if (!mul_ok(B, D, &tmp) || !mul_ok(tmp, L, &n_x)) return SS2D_ERR_SHAPE;
   if (!mul_ok(n_x, K, &n_dt)) return SS2D_ERR_SHAPE;
   if (!mul_ok(B * K, N, &tmp) || !mul_ok(tmp, L, &n_bc)) return SS2D_ERR_SHAPE;
+  // from_saved: the checkpoints (and with the gate the route sum) a training forward kept
+  if (from_saved && N % 4 != 0) return SS2D_ERR_UNSUPPORTED;
   if (B == 0 || D == 0) return SS2D_OK;
+  if (from_saved && !saved) return SS2D_ERR_NULL;
+  if (from_saved && (reinterpret_cast<uintptr_t>(saved) & 15u)) return SS2D_ERR_ALIGN;
   // z and dz are the last input and output of the gated entry points
   const void* ins[] = {x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z};
   const void* outs[] = {dx, ddt_raw, dA_log, dBs, dCs, dDs, ddt_bias, dz};
@@ -434,6 +496,12 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SS2D_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SS2D_ERR_ALIAS;
+  }
+  if (from_saved) {
+    const int64_t sb = saved_bytes(K, B, D, L, N, gated);
+    if (sb < 0) return SS2D_ERR_SHAPE;
+    for (int i = 0; i < n_out; ++i)
+      if (overlaps(outs[i], out_bytes[i], saved, sb)) return SS2D_ERR_ALIAS;
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -504,7 +572,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   const size_t off_g = off;
   if (gated) off = align256(off + size_t(n_x * 4));
   const size_t off_ck = off;
-  off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
+  if (!from_saved) off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
   // per-route du in fp32: merged into dx, or (gate) first the route outputs; with per-route
   // inputs and no gate the adjoint writes du straight to the output
   const bool need_du = !routes || gated;
@@ -531,9 +599,11 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     err = timed(SS2D_KERNEL_TRANSPOSE, st, [&] {
       return ss2d::launch_transpose(x, ws + off_xt, int(B), int(D), int(H), int(W), dtype, st);
     });
+  const float* h_ck = from_saved ? saved : reinterpret_cast<const float*>(ws + off_ck);
   // Checkpoints: the forward scan storing the state before every 32-step tile (and, with the
-  // gate, the per-route outputs, which the merge kernel turns into g and dz).
-  if (!err) {
+  // gate, the per-route outputs, which the merge kernel turns into g and dz), unless a
+  // training forward kept them.
+  if (!err && !from_saved) {
     ss2d::ScanArgs a{};
     a.x_row = x;
     a.x_col = xt;
@@ -561,7 +631,13 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     p.split = 4;
     rc = scan_pass(a, dtype, p, gated ? ss2d::kModeCkptOut : ss2d::kModeCkpt, e, st);
   }
-  if (gated && !err && rc == SS2D_OK)
+  if (gated && from_saved && !err)  // g and dz from the route sum the forward kept
+    err = timed(SS2D_KERNEL_MERGE, st, [&] {
+      const float* v = saved + saved_ck_bytes(B, K, D, L, N) / 4;
+      return ss2d::launch_gate_bwd(v, z, dy, reinterpret_cast<float*>(ws + off_g), dz, n_x,
+                                   dtype, st);
+    });
+  else if (gated && !err && rc == SS2D_OK)
     err = timed(SS2D_KERNEL_MERGE, st, [&] {
       const float* yr = reinterpret_cast<const float*>(ws + off_du);
       return (K == 4) ? ss2d::launch_merge4_gate_bwd(yr, z, dy, ws + off_g, dz, int(B), int(D),
@@ -593,7 +669,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     g.A_log = A_log;
     g.Ds = Ds;
     g.dt_bias = dt_bias;
-    g.h_ck = reinterpret_cast<const float*>(ws + off_ck) + b0 * K * D * tiles * N;
+    g.h_ck = h_ck + b0 * K * D * tiles * N;
     g.du_route = need_du ? reinterpret_cast<float*>(ws + off_du) + b0 * K * D * L : nullptr;
     g.ddt_raw = static_cast<char*>(ddt_raw) + b0 * K * D * L * e;
     g.dbc_part = reinterpret_cast<float*>(ws + off_bc) + b0 * K * n_cb * 2 * N * L;
@@ -833,6 +909,49 @@ int ss1d_bidir_backward_routes(const void* u, const void* dt_raw, const float* A
                                int64_t N, int dtype, int flags, void* stream) {
   return backward(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, du, ddt_raw, dA_log, dBs, dCs,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags, true);
+}
+
+int64_t ss2d_saved_state_bytes(int K, int64_t B, int64_t D, int64_t L, int64_t N, int gated) {
+  return saved_bytes(K, B, D, L, N, gated != 0);
+}
+
+int ss2d_forward_save(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                      const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                      void* y, float* saved, int64_t B, int64_t D, int64_t H, int64_t W,
+                      int64_t N, int dtype, int flags, void* stream) {
+  return forward(4, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype,
+                 flags, stream, nullptr, nullptr, 0, false, saved, true);
+}
+
+int ss1d_bidir_forward_save(const void* x, const void* dt_raw, const float* A_log,
+                            const void* Bs, const void* Cs, const float* Ds,
+                            const float* dt_bias, const void* z, void* y, float* saved,
+                            int64_t B, int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                            void* stream) {
+  return forward(2, false, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype,
+                 flags, stream, nullptr, nullptr, 0, false, saved, true);
+}
+
+int ss2d_backward_saved(const void* x, const void* dt_raw, const float* A_log, const void* Bs,
+                        const void* Cs, const float* Ds, const float* dt_bias, const void* z,
+                        const float* saved, const void* dy, void* dx, void* ddt_raw,
+                        float* dA_log, void* dBs, void* dCs, float* dDs, float* ddt_bias,
+                        void* dz, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                        int dtype, int flags, void* stream) {
+  return backward(4, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, flags, false, saved,
+                  true);
+}
+
+int ss1d_bidir_backward_saved(const void* x, const void* dt_raw, const float* A_log,
+                              const void* Bs, const void* Cs, const float* Ds,
+                              const float* dt_bias, const void* z, const float* saved,
+                              const void* dy, void* dx, void* ddt_raw, float* dA_log, void* dBs,
+                              void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B,
+                              int64_t D, int64_t L, int64_t N, int dtype, int flags,
+                              void* stream) {
+  return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags, false, saved, true);
 }
 
 int ss2d_project(const void* x, const float* conv_w, const float* conv_b,

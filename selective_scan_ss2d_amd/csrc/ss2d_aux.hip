@@ -4,6 +4,7 @@
 #include <type_traits>
 
 #include "ss2d_device.h"
+#include "ss2d_gate.h"
 
 namespace ss2d {
 namespace {
@@ -802,6 +803,94 @@ int launch_merge4_gate_bwd(const float* y_route, const void* z, const void* dy, 
 int launch_merge2_gate_bwd(const float* y_route, const void* z, const void* dy, void* g,
                            void* dz, int B, int D, int L, int dtype, hipStream_t st) {
   return merge2(y_route, kGateBwd, z, dy, g, dz, B, D, L, dtype, st);
+}
+
+namespace {
+
+// The gate over a kept route sum, four positions per thread (16-byte accesses when every
+// pointer allows them, element by element otherwise and for the last positions).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_gate_fwd(const float* __restrict__ v, const T* __restrict__ z, T* __restrict__ y, int64_t n,
+           bool vec) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n;
+       i += stride) {
+    if (vec && i + 4 <= n) {
+      const float4 vv = *reinterpret_cast<const float4*>(v + i);
+      Out4<T>::store(y + i, vv.x * silu_f32(Elem<T>::load(z + i)),
+                     vv.y * silu_f32(Elem<T>::load(z + i + 1)),
+                     vv.z * silu_f32(Elem<T>::load(z + i + 2)),
+                     vv.w * silu_f32(Elem<T>::load(z + i + 3)));
+    } else {
+      for (int64_t j = i; j < i + 4 && j < n; ++j)
+        y[j] = Elem<T>::from_f32(v[j] * silu_f32(Elem<T>::load(z + j)));
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_gate_bwd(const float* __restrict__ v, const T* __restrict__ z, const T* __restrict__ dy,
+           float* __restrict__ g, T* __restrict__ dz, int64_t n, bool vec) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n;
+       i += stride) {
+    if (vec && i + 4 <= n) {
+      const float4 vv = *reinterpret_cast<const float4*>(v + i);
+      const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+      float gs[4], zs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gate_bwd(vs[j], Elem<T>::load(z + i + j), Elem<T>::load(dy + i + j), gs[j], zs[j]);
+      Out4<float>::store(g + i, gs[0], gs[1], gs[2], gs[3]);
+      Out4<T>::store(dz + i, zs[0], zs[1], zs[2], zs[3]);
+    } else {
+      for (int64_t j = i; j < i + 4 && j < n; ++j) {
+        float gj, zj;
+        gate_bwd(v[j], Elem<T>::load(z + j), Elem<T>::load(dy + j), gj, zj);
+        g[j] = gj;
+        dz[j] = Elem<T>::from_f32(zj);
+      }
+    }
+  }
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+unsigned gate_blocks(int64_t n) {
+  const int64_t want = (n + 1023) / 1024;  // four positions per thread
+  return static_cast<unsigned>(want < 65536 ? (want > 0 ? want : 1) : 65536);
+}
+
+}  // namespace
+
+int launch_gate_fwd(const float* v, const void* z, void* y, int64_t n, int dtype,
+                    hipStream_t st) {
+  if (n <= 0) return 0;
+  const bool vec = aligned16(v) && aligned16(z) && aligned16(y);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gate_fwd<float>, dim3(gate_blocks(n)), dim3(256), 0, st, v,
+                       static_cast<const float*>(z), static_cast<float*>(y), n, vec);
+  else
+    hipLaunchKernelGGL(k_gate_fwd<uint16_t>, dim3(gate_blocks(n)), dim3(256), 0, st, v,
+                       static_cast<const uint16_t*>(z), static_cast<uint16_t*>(y), n, vec);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_gate_bwd(const float* v, const void* z, const void* dy, float* g, void* dz,
+                    int64_t n, int dtype, hipStream_t st) {
+  if (n <= 0) return 0;
+  const bool vec = aligned16(v) && aligned16(z) && aligned16(dy) && aligned16(g) && aligned16(dz);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gate_bwd<float>, dim3(gate_blocks(n)), dim3(256), 0, st, v,
+                       static_cast<const float*>(z), static_cast<const float*>(dy), g,
+                       static_cast<float*>(dz), n, vec);
+  else
+    hipLaunchKernelGGL(k_gate_bwd<uint16_t>, dim3(gate_blocks(n)), dim3(256), 0, st, v,
+                       static_cast<const uint16_t*>(z), static_cast<const uint16_t*>(dy), g,
+                       static_cast<uint16_t*>(dz), n, vec);
+  return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace ss2d
