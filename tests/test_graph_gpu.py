@@ -107,3 +107,21 @@ def test_front_chain_in_graph():
                                    dev["Ds"], dev["dt_bias"], wl.H, wl.W, z=z)
         return {"y": y, **o}
     _check_replays("front end + routes operator", chain)
+
+
+@pytest.mark.parametrize("gate", [False, True], ids=["plain", "gate"])
+def test_training_pair_in_graph(gate):
+    """The training forward and the backward from its kept state, captured as one graph."""
+    import torch
+    import selective_scan_ss2d_amd as ss
+    wl = workloads.custom(2, 70, 16, 24, 16, 4, "bf16")
+    dev, z, dy = _inputs(wl, 55)
+    args = [dev[k] for k in ARGS]
+    zz = z if gate else None
+    saved = torch.empty(ss.saved_state_bytes(4, wl.B, wl.D, wl.H * wl.W, wl.N, gate) // 4,
+                        dtype=torch.float32, device="cuda:0")
+
+    def step():
+        y, _ = ss.ss2d_forward_save(*args, z=zz, saved=saved)
+        return {"y": y, **ss.ss2d_backward_saved(*args, dy, saved, z=zz)}
+    _check_replays(f"training pair gate={gate}", step)
