@@ -292,6 +292,37 @@ int ss1d_bidir_backward_saved(const void *x, const void *dt_raw, const float *A_
                               int64_t D, int64_t L, int64_t N, int dtype, int flags,
                               void *stream);
 
+/* The same pair for the operator over per-route inputs (ss2d_forward_routes,
+ * ss2d_backward_routes): u (B, K, D, L) in place of x, du in place of dx; the saved state's
+ * size and layout are those above. */
+int ss2d_forward_routes_save(const void *u, const void *dt_raw, const float *A_log,
+                             const void *Bs, const void *Cs, const float *Ds,
+                             const float *dt_bias, const void *z, void *y, float *saved,
+                             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                             int flags, void *stream);
+
+int ss1d_bidir_forward_routes_save(const void *u, const void *dt_raw, const float *A_log,
+                                   const void *Bs, const void *Cs, const float *Ds,
+                                   const float *dt_bias, const void *z, void *y, float *saved,
+                                   int64_t B, int64_t D, int64_t L, int64_t N, int dtype,
+                                   int flags, void *stream);
+
+int ss2d_backward_routes_saved(const void *u, const void *dt_raw, const float *A_log,
+                               const void *Bs, const void *Cs, const float *Ds,
+                               const float *dt_bias, const void *z, const float *saved,
+                               const void *dy, void *du, void *ddt_raw, float *dA_log, void *dBs,
+                               void *dCs, float *dDs, float *ddt_bias, void *dz, int64_t B,
+                               int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
+                               void *stream);
+
+int ss1d_bidir_backward_routes_saved(const void *u, const void *dt_raw, const float *A_log,
+                                     const void *Bs, const void *Cs, const float *Ds,
+                                     const float *dt_bias, const void *z, const float *saved,
+                                     const void *dy, void *du, void *ddt_raw, float *dA_log,
+                                     void *dBs, void *dCs, float *dDs, float *ddt_bias, void *dz,
+                                     int64_t B, int64_t D, int64_t L, int64_t N, int dtype,
+                                     int flags, void *stream);
+
 /* ---- backward of the operator over per-route inputs ---------------------------------------
  * Gradients of the scalar sum over (b, d, l) of dy[b, d, l] * y[b, d, l], y being the output
  * of ss2d_forward_routes (ss1d_bidir_forward_routes) on the same inputs, gate z and flags:

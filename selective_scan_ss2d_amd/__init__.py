@@ -19,7 +19,9 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
                        ss2d_project_lr, status_string, timing_enable, timing_read,
                        launch_plan, probe_issue_rates, saved_state_bytes,
                        ss2d_forward_save, ss1d_bidir_forward_save, ss2d_backward_saved,
-                       ss1d_bidir_backward_saved)
+                       ss1d_bidir_backward_saved, ss2d_forward_routes_save,
+                       ss1d_bidir_forward_routes_save, ss2d_backward_routes_saved,
+                       ss1d_bidir_backward_routes_saved)
 
 __all__ = [
     "ss2d_forward", "ss1d_bidir_forward", "ss2d_forward_ex", "ss1d_bidir_forward_ex",
@@ -33,5 +35,7 @@ __all__ = [
     "SS2D_ERR_UNSUPPORTED", "SS2D_ERR_ALIGN", "SS2D_ERR_HIP", "SS2D_ERR_ALIAS", "SS2D_F32",
     "SS2D_BF16", "KERNEL_KINDS", "timing_enable", "timing_read", "launch_plan",
     "probe_issue_rates", "saved_state_bytes", "ss2d_forward_save", "ss1d_bidir_forward_save",
-    "ss2d_backward_saved", "ss1d_bidir_backward_saved",
+    "ss2d_backward_saved", "ss1d_bidir_backward_saved", "ss2d_forward_routes_save",
+    "ss1d_bidir_forward_routes_save", "ss2d_backward_routes_saved",
+    "ss1d_bidir_backward_routes_saved",
 ]

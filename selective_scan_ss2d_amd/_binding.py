@@ -60,6 +60,14 @@ SIGNATURES = {
     "ss2d_backward_saved": (ctypes.c_int, [_P] * 18 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
     "ss1d_bidir_backward_saved": (ctypes.c_int,
                                   [_P] * 18 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_forward_routes_save": (ctypes.c_int,
+                                 [_P] * 10 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_forward_routes_save": (ctypes.c_int,
+                                       [_P] * 10 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
+    "ss2d_backward_routes_saved": (ctypes.c_int,
+                                   [_P] * 18 + [_I64] * 5 + [ctypes.c_int] * 2 + [_P]),
+    "ss1d_bidir_backward_routes_saved": (ctypes.c_int,
+                                         [_P] * 18 + [_I64] * 4 + [ctypes.c_int] * 2 + [_P]),
     "ss2d_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
@@ -269,9 +277,9 @@ def ss1d_bidir_forward_ex(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=Fal
 
 
 def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream, xshape,
-                    dt_w=None):
+                    dt_w=None, save=False, saved=None):
     """dt_w given: dt_raw is the low-rank dt_lr (B, K, R, L), multiplied by dt_w (K, D, R)
-    inside the scan."""
+    inside the scan.  save: the training forward, returning (y, saved)."""
     torch = _torch()
     lib = load_library()
     if u.device.type != "cuda":
@@ -302,6 +310,12 @@ def _routes_forward(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
     common = (A_log.data_ptr(), Bs.data_ptr(), Cs.data_ptr(), Ds.data_ptr(),
               dt_bias.data_ptr(), zp, y.data_ptr(), *xshape[:2], *xshape[2:], N)
     tail = (_dtype_code(u), SS2D_FLAG_ZOH if zoh else 0, _stream_handle(dev, stream))
+    if save:
+        saved = _saved_tensor(saved, saved_state_bytes(K, B, D, L, N, z is not None), dev)
+        fn = lib.ss2d_forward_routes_save if K == 4 else lib.ss1d_bidir_forward_routes_save
+        common = common[:6] + (y.data_ptr(), saved.data_ptr()) + common[7:]
+        _check(fn(u.data_ptr(), dt_raw.data_ptr(), *common, *tail))
+        return y, saved
     if dt_w is None:
         fn = lib.ss2d_forward_routes if K == 4 else lib.ss1d_bidir_forward_routes
         status = fn(u.data_ptr(), dt_raw.data_ptr(), *common, *tail)
@@ -604,7 +618,8 @@ def ss1d_bidir_backward_saved(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, 
                            (B, D, L), L)
 
 
-def _backward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, z, zoh, stream):
+def _backward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, z, zoh, stream,
+                     saved=None):
     torch = _torch()
     lib = load_library()
     if u.device.type != "cuda":
@@ -629,9 +644,15 @@ def _backward_routes(K, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, xshape, z, zo
     if z is not None:
         _expect("z", z, xshape, u.dtype, u.device)
         grads["z"] = torch.empty_like(z)
-    args = [t.data_ptr() for t in ins] + [None if z is None else z.data_ptr(), dy.data_ptr()] + \
+    zp = [None if z is None else z.data_ptr()]
+    if saved is not None:  # from the state ss2d_forward_routes_save kept
+        saved = _saved_tensor(saved, saved_state_bytes(K, B, D, L, N, z is not None), dev)
+        zp.append(saved.data_ptr())
+        fn = lib.ss2d_backward_routes_saved if K == 4 else lib.ss1d_bidir_backward_routes_saved
+    else:
+        fn = lib.ss2d_backward_routes if K == 4 else lib.ss1d_bidir_backward_routes
+    args = [t.data_ptr() for t in ins] + zp + [dy.data_ptr()] + \
         [grads[n].data_ptr() for n in names] + [None if z is None else grads["z"].data_ptr()]
-    fn = lib.ss2d_backward_routes if K == 4 else lib.ss1d_bidir_backward_routes
     dims = (B, D, xshape[2], xshape[3]) if K == 4 else (B, D, L)
     _check(fn(*args, *dims, N, _dtype_code(u), SS2D_FLAG_ZOH if zoh else 0,
               _stream_handle(u.device, stream)))
@@ -658,6 +679,50 @@ def ss1d_bidir_backward_routes(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, z=None
     B, D, L = u.shape[0], u.shape[2], u.shape[3]
     return _backward_routes(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, L), z, zoh,
                             stream)
+
+
+def ss2d_forward_routes_save(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, H, W, z=None, zoh=False,
+                             y=None, saved=None, stream=None):
+    """The training forward of the operator over per-route inputs: y as ss2d_forward_routes,
+    and the state ss2d_backward_routes_saved starts from.  Returns (y, saved)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 4, D, L)")
+    if u.shape[-1] != H * W:
+        raise ValueError(f"u has {u.shape[-1]} steps, expected H * W = {H * W}")
+    B, D = u.shape[0], u.shape[2]
+    return _routes_forward(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (B, D, H, W), save=True, saved=saved)
+
+
+def ss1d_bidir_forward_routes_save(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False,
+                                   y=None, saved=None, stream=None):
+    """ss2d_forward_routes_save for the bidirectional operator, u (B, 2, D, L)."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 2, D, L)")
+    B, D, L = u.shape[0], u.shape[2], u.shape[3]
+    return _routes_forward(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, stream,
+                           (B, D, L), save=True, saved=saved)
+
+
+def ss2d_backward_routes_saved(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, H, W,
+                               z=None, zoh=False, stream=None):
+    """The gradients of ss2d_backward_routes, starting from the state that
+    ss2d_forward_routes_save kept for the same inputs, gate and option."""
+    if u.dim() != 4:
+        raise ValueError("u must be (B, 4, D, L)")
+    if u.shape[-1] != H * W:
+        raise ValueError(f"u has {u.shape[-1]} steps, expected H * W = {H * W}")
+    B, D = u.shape[0], u.shape[2]
+    return _backward_routes(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, H, W), z, zoh,
+                            stream, saved=saved)
+
+
+def ss1d_bidir_backward_routes_saved(u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, saved, z=None,
+                                     zoh=False, stream=None):
+    """ss2d_backward_routes_saved for the bidirectional operator, u (B, 2, D, L)."""
+    B, D, L = u.shape[0], u.shape[2], u.shape[3]
+    return _backward_routes(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, (B, D, L), z, zoh,
+                            stream, saved=saved)
 
 
 class launch_plan:

@@ -334,7 +334,7 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
     const int64_t sb = saved_bytes(K, B, D, L, N, z != nullptr);
     if (sb < 0) return SS2D_ERR_SHAPE;
     const void* others[] = {x, dt_raw, Bs, Cs, A_log, Ds, dt_bias, z, y};
-    const int64_t other_bytes[] = {n_x * e, n_dt * e, n_bc * e, n_bc * e,
+    const int64_t other_bytes[] = {(routes ? n_dt : n_x) * e, n_dt * e, n_bc * e, n_bc * e,
                                    int64_t(K) * D * N * 4, int64_t(K) * D * 4,
                                    int64_t(K) * D * 4, n_x * e, y_bytes};
     for (int i = 0; i < 9; ++i)
@@ -952,6 +952,46 @@ int ss1d_bidir_backward_saved(const void* x, const void* dt_raw, const float* A_
                               void* stream) {
   return backward(2, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, dx, ddt_raw, dA_log, dBs, dCs,
                   dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags, false, saved, true);
+}
+
+int ss2d_forward_routes_save(const void* u, const void* dt_raw, const float* A_log,
+                             const void* Bs, const void* Cs, const float* Ds,
+                             const float* dt_bias, const void* z, void* y, float* saved,
+                             int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                             int flags, void* stream) {
+  return forward(4, true, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, H, W, N, dtype,
+                 flags, stream, nullptr, nullptr, 0, false, saved, true);
+}
+
+int ss1d_bidir_forward_routes_save(const void* u, const void* dt_raw, const float* A_log,
+                                   const void* Bs, const void* Cs, const float* Ds,
+                                   const float* dt_bias, const void* z, void* y, float* saved,
+                                   int64_t B, int64_t D, int64_t L, int64_t N, int dtype,
+                                   int flags, void* stream) {
+  return forward(2, true, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, y, B, D, 1, L, N, dtype,
+                 flags, stream, nullptr, nullptr, 0, false, saved, true);
+}
+
+int ss2d_backward_routes_saved(const void* u, const void* dt_raw, const float* A_log,
+                               const void* Bs, const void* Cs, const float* Ds,
+                               const float* dt_bias, const void* z, const float* saved,
+                               const void* dy, void* du, void* ddt_raw, float* dA_log, void* dBs,
+                               void* dCs, float* dDs, float* ddt_bias, void* dz, int64_t B,
+                               int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int flags,
+                               void* stream) {
+  return backward(4, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, du, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, H, W, N, dtype, stream, z, dz, flags, true, saved, true);
+}
+
+int ss1d_bidir_backward_routes_saved(const void* u, const void* dt_raw, const float* A_log,
+                                     const void* Bs, const void* Cs, const float* Ds,
+                                     const float* dt_bias, const void* z, const float* saved,
+                                     const void* dy, void* du, void* ddt_raw, float* dA_log,
+                                     void* dBs, void* dCs, float* dDs, float* ddt_bias, void* dz,
+                                     int64_t B, int64_t D, int64_t L, int64_t N, int dtype,
+                                     int flags, void* stream) {
+  return backward(2, u, dt_raw, A_log, Bs, Cs, Ds, dt_bias, dy, du, ddt_raw, dA_log, dBs, dCs,
+                  dDs, ddt_bias, B, D, 1, L, N, dtype, stream, z, dz, flags, true, saved, true);
 }
 
 int ss2d_project(const void* x, const float* conv_w, const float* conv_b,

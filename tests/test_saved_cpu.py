@@ -93,3 +93,20 @@ def test_backward_saved_checks(lib):
         assert bwd_saved(lib, p) == bnd.SS2D_ERR_HIP
     assert lib.ss1d_bidir_backward_saved(*p[:8], None, *p[9:], 2, 8, 16, 4, 0, 0, None) == \
         bnd.SS2D_ERR_NULL
+
+
+def test_routes_pair_checks(lib):
+    p = fake_ptrs(10)
+    q = list(p)
+    q[9] = None
+    assert lib.ss2d_forward_routes_save(*q, 1, 8, 8, 8, 4, 0, 0, None) == bnd.SS2D_ERR_NULL
+    q = list(p)
+    q[9] = p[0] + (1 << 12)  # inside u, which holds K routes: 4x the image's bytes
+    assert lib.ss2d_forward_routes_save(*q, 1, 8, 8, 8, 4, 0, 0, None) == bnd.SS2D_ERR_ALIAS
+    p = fake_ptrs(18)
+    assert lib.ss2d_backward_routes_saved(*p, 1, 8, 8, 8, 2, 0, 0, None) == \
+        bnd.SS2D_ERR_UNSUPPORTED
+    q = list(p)
+    q[8] = None
+    assert lib.ss1d_bidir_backward_routes_saved(*q, 2, 8, 16, 4, 0, 0, None) == \
+        bnd.SS2D_ERR_NULL

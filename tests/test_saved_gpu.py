@@ -2,7 +2,8 @@
 (one pass) bit for bit, and ss2d_backward_saved, starting from the state it kept, gives
 ss2d_backward_ex's gradients bit for bit; for both route sets and element types, with and
 without the gate and the zero-order hold, on ragged and whole-tile shapes and at the
-benchmark size.  The backward_ex results themselves are checked against the float64 oracle
+benchmark size; and the same for the pair over per-route inputs against
+ss2d_forward_routes and ss2d_backward_routes.  The backward_ex results themselves are checked against the float64 oracle
 in tests/test_backward_gpu.py and tests/test_backward_ex_gpu.py."""
 import numpy as np
 import pytest
@@ -115,3 +116,44 @@ def test_saved_deterministic():
     assert _same(y1, y2) and _same(c1, c2) and _same(s1[ck:], s2[ck:])
     for name in g1:
         assert _same(g1[name], g2[name]), name
+
+
+ROUTE_SHAPES = [(2, 70, 5, 7, 16, 4, "bf16"), (1, 64, 8, 8, 16, 4, "f32"),
+                (3, 40, 1, 197, 16, 2, "bf16"), (2, 16, 1, 64, 8, 2, "f32")]
+
+
+@pytest.mark.parametrize("gate,zoh", [(False, False), (True, True)], ids=["plain", "gate_zoh"])
+@pytest.mark.parametrize("shape", ROUTE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_routes_saved_equals_recomputed(shape, gate, zoh):
+    """The training pair of the operator over per-route inputs against ss2d_forward_routes
+    and ss2d_backward_routes, bit for bit."""
+    import torch
+    import selective_scan_ss2d_amd as ss
+    B, D, H, W, N, K, dt = shape
+    wl = workloads.custom(B, D, H, W, N, K, dt)
+    log(f"case routes saved B{B} D{D} {H}x{W} N{N} K{K} {dt} gate={gate} zoh={zoh}")
+    inp = workloads.make_inputs(wl, seed=11, a_log="random")
+    dev = to_device(inp, wl)
+    r = workloads.make_route_inputs(wl, 11)
+    u = (torch.from_numpy(r["u_bf16"].view(np.int16)).view(torch.bfloat16) if dt == "bf16"
+         else torch.from_numpy(r["u"])).to("cuda:0")
+    rest = [dev[k] for k in ARGS[1:]]
+    dy = _image(workloads.make_output_grad(wl, 11), "dy", wl)
+    z = _image(workloads.make_gate(wl, 11), "z", wl) if gate else None
+    hw = (H, W) if K == 4 else ()
+    if K == 4:
+        fwd, fsave = ss.ss2d_forward_routes, ss.ss2d_forward_routes_save
+        bwd, bsaved = ss.ss2d_backward_routes, ss.ss2d_backward_routes_saved
+    else:
+        fwd, fsave = ss.ss1d_bidir_forward_routes, ss.ss1d_bidir_forward_routes_save
+        bwd, bsaved = ss.ss1d_bidir_backward_routes, ss.ss1d_bidir_backward_routes_saved
+    with plan_override(split=4, chunk_len=0):
+        y_ref = fwd(u, *rest, *hw, z=z, zoh=zoh)
+    y, saved = fsave(u, *rest, *hw, z=z, zoh=zoh)
+    g_ref = bwd(u, *rest, dy, *hw, z=z, zoh=zoh)
+    g = bsaved(u, *rest, dy, saved, *hw, z=z, zoh=zoh)
+    torch.cuda.synchronize()
+    assert _same(y, y_ref)
+    assert set(g) == set(g_ref)
+    for name in g_ref:
+        assert _same(g[name], g_ref[name]), name
