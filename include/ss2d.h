@@ -48,7 +48,8 @@
  *     launched and y is untouched.  Nothing is printed and no exception crosses the ABI.
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default stream).
  *     Faults inside the kernels surface at the caller's next synchronisation.
- *   - Calls keep no data between them.  Internal scratch (a transposed copy of x, per-route
+ *   - Calls keep no data between them (the training pair below hands its state over in a
+ *     caller-owned buffer).  Internal scratch (a transposed copy of x, per-route
  *     fp32 partial outputs, chunk carries) is allocated on `stream` from a stream-ordered
  *     memory pool of the library's own (one per device, created at the first call on that
  *     device, held until the process ends) and released on `stream` in the same call.  The
