@@ -37,7 +37,7 @@ METRIC = ("SS2D fwd state-updates/s (B·K·D·L·N) + achieved HBM GB/s, "
 # 157.3 TFLOP/s, against the algorithmic 4 flops of one state update (delta*A, the decay
 # times h, (delta*u)*B, C*h) plus its exponential.  Issue slots: the VALU issues one wave64
 # instruction per 4 cycles on each of 256 CUs x 4 SIMDs at 2.4 GHz, 3.93e13 lane-slots/s
-# without packed fp32 (which this build does not emit); one update needs at least 2
+# without packed fp32 (which the library's compile flags exclude); one update needs at least 2
 # multiplies, 2 FMAs and one v_exp_f32, which takes two issue slots: 6 slots.  The
 # issue-floor fraction is that floor's time over the measured time.
 FP32_PEAK_TFLOPS = 157.3
