@@ -569,8 +569,18 @@ k_bwd_reduce_params(const float* __restrict__ dA_part, const float* __restrict__
   } else {
     src = dbias_part + (i - nA - KD); stride = KD; dst = ddt_bias + (i - nA - KD);
   }
+  // images in order; the loads of 32 images are issued together (a loop of dependent
+  // load-then-add steps waits for every load in turn)
   double v = 0.0;
-  for (int b = 0; b < B; ++b) v += static_cast<double>(src[b * stride]);
+  int b = 0;
+  for (; b + 32 <= B; b += 32) {
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] = src[static_cast<int64_t>(b + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v += static_cast<double>(x[j]);
+  }
+  for (; b < B; ++b) v += static_cast<double>(src[static_cast<int64_t>(b) * stride]);
   *dst = static_cast<float>(v);
 }
 
