@@ -697,6 +697,15 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        # The only speed figure the pages give for SS2D on named hardware: a module-level
+        # comparison with attention, not this operator's metric, so never a baseline.
+        "published_context": {
+            "claim": "SS2D module against conventional attention: memory use down 63%, "
+                     "throughput up 2.4x",
+            "hardware": "A100",
+            "source": "mhpn.cn, VMamba架构解析, section 2",
+            "comparable": False,
+        },
     }
     if roofline_front is not None:
         out["roofline_front"] = roofline_front
