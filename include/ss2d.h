@@ -54,8 +54,9 @@
  *     memory pool of the library's own (one per device, created at the first call on that
  *     device, held until the process ends) and released on `stream` in the same call.  The
  *     pool keeps freed blocks for later calls (its release threshold is unlimited), so the
- *     device memory of the largest scratch used so far stays reserved by the library; the
- *     device's default pool and its attributes are not touched.  Under stream capture the
+ *     device memory of the largest scratch used so far stays reserved by the library until
+ *     ss2d_scratch_trim hands it back; the device's default pool and its attributes are not
+ *     touched.  Under stream capture the
  *     scratch becomes an allocation node of the graph (no synchronisation, copy or memset
  *     is enqueued, so every entry point can be captured).
  *   - Results are deterministic: identical inputs, shapes and device give bitwise identical
@@ -75,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 10
+#define SS2D_ABI_VERSION 11
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -463,6 +464,17 @@ int ss2d_abi_version(void);
 /* hipError_t value of the last failed HIP call made by this library on the calling thread
  * (0 if none). */
 int ss2d_last_hip_error(void);
+
+/* ---- scratch pool (memory management, not part of the operator) -----------------------
+ * Hands the device memory that the library's scratch pool on the calling thread's current
+ * device reserves beyond keep_bytes back to the driver (hipMemPoolTrimTo), for callers that
+ * need it for other allocations between calls; later calls allocate it again.  Writes the
+ * bytes the pool still reserves afterwards to *reserved (may be NULL).  Only memory that
+ * no call uses is released: scratch of a call still running, or whose release is still
+ * pending on its stream, stays reserved, so synchronise the streams of earlier calls first.
+ * On a device where the library has made no call there is no pool: SS2D_OK with
+ * *reserved = 0.  Returns SS2D_OK or SS2D_ERR_HIP. */
+int ss2d_scratch_trim(size_t keep_bytes, size_t *reserved);
 
 /* ---- kernel timing (measurement support, not part of the operator) -----------------------
  * While enabled on a host thread, every call from that thread brackets each kernel launch

@@ -21,7 +21,7 @@ from ._binding import (LIBRARY_PATH, SS2D_BF16, SS2D_ERR_ALIAS, SS2D_ERR_ALIGN, 
                        ss2d_forward_save, ss1d_bidir_forward_save, ss2d_backward_saved,
                        ss1d_bidir_backward_saved, ss2d_forward_routes_save,
                        ss1d_bidir_forward_routes_save, ss2d_backward_routes_saved,
-                       ss1d_bidir_backward_routes_saved)
+                       ss1d_bidir_backward_routes_saved, scratch_trim)
 
 __all__ = [
     "ss2d_forward", "ss1d_bidir_forward", "ss2d_forward_ex", "ss1d_bidir_forward_ex",
@@ -37,5 +37,5 @@ __all__ = [
     "probe_issue_rates", "saved_state_bytes", "ss2d_forward_save", "ss1d_bidir_forward_save",
     "ss2d_backward_saved", "ss1d_bidir_backward_saved", "ss2d_forward_routes_save",
     "ss1d_bidir_forward_routes_save", "ss2d_backward_routes_saved",
-    "ss1d_bidir_backward_routes_saved",
+    "ss1d_bidir_backward_routes_saved", "scratch_trim",
 ]

@@ -72,6 +72,7 @@ SIGNATURES = {
     "ss2d_abi_version": (ctypes.c_int, []),
     "ss2d_last_hip_error": (ctypes.c_int, []),
     "ss2d_set_launch_plan": (ctypes.c_int, [ctypes.c_int, _I64]),
+    "ss2d_scratch_trim": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
     "ss2d_probe_issue_rates": (ctypes.c_int, [_P, _P]),
     "ss2d_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "ss2d_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
@@ -116,6 +117,17 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
 
 def abi_version() -> int:
     return load_library().ss2d_abi_version()
+
+
+def scratch_trim(keep_bytes: int = 0) -> int:
+    """Hand the library's pooled scratch on the current device beyond keep_bytes back to
+    the driver; returns the bytes it still reserves.  Synchronise the streams of earlier
+    calls first: scratch still in use stays reserved."""
+    if keep_bytes < 0:
+        raise ValueError("keep_bytes must be >= 0")
+    reserved = ctypes.c_size_t(0)
+    _check(load_library().ss2d_scratch_trim(int(keep_bytes), ctypes.byref(reserved)))
+    return int(reserved.value)
 
 
 def status_string(status: int) -> str:

@@ -61,11 +61,13 @@ int hip_fail(hipError_t e) {
 // so after the first call the per-call allocation is a pool hit.  The device's default pool
 // is left as it is.  Under stream capture the allocation becomes a node of the graph.
 constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
 int scratch_pool(int device, hipMemPool_t* out) {
-  static std::mutex mu;
-  static hipMemPool_t pools[kMaxDevices] = {};
+  hipMemPool_t* const pools = g_pools;
   if (device < 0 || device >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
-  std::lock_guard<std::mutex> lock(mu);
+  std::lock_guard<std::mutex> lock(g_pool_mu);
   if (!pools[device]) {
     hipMemPoolProps props{};
     props.allocType = hipMemAllocationTypePinned;
@@ -1087,6 +1089,26 @@ int ss2d_set_launch_plan(int split, int64_t chunk_len) {
 }
 
 int ss2d_last_hip_error(void) { return g_last_hip_error; }
+
+int ss2d_scratch_trim(size_t keep_bytes, size_t* reserved) {
+  if (reserved) *reserved = 0;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e);
+  if (device < 0 || device >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  hipMemPool_t pool = g_pools[device];
+  if (!pool) return SS2D_OK;  // no call has run on this device: nothing is reserved
+  e = hipMemPoolTrimTo(pool, keep_bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  if (reserved) {
+    uint64_t now = 0;
+    e = hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &now);
+    if (e != hipSuccess) return hip_fail(e);
+    *reserved = static_cast<size_t>(now);
+  }
+  return SS2D_OK;
+}
 
 int ss2d_probe_issue_rates(double* out, void* stream) {
   if (!out) return SS2D_ERR_NULL;

@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 10
+    assert lib.ss2d_abi_version() == 11
     seen = set()
     for code in range(8):
         s = lib.ss2d_status_string(code)
@@ -511,6 +511,21 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
         pytest.skip("a GPU is present")
     assert call2d(lib, fake_ptrs()) == bnd.SS2D_ERR_HIP
     assert lib.ss2d_last_hip_error() != 0
+
+
+def test_scratch_trim_without_gpu_fails_cleanly(lib):
+    # No device: the HIP runtime call fails and the status says so; the reserved-bytes
+    # output is written (0) whatever the outcome.
+    import ctypes
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    reserved = ctypes.c_size_t(12345)
+    assert lib.ss2d_scratch_trim(0, ctypes.byref(reserved)) == bnd.SS2D_ERR_HIP
+    assert reserved.value == 0
+    assert lib.ss2d_scratch_trim(0, None) == bnd.SS2D_ERR_HIP
+    with pytest.raises(ValueError):
+        bnd.scratch_trim(-1)
 
 
 # ---- host logic: the input generator --------------------------------------------------
