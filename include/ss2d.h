@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 11
+#define SS2D_ABI_VERSION 12
 
 /* Status codes returned by every entry point. */
 #define SS2D_OK 0
@@ -243,16 +243,17 @@ int ss1d_bidir_backward_ex(const void *x, const void *dt_raw, const float *A_log
 
 /* ---- training: a forward that keeps the backward's checkpoints ---------------------------
  * In training the forward and the backward run on the same inputs.  The backward restarts
- * every 32-step tile of the scan from the state before it, which ss2d_backward_ex obtains by
- * running the forward scan once more (the Vim summary, section 4.4: states are recomputed,
- * not kept in HBM per step); ss2d_forward_save keeps those tile states while it computes y,
- * and ss2d_backward_saved starts from them, so that the pair does the scan's forward work
- * once.
+ * every 8-step quarter of the scan from the state before it, which ss2d_backward_ex obtains
+ * by running the forward scan once more (the Vim summary, section 4.4: states are
+ * recomputed, not kept in HBM per step); ss2d_forward_save keeps those states while it
+ * computes y, and ss2d_backward_saved starts from them, so that the pair does the scan's
+ * forward work once.
  *
  * saved: caller-owned device memory of ss2d_saved_state_bytes(K, B, D, L, N, gated) bytes
  * (K = 4 with L = H * W for the image operators, K = 2 for the bidirectional one; gated:
- * whether z is given), 16-byte aligned.  Layout: the state before every 32-step tile,
- * (B, K, D, ceil(L / 32), N) fp32 (the first tile's, zero, is not written), then with the
+ * whether z is given), 16-byte aligned.  Layout: the state before every 8-step quarter,
+ * (B, K, D, ceil(L / 8), N) fp32 (the first quarter's, zero, is not written; 16 bytes per
+ * element of x for N = 16), then with the
  * gate the ungated route sum ((y_0 + y_1) + y_2) + y_3, (B, D, L) fp32, from which the
  * gate's backward forms g and dz.  ss2d_saved_state_bytes returns -1 for sizes the
  * operator rejects and for N not a multiple of 4.
@@ -488,7 +489,7 @@ int ss2d_scratch_trim(size_t keep_bytes, size_t *reserved);
 #define SS2D_KERNEL_CARRY 3     /* not launched: chunk start states are composed in the
                                    scan's second pass (the kind keeps its number)        */
 #define SS2D_KERNEL_MERGE 4     /* cross-merge into y (backward: route gradients into dx) */
-#define SS2D_KERNEL_CHECKPOINT 5 /* backward: forward pass storing states every 32 steps */
+#define SS2D_KERNEL_CHECKPOINT 5 /* backward: forward pass storing states every 8 steps  */
 #define SS2D_KERNEL_SCAN_BWD 6  /* backward: adjoint scan                               */
 #define SS2D_KERNEL_REDUCE 7    /* backward: sums over channel blocks and images         */
 #define SS2D_KERNEL_PROJECT 8   /* per-route front end: conv + SiLU, x_proj, dt_proj      */

@@ -567,7 +567,7 @@ def _forward_save(K, x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z, zoh, y, saved, st
 def ss2d_forward_save(x, dt_raw, A_log, Bs, Cs, Ds, dt_bias, z=None, zoh=False, y=None,
                       saved=None, stream=None):
     """The training forward: y as ss2d_forward_ex(..., z=z, zoh=zoh), and the state its
-    backward starts from (the scan's state before every 32-step tile, and with the gate the
+    backward starts from (the scan's state before every 8-step quarter, and with the gate the
     ungated route sum), for ss2d_backward_saved.  Returns (y, saved); saved is an fp32
     tensor of saved_state_bytes(4, B, D, H * W, N, z is not None) / 4 elements."""
     if x.dim() != 4:

@@ -241,7 +241,7 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
   const int64_t max_b = kMaxGridZ / per > 0 ? kMaxGridZ / per : 1;
   const int64_t L = a.L, D = a.D, K = a.K, N = a.N;
   const bool ckpt = mode == ss2d::kModeCkpt || mode == ss2d::kModeCkptOut;
-  const int64_t C = ckpt ? a.ck_tiles : a.num_chunks;
+  const int64_t C = ckpt ? ss2d::ck_slots(L) : a.num_chunks;
   for (int64_t b0 = 0; b0 < B; b0 += max_b) {
     const int64_t nb = (B - b0 < max_b) ? (B - b0) : max_b;
     ss2d::ScanArgs s = a;
@@ -267,18 +267,18 @@ int scan_pass(ss2d::ScanArgs a, int dtype, const Plan& p, int mode, int64_t e, h
 }
 
 // The state a training forward keeps for its backward (ss2d_forward_save): the scan's state
-// before every 32-step tile, (B, K, D, ceil(L / 32), N) fp32 (the first tile's, zero, is not
-// written), then with the gate the ungated route sum v, (B, D, L) fp32.  Sizes in bytes;
+// before every 8-step quarter, (B, K, D, ceil(L / 8), N) fp32 (the first quarter's, zero, is
+// not written), then with the gate the ungated route sum v, (B, D, L) fp32.  Sizes in bytes;
 // -1 for sizes the operator rejects or N not a multiple of 4.
 int64_t saved_ck_bytes(int64_t B, int64_t K, int64_t D, int64_t L, int64_t N) {
-  return B * K * D * ((L + 31) / 32) * N * 4;
+  return B * K * D * ss2d::ck_slots(L) * N * 4;
 }
 int64_t saved_bytes(int K, int64_t B, int64_t D, int64_t L, int64_t N, bool gated) {
   if ((K != 2 && K != 4) || B < 0 || D < 0 || L < 1 || L >= kMaxL || N < 4 || N > 32 ||
       (N & (N - 1)) != 0)
     return -1;
   int64_t ck, t, v = 0;
-  if (!mul_ok(B * K, D, &t) || !mul_ok(t, ((L + 31) / 32) * N * 4, &ck)) return -1;
+  if (!mul_ok(B * K, D, &t) || !mul_ok(t, ss2d::ck_slots(L) * N * 4, &ck)) return -1;
   if (gated && (!mul_ok(B, D, &t) || !mul_ok(t, L * 4, &v))) return -1;
   return ck + v;
 }
@@ -391,7 +391,6 @@ int forward(int K, bool routes, const void* x, const void* dt_raw, const float* 
     });
   if (!err && save) {
     a.h_in = saved;
-    a.ck_tiles = static_cast<int>(tiles);
     a.chunk_base = 0;
     a.chunks_in_launch = 1;
     rc = scan_pass(a, dtype, p, ss2d::kModeCkptOut, e, st);
@@ -574,7 +573,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
   const size_t off_g = off;
   if (gated) off = align256(off + size_t(n_x * 4));
   const size_t off_ck = off;
-  if (!from_saved) off = align256(off + size_t(B * K * D) * size_t(tiles * N) * 4);
+  if (!from_saved) off = align256(off + size_t(B * K * D) * size_t(ss2d::ck_slots(L) * N) * 4);
   // per-route du in fp32: merged into dx, or (gate) first the route outputs; with per-route
   // inputs and no gate the adjoint writes du straight to the output
   const bool need_du = !routes || gated;
@@ -602,7 +601,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
       return ss2d::launch_transpose(x, ws + off_xt, int(B), int(D), int(H), int(W), dtype, st);
     });
   const float* h_ck = from_saved ? saved : reinterpret_cast<const float*>(ws + off_ck);
-  // Checkpoints: the forward scan storing the state before every 32-step tile (and, with the
+  // Checkpoints: the forward scan storing the state before every 8-step quarter (and, with the
   // gate, the per-route outputs, which the merge kernel turns into g and dz), unless a
   // training forward kept them.
   if (!err && !from_saved) {
@@ -625,7 +624,6 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     a.chunk_len = int(tiles * 32);
     a.chunk_base = 0;
     a.chunks_in_launch = 1;
-    a.ck_tiles = int(tiles);
     a.zoh = (flags & SS2D_FLAG_ZOH) ? 1 : 0;
     a.x_routes = routes ? 1 : 0;
     if (gated) a.y_route = reinterpret_cast<float*>(ws + off_du);
@@ -671,7 +669,7 @@ int backward(int K, const void* x, const void* dt_raw, const float* A_log, const
     g.A_log = A_log;
     g.Ds = Ds;
     g.dt_bias = dt_bias;
-    g.h_ck = h_ck + b0 * K * D * tiles * N;
+    g.h_ck = h_ck + b0 * K * D * ss2d::ck_slots(L) * N;
     g.du_route = need_du ? reinterpret_cast<float*>(ws + off_du) + b0 * K * D * L : nullptr;
     g.ddt_raw = static_cast<char*>(ddt_raw) + b0 * K * D * L * e;
     g.dbc_part = reinterpret_cast<float*>(ws + off_bc) + b0 * K * n_cb * 2 * N * L;

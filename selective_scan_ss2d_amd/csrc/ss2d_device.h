@@ -164,14 +164,14 @@ struct ScanArgs {
   float* y_route;         // (B, K, D, L) fp32 per-route outputs in scan order
   float* h_end;           // (B, K, D, C, N) chunk end states from a zero start
   float* delta_sum;       // (B, K, D, C) sum of delta over each chunk
-  float* h_in;            // kModeCkpt(Out): the states before each 32-step tile
+  float* h_in;            // kModeCkpt(Out): (B, K, D, ck_slots(L), N) states, slot c the
+                          // state before step 8 c (slot 0, the zero state, not written)
   int B, K, D, L, N;
   int num_chunks;         // C
   int chunk_len;          // steps per chunk, a multiple of kChunkAlign (>= L when C == 1)
   int chunk_base;         // first chunk index covered by this launch
   int chunks_in_launch;   // chunks covered by this launch per (b, k)
   int zoh;                // nonzero: zero-order hold for B, (exp(delta A) - 1) / A * B
-  int ck_tiles;           // kModeCkpt(Out): 32-step tiles per sequence; h_in gets the states
   int x_routes;           // nonzero: x_row holds each route's own input sequence
   const void* dt_lr;      // dt_proj folded in (else NULL): x_proj's dt rows (B, K, R, L) ...
   const float* dt_w;      // ... and the dt_proj weight (K, D, R): dt_raw = dt_w @ dt_lr
@@ -180,6 +180,9 @@ struct ScanArgs {
 constexpr int kMaxLowRank = 4;  // dt rows a tile row of the scan's B/C LDS tile can hold
 
 enum ScanMode { kModeOut = 0, kModeAgg = 1, kModeCkpt = 2, kModeCkptOut = 3 };
+
+// Checkpoint slots per sequence of L steps: one per 8-step quarter of a 32-step tile.
+__host__ __device__ constexpr int64_t ck_slots(int64_t L) { return (L + 7) / 8; }
 
 // Arguments of the backward scan kernel (gradients of sum(dy * y), plain operator).
 struct BwdArgs {
@@ -193,7 +196,8 @@ struct BwdArgs {
   const float* A_log;     // (K, D, N)
   const float* Ds;        // (K, D)
   const float* dt_bias;   // (K, D)
-  const float* h_ck;      // (B, K, D, ck_tiles, N) state before each 32-step tile (>= 1)
+  const float* h_ck;      // (B, K, D, ck_slots(L), N) state before each 8-step quarter
+                          // (slot c: before step 8 c; slot 0, the zero state, is not read)
   float* du_route;        // (B, K, D, L) fp32 dL/du per route, scan order
   void* ddt_raw;          // (B, K, D, L) gradient of dt_raw, element type of the inputs
   float* dbc_part;        // (B, K, n_cb, 2N, L) per channel-block sums of dB (rows < N), dC

@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 11
+    assert lib.ss2d_abi_version() == 12
     seen = set()
     for code in range(8):
         s = lib.ss2d_status_string(code)

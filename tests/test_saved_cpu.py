@@ -27,8 +27,8 @@ def fake_ptrs(n, base=1 << 40, gap=1 << 32):
 @pytest.mark.parametrize("K,B,D,L,N", [(4, 64, 192, 3136, 16), (2, 128, 768, 197, 16),
                                        (4, 1, 8, 64, 4), (4, 3, 5, 33, 32), (2, 2, 1, 1, 8)])
 def test_saved_state_bytes(lib, K, B, D, L, N):
-    tiles = (L + 31) // 32  # the state before every 32-step tile, fp32
-    ck = B * K * D * tiles * N * 4
+    slots = (L + 7) // 8  # the state before every 8-step quarter, fp32
+    ck = B * K * D * slots * N * 4
     assert lib.ss2d_saved_state_bytes(K, B, D, L, N, 0) == ck
     assert lib.ss2d_saved_state_bytes(K, B, D, L, N, 1) == ck + B * D * L * 4  # + route sum
 

@@ -75,16 +75,16 @@ def test_saved_equals_recomputed(shape, gate, zoh):
 
 
 def test_saved_state_is_the_checkpoints():
-    """The saved state's layout: zero-free checkpoints where tiles start, and with the gate
-    the fp32 route sum, whose gate product rounds to y."""
+    """The saved state's layout: zero-free checkpoints where 8-step quarters start, and
+    with the gate the fp32 route sum, whose gate product rounds to y."""
     import torch
     import selective_scan_ss2d_amd as ss
-    wl = workloads.custom(2, 64, 8, 12, 16, 4, "f32")  # L = 96: three tiles
+    wl = workloads.custom(2, 64, 8, 12, 16, 4, "f32")  # L = 96: three tiles, 12 quarters
     y_ref, y, _, _, saved = _run(wl, True, False, seed=5)
-    L, tiles = wl.H * wl.W, 3
-    ck_floats = wl.B * 4 * wl.D * tiles * wl.N
+    L, slots = wl.H * wl.W, 12
+    ck_floats = wl.B * 4 * wl.D * slots * wl.N
     assert saved.numel() * 4 == ss.saved_state_bytes(4, wl.B, wl.D, L, wl.N, True)
-    ck = saved[:ck_floats].view(wl.B, 4, wl.D, tiles, wl.N)
+    ck = saved[:ck_floats].view(wl.B, 4, wl.D, slots, wl.N)
     assert torch.isfinite(ck[:, :, :, 1:]).all() and (ck[:, :, :, 1:] != 0).any()
     v = saved[ck_floats:].view(wl.B, wl.D, wl.H, wl.W)
     z = torch.from_numpy(workloads.make_gate(wl, 5)["z"]).to("cuda:0")
@@ -109,10 +109,10 @@ def test_saved_deterministic():
     _, y1, _, g1, s1 = _run(wl, True, True, seed=9)
     _, y2, _, g2, s2 = _run(wl, True, True, seed=9)
     L = wl.H * wl.W
-    ck = wl.B * 4 * wl.D * ((L + 31) // 32) * wl.N
-    # the first tile's checkpoint slots are not written: compare the rest, and the route sum
-    c1 = s1[:ck].view(-1, (L + 31) // 32, wl.N)[:, 1:]
-    c2 = s2[:ck].view(-1, (L + 31) // 32, wl.N)[:, 1:]
+    ck = wl.B * 4 * wl.D * ((L + 7) // 8) * wl.N
+    # the first quarter's checkpoint slots are not written: compare the rest, and the route sum
+    c1 = s1[:ck].view(-1, (L + 7) // 8, wl.N)[:, 1:]
+    c2 = s2[:ck].view(-1, (L + 7) // 8, wl.N)[:, 1:]
     assert _same(y1, y2) and _same(c1, c2) and _same(s1[ck:], s2[ck:])
     for name in g1:
         assert _same(g1[name], g2[name]), name
